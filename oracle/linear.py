@@ -1,0 +1,49 @@
+"""Forward and backward of the frozen-base LoRA linear layer (CPU oracle, fp64).
+
+Test infrastructure only (see the package docstring).
+
+Notation (aivaro.ru "Как работает QLoRA", §2): W in R^{d x k} (here N x K, the
+frozen base, already dequantized), B in R^{d x r}, A in R^{r x k}, h = Wx + BAx.
+apxml.com "量化 LoRA (QLoRA) 与 4 位训练": in QLoRA the base enters as
+dequant(W_NF4). With a batch of row vectors X [T, K] the layer is
+
+    U = X A^T          [T, r]
+    H = X W'^T + s U B^T   [T, N],  s = alpha / r
+
+(the scale s is the reading of the "lora_alpha" scaling factor; the printed
+equations omit it). aivaro.ru §7: gradients flow through the dequantized
+4-bit weight, which is never updated; only A and B are trained.
+"""
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def lora_forward(X, Wd, A, B, scale):
+    """Return (H, U) in fp64 from bf16-valued inputs X [T,K], dequantized
+    W' [N,K], A [r,K], B [N,r]."""
+    X, Wd, A, B = _f64(X), _f64(Wd), _f64(A), _f64(B)
+    U = X @ A.T
+    H = X @ Wd.T + float(scale) * (U @ B.T)
+    return H, U
+
+
+def lora_backward(X, dY, Wd, A, B, scale):
+    """Return (dX, dA, dB, G, U) in fp64 for the upstream gradient dY [T,N]:
+
+        G  = s dY B        [T, r]
+        dX = dY W' + G A   [T, K]
+        dA = G^T X         [r, K]
+        dB = s dY^T U      [N, r]
+    """
+    X, dY, Wd, A, B = _f64(X), _f64(dY), _f64(Wd), _f64(A), _f64(B)
+    s = float(scale)
+    U = X @ A.T
+    G = s * (dY @ B)
+    dX = dY @ Wd + G @ A
+    dA = G.T @ X
+    dB = s * (dY.T @ U)
+    return dX, dA, dB, G, U

@@ -1,0 +1,128 @@
+"""Pins for the oracle's forward and backward (no GPU): brute-force loops on
+tiny shapes, gradients derived by torch.autograd (fp64) and by central
+differences, and closed forms for the special cases B = 0, A = 0 and W = 0."""
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def _case(T=3, N=5, K=8, r=2, seed=0, b_std=0.5):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K))
+    W = rng.standard_normal((N, K)) * 0.1
+    A = rng.standard_normal((r, K)) * 0.3
+    B = rng.standard_normal((N, r)) * b_std
+    dY = rng.standard_normal((T, N))
+    return X, W, A, B, dY
+
+
+def test_forward_matches_brute_force_loops():
+    X, W, A, B, _ = _case(T=3, N=7, K=16, r=3, seed=1)
+    s = 1.75
+    H, U = oracle.lora_forward(X, W, A, B, s)
+    T_, K = X.shape
+    N, r = B.shape
+    for t in range(T_):
+        for j in range(r):
+            u = 0.0
+            for k in range(K):
+                u += X[t, k] * A[j, k]
+            assert abs(u - U[t, j]) < 1e-12
+        for n in range(N):
+            h = 0.0
+            for k in range(K):
+                h += X[t, k] * W[n, k]
+            lora = 0.0
+            for j in range(r):
+                ba = 0.0
+                for k in range(K):
+                    ba += B[n, j] * A[j, k] * X[t, k]
+                lora += ba
+            assert abs(h + s * lora - H[t, n]) < 1e-12
+
+
+def test_backward_matches_autograd_fp64():
+    X, W, A, B, dY = _case(T=4, N=6, K=12, r=3, seed=2)
+    s = 2.0
+    tX = torch.tensor(X, dtype=torch.float64, requires_grad=True)
+    tA = torch.tensor(A, dtype=torch.float64, requires_grad=True)
+    tB = torch.tensor(B, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64)
+    H = tX @ tW.T + s * ((tX @ tA.T) @ tB.T)
+    H.backward(torch.tensor(dY, dtype=torch.float64))
+    dX, dA, dB, G, U = oracle.lora_backward(X, dY, W, A, B, s)
+    assert np.allclose(dX, tX.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dA, tA.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dB, tB.grad.numpy(), rtol=0, atol=1e-12)
+    Href, _ = oracle.lora_forward(X, W, A, B, s)
+    assert np.allclose(Href, H.detach().numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_matches_central_differences():
+    X, W, A, B, dY = _case(T=2, N=4, K=6, r=2, seed=3)
+    s = 0.5
+    dX, dA, dB, _, _ = oracle.lora_backward(X, dY, W, A, B, s)
+
+    def loss(X_, A_, B_):
+        H, _ = oracle.lora_forward(X_, W, A_, B_, s)
+        return float(np.sum(H * dY))
+
+    h = 1e-6
+    for arr, grad, which in ((X, dX, 0), (A, dA, 1), (B, dB, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p = arr.copy()
+            m = arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            args_p = [X, A, B]
+            args_m = [X, A, B]
+            args_p[which] = p
+            args_m[which] = m
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.allclose(num, grad, rtol=1e-6, atol=1e-8)
+
+
+def test_special_case_B_zero():
+    X, W, A, B, dY = _case(seed=4)
+    B = np.zeros_like(B)
+    H, _ = oracle.lora_forward(X, W, A, B, 2.0)
+    assert np.array_equal(H, X @ W.T)
+    dX, dA, dB, _, _ = oracle.lora_backward(X, dY, W, A, B, 2.0)
+    assert np.all(dA == 0)
+    assert np.allclose(dX, dY @ W, rtol=0, atol=1e-14)
+
+
+def test_special_case_A_zero():
+    X, W, A, B, dY = _case(seed=5)
+    A = np.zeros_like(A)
+    H, U = oracle.lora_forward(X, W, A, B, 2.0)
+    assert np.all(U == 0) and np.array_equal(H, X @ W.T)
+    _, _, dB, _, _ = oracle.lora_backward(X, dY, W, A, B, 2.0)
+    assert np.all(dB == 0)
+
+
+def test_special_case_W_zero():
+    X, W, A, B, dY = _case(seed=6)
+    W = np.zeros_like(W)
+    s = 3.0
+    H, _ = oracle.lora_forward(X, W, A, B, s)
+    assert np.allclose(H, s * X @ A.T @ B.T, rtol=0, atol=1e-13)
+    dX, _, _, G, _ = oracle.lora_backward(X, dY, W, A, B, s)
+    assert np.allclose(dX, (s * dY @ B) @ A, rtol=0, atol=1e-13)
+    assert np.allclose(G, s * dY @ B, rtol=0, atol=1e-14)
+
+
+def test_quantized_all_zero_weight_gives_zero_base():
+    # an all-zero weight quantizes to code 7 everywhere and dequantizes to 0,
+    # which is how the GPU tests isolate the LoRA branch
+    w = np.zeros((8, 128), dtype=np.float32)
+    packed, a = oracle.quantize(w)
+    assert np.all(packed == 0x77) and np.all(a == 0)
+    c8, S, mu = oracle.double_quant(a)
+    ar = oracle.dequant_absmax(c8, S, mu)
+    assert np.all(ar == 0)
+    wd = oracle.dequantize(packed, ar, w.size, out="f32")
+    assert np.all(wd == 0)
