@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 hot path on one MI355X.
+
+One step is one pass of every stage of the path over one batch of seeded
+synthetic input at Llama-7B shapes:
+
+  attention projection 4096 x 4096 (W ~ N(0, 0.02), 0.1% outliers x20, r=16):
+      nf4_quantize (fp32 in) + nf4_double_quant, nf4_dequantize (bf16 out),
+      qlora_linear_fwd at T = 1 and T = 16 (dequant-GEMV)
+  MLP gate / up 11008 x 4096 and down 4096 x 11008 (W ~ 0.02 t(5), r=16):
+      nf4_quantize + nf4_double_quant of each,
+      qlora_linear_fwd at T = 1024 (dequant-in-LDS MFMA GEMM + LoRA),
+      qlora_linear_bwd at T = 1024 (dX, dA, dB)
+
+The reported value is the step's roofline-ideal time (each stage's
+algorithmic bytes at 8 TB/s or flops at 2.5 PFLOP/s dense bf16) divided by
+the measured step time, in percent. Per-stage throughput (GB/s, TFLOP/s)
+measured with cold caches is in "rows"; "roofline" is the dominant kernel
+timed with HIP events inside the timed steps; "cpu_baseline" is the CPU
+oracle on a bounded sample of the same step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12  # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15  # flop/s, MI355X dense bf16 MFMA
+
+BPW_QUANT_F32 = 4 + 0.5 + 4 / 64  # read fp32, write code nibble + absmax share
+BPW_QUANT_BF16 = 2 + 0.5 + 4 / 64
+BPW_DQ = (4 + 4 + 1 + 4 / 256) / 64  # absmax read twice, c8 + scale written
+BPW_DEQUANT = 0.5 + 1 / 64 + 4 / (64 * 256) + 2  # codes + c8 + scale in, bf16 out
+BPW_PACKED = 0.5 + 1 / 64 + 4 / (64 * 256)  # what a matmul reads per weight
+
+
+def gemv_bytes(N, K, T, r):
+    return BPW_PACKED * N * K + 2 * T * K + 2 * T * N + 2 * r * (K + N)
+
+
+def fwd_flops(N, K, T, r):
+    return 2 * T * N * K + 2 * T * K * r + 2 * T * r * N
+
+
+def dx_flops(N, K, T, r):
+    return 2 * T * N * K + 2 * T * N * r + 2 * T * r * K
+
+
+def lora_grad_bytes(N, K, T, r):
+    # dA = G^T X reads X and writes dA; dB = s dY^T U reads dY and writes dB
+    return 2 * T * K + 2 * T * N + 4 * T * r * 2 + 4 * r * (K + N)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-stage cold-cache measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+class Inputs:
+    """Seeded synthetic inputs of one step, resident on the GPU."""
+
+    def __init__(self, torch, workloads):
+        attn = workloads.attn_proj_7b(T=16, seed=1)
+        self.attn = attn
+        self.W_attn = attn.W.cuda()
+        self.X1 = attn.X[:1].contiguous().cuda()
+        self.X16 = attn.X.cuda()
+        self.A_attn, self.B_attn = attn.A.cuda(), attn.B.cuda()
+        self.s_attn = attn.scale
+        self.mlp = [workloads.mlp_7b(w, T=1024, seed=2) for w in ("gate", "up", "down")]
+        self.mlp_dev = []
+        for c in self.mlp:
+            self.mlp_dev.append(dict(W=c.W.cuda(), X=c.X.cuda(), dY=c.dY.cuda(), A=c.A.cuda(), B=c.B.cuda(),
+                                     s=c.scale, r=c.r, N=c.W.shape[0], K=c.W.shape[1], T=c.X.shape[0]))
+
+
+def run_step(qn, inp):
+    """One pass of the whole path. Returns nothing; results stay on device."""
+    wa = qn.quantize_weight(inp.W_attn)
+    qn.nf4_dequantize(wa)
+    wm = [qn.quantize_weight(m["W"]) for m in inp.mlp_dev]
+    # the decode GEMVs run after the 0.5 GB of MLP quantization has streamed
+    # through the caches, so the attention weight is read from HBM
+    qn.qlora_linear_fwd(wa, inp.X1, inp.A_attn, inp.B_attn, inp.s_attn)
+    qn.qlora_linear_fwd(wa, inp.X16, inp.A_attn, inp.B_attn, inp.s_attn)
+    for w, m in zip(wm, inp.mlp_dev):
+        _, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
+        qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U)
+
+
+def ideal_step_seconds(inp):
+    """Roofline-ideal time of one step, stage by stage."""
+    t = 0.0
+    na = 4096 * 4096
+    t += (BPW_QUANT_F32 + BPW_DQ) * na / PEAK_HBM
+    t += BPW_DEQUANT * na / PEAK_HBM
+    r = inp.attn.r
+    t += gemv_bytes(4096, 4096, 1, r) / PEAK_HBM + gemv_bytes(4096, 4096, 16, r) / PEAK_HBM
+    for m in inp.mlp_dev:
+        N, K, T, r = m["N"], m["K"], m["T"], m["r"]
+        t += (BPW_QUANT_F32 + BPW_DQ) * N * K / PEAK_HBM
+        t += fwd_flops(N, K, T, r) / PEAK_BF16
+        t += dx_flops(N, K, T, r) / PEAK_BF16
+        t += max(lora_grad_bytes(N, K, T, r) / PEAK_HBM, 4.0 * T * r * (N + K) / PEAK_BF16)
+    return t
+
+
+KERNELS = {
+    "quantize": 1,
+    "dq_encode": 2,
+    "dequantize": 3,
+    "gemv": 4,
+    "gemm_fwd": 5,
+    "gemm_dx": 6,
+    "lora_grad": 7,
+}
+
+
+def per_launch_work(inp):
+    """Algorithmic work of one launch of each kernel in the step (all launches
+    of a kernel in the step do the same work, except where noted)."""
+    m = inp.mlp_dev[0]
+    N, K, T, r = m["N"], m["K"], m["T"], m["r"]
+    return {
+        "gemm_fwd": ("mfma", fwd_flops(N, K, T, r) - 2 * T * K * r, "TFLOP/s"),  # U = X A^T runs outside
+        "gemm_dx": ("mfma", dx_flops(N, K, T, r) - 2 * T * N * r, "TFLOP/s"),  # G = s dY B runs outside
+    }
+
+
+def measure_rows(torch, qn, inp, flush):
+    """Cold-cache throughput of each stage: a 512 MiB buffer is overwritten
+    before every timed repetition; the kernel time is the library's HIP-event
+    timer of that stage's main kernel."""
+    rows = {}
+    reps = 5
+
+    def timed(kid, fn):
+        t = qn.KernelTimer(kid)
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t.arm()
+        for _ in range(reps):
+            flush()
+            fn()
+        n, ms = t.read()
+        t.disarm()
+        return ms / max(n, 1) / 1e3
+
+    na = 4096 * 4096
+    W = inp.W_attn
+    sec = timed(1, lambda: qn.nf4_quantize(W))
+    rows["quantize_f32_4096x4096"] = _hbm_row(BPW_QUANT_F32 * na, sec)
+    Wb = W.to(torch.bfloat16)
+    sec = timed(1, lambda: qn.nf4_quantize(Wb))
+    rows["quantize_bf16_4096x4096"] = _hbm_row(BPW_QUANT_BF16 * na, sec)
+    Wm = inp.mlp_dev[0]["W"]
+    sec = timed(1, lambda: qn.nf4_quantize(Wm))
+    rows["quantize_f32_11008x4096"] = _hbm_row(BPW_QUANT_F32 * Wm.numel(), sec)
+    _, absmax = qn.nf4_quantize(W)
+    sec = timed(2, lambda: qn.nf4_double_quant(absmax))
+    rows["dq_encode_4096x4096"] = _hbm_row((4 + 1 + 4 / 256) / 64 * na, sec)
+    wa = qn.quantize_weight(W)
+    sec = timed(3, lambda: qn.nf4_dequantize(wa))
+    rows["dequantize_bf16_4096x4096"] = _hbm_row(BPW_DEQUANT * na, sec)
+    r = inp.attn.r
+    for T, X in ((1, inp.X1), (16, inp.X16)):
+        sec = timed(4, lambda: qn.qlora_linear_fwd(wa, X, inp.A_attn, inp.B_attn, inp.s_attn))
+        rows["gemv_T%d_4096x4096" % T] = _hbm_row(BPW_PACKED * na + 2 * T * 4096, sec)
+    m = inp.mlp_dev[0]
+    w = qn.quantize_weight(m["W"])
+    N, K, T, r = m["N"], m["K"], m["T"], m["r"]
+    sec = timed(5, lambda: qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"]))
+    rows["gemm_fwd_T1024_11008x4096"] = _mfma_row(fwd_flops(N, K, T, r) - 2 * T * K * r, sec)
+    _, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
+    sec = timed(6, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U,
+                                              need_da=False, need_db=False))
+    rows["gemm_dx_T1024_11008x4096"] = _mfma_row(dx_flops(N, K, T, r) - 2 * T * N * r, sec)
+    sec = timed(7, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_dx=False))
+    rows["lora_grad_T1024_11008x4096"] = _hbm_row(lora_grad_bytes(N, K, T, r) / 2, sec)  # per launch: dA or dB
+    return rows
+
+
+def _hbm_row(nbytes, sec):
+    gbs = nbytes / sec / 1e9
+    return {"us": round(sec * 1e6, 2), "GB/s": round(gbs, 1), "frac": round(gbs * 1e9 / PEAK_HBM, 4)}
+
+
+def _mfma_row(flops, sec):
+    tf = flops / sec / 1e12
+    return {"us": round(sec * 1e6, 2), "TFLOP/s": round(tf, 1), "frac": round(tf * 1e12 / PEAK_BF16, 4)}
+
+
+def cpu_baseline(inp, ideal_s):
+    """The CPU oracle on a bounded sample of the step; the full-step CPU time is
+    extrapolated linearly from the sample (stated in 'sample')."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    est = 0.0
+    rows_q = 128
+    # quantize + double quant + dequantize: a 128-row slice of each weight
+    for W, full_rows in [(inp.attn.W, 4096)] + [(c.W, c.W.shape[0]) for c in inp.mlp]:
+        Wn = W[:rows_q].numpy()
+        t0 = time.perf_counter()
+        p, a = oracle.quantize(Wn)
+        c8, s, mu = oracle.double_quant(a)
+        ae = oracle.dequant_absmax(c8, s, mu)
+        oracle.dequantize(p, ae, Wn.size)
+        est += (time.perf_counter() - t0) * full_rows / rows_q
+    # decode GEMVs: full size (fp64 matmul)
+    ref = oracle.bf16_bits_to_f32(oracle.dequantize(*oracle.quantize(inp.attn.W[:512].numpy()), 512 * 4096))
+    Wd = np.tile(ref.reshape(512, 4096), (8, 1))
+    X16 = inp.attn.X.float().numpy()
+    A, B = inp.attn.A.float().numpy(), inp.attn.B.float().numpy()
+    t0 = time.perf_counter()
+    oracle.lora_forward(X16[:1], Wd, A, B, inp.attn.scale)
+    oracle.lora_forward(X16, Wd, A, B, inp.attn.scale)
+    est += time.perf_counter() - t0
+    # MLP forward + backward: 64 of the 1024 tokens, scaled by 1024 / 64
+    t_s = 64
+    for c in inp.mlp:
+        N, K = c.W.shape
+        Wd = np.random.default_rng(0).standard_normal((N, K)).astype(np.float32) * 0.02
+        Xn = c.X[:t_s].float().numpy()
+        dYn = c.dY[:t_s].float().numpy()
+        An, Bn = c.A.float().numpy(), c.B.float().numpy()
+        t0 = time.perf_counter()
+        oracle.lora_forward(Xn, Wd, An, Bn, c.scale)
+        oracle.lora_backward(Xn, dYn, Wd, An, Bn, c.scale)
+        est += (time.perf_counter() - t0) * c.X.shape[0] / t_s
+    return {
+        "value": round(100.0 * ideal_s / est, 6),
+        "unit": "% of MI355X roofline",
+        "cores": int(min(cores, blas_threads)) if blas_threads > 1 else 1,
+        "kind": "oracle",
+        "sample": "numpy oracle: quantize+double-quant+dequantize of 128 rows of each weight (x rows/128), "
+                  "both decode GEMVs in full, MLP fwd+bwd on 64 of 1024 tokens (x16); "
+                  "extrapolated step time %.2f s; elementwise numpy single-threaded, fp64 matmuls on %d BLAS "
+                  "threads, %d host cores" % (est, blas_threads, cores),
+        "step_seconds_est": round(est, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (--gpus 1); no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_nf4_quantized_16_amd as qn
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    torch.cuda.set_device(0)
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    inp = Inputs(torch, workloads)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: copy calibration 268435456 bytes read + written", file=sys.stderr, flush=True)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run_step(qn, inp)
+    torch.cuda.synchronize()
+
+    timers = {k: qn.KernelTimer(v) for k, v in KERNELS.items()}
+    for t in timers.values():
+        t.arm()
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(qn, inp)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kstats = {}
+    for k, t in timers.items():
+        n, ms = t.read()
+        t.disarm()
+        kstats[k] = (n, ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    ideal = ideal_step_seconds(inp)
+    value = 100.0 * ideal / (ms_per_step / 1e3)
+
+    # dominant kernel: the largest total time in the timed steps
+    dom = max(kstats, key=lambda k: kstats[k][1])
+    work = per_launch_work(inp)
+    roof = None
+    if dom in work:
+        bound, per_launch, unit = work[dom]
+        n, ms = kstats[dom]
+        avg_s = ms / n / 1e3
+        achieved = per_launch / avg_s / 1e12
+        roof = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16 / 1e12,
+                "unit": unit, "frac": round(achieved / (PEAK_BF16 / 1e12), 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 2), "launches": n}
+    out = {
+        "metric": "dequant-GEMM TFLOP/s + quant/GEMV GB/s at 7B shapes, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "% of MI355X roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the 7B workloads)",
+        "config": {
+            "workload": "llama7b_qlora_step: attn 4096x4096 quantize+DQ+dequant+GEMV T=1,16 (r=16); "
+                        "MLP 11008x4096 x2 + 4096x11008 quantize+DQ+fwd+bwd at T=1024 (r=16)",
+            "ideal_step_ms": round(ideal * 1e3, 4),
+            "blocksize": 64,
+            "dq_blocksize": 256,
+        },
+        "roofline": roof,
+        "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kstats.items()},
+    }
+    if not args.no_rows:
+        flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        print("bench: per-stage cold-cache rows", file=sys.stderr, flush=True)
+        out["rows"] = measure_rows(torch, qn, inp, lambda: flushbuf.fill_(1))
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, ideal)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""MI355X (gfx950) QLoRA frozen-base linear layer: blockwise NF4 quantization
+with double quantization, and the LoRA forward / backward on the 4-bit base.
+
+The functions below carry the names of the C ABI (include/qlora_nf4.h) and do
+argument marshalling only: every step runs in the HIP library
+libqlora_nf4.so. torch supplies device memory and the current stream.
+Importing this package fails if the library has not been built.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+lib = _lib.load()
+
+__all__ = [
+    "NF4Weight",
+    "QLoraError",
+    "nf4_quantize",
+    "nf4_double_quant",
+    "nf4_dequantize",
+    "qlora_linear_fwd",
+    "qlora_linear_bwd",
+    "quantize_weight",
+    "QLoRALinearFunction",
+    "KernelTimer",
+    "lib",
+]
+
+BLOCKSIZE = 64
+DQ_BLOCKSIZE = 256
+
+
+class QLoraError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (%d): %s" % (lib.qlora_status_string(status).decode(), status, message))
+        self.status = status
+
+
+def _check(status):
+    if status != _lib.QL_OK:
+        raise QLoraError(status, lib.qlora_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _bits(t):
+    """bf16 tensor -> its storage (the library takes bf16 as raw 16-bit)."""
+    if t is None:
+        return None
+    assert t.dtype == torch.bfloat16 and t.is_contiguous(), "expected a contiguous bf16 tensor"
+    return t
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+@dataclass
+class NF4Weight:
+    """A frozen weight in NF4 (+ double-quantized constants) on the device."""
+
+    rows: int
+    cols: int
+    packed: torch.Tensor
+    absmax: torch.Tensor = None  # fp32 [nblocks]; kept when double_quant=False
+    c8: torch.Tensor = None  # uint8 [nblocks]
+    dq_scale: torch.Tensor = None  # fp32 [ngroups]
+    dq_mean: torch.Tensor = None  # fp32 [1]
+
+    @property
+    def double_quant(self):
+        return self.c8 is not None
+
+    @property
+    def shape(self):
+        return (self.rows, self.cols)
+
+    def nbytes(self):
+        n = self.packed.numel()
+        if self.double_quant:
+            n += self.c8.numel() + 4 * self.dq_scale.numel() + 4
+        else:
+            n += 4 * self.absmax.numel()
+        return n
+
+    def descriptor(self):
+        d = _lib.QlNf4Weight()
+        d.rows = self.rows
+        d.cols = self.cols
+        d.blocksize = BLOCKSIZE
+        d.dq_blocksize = DQ_BLOCKSIZE if self.double_quant else 0
+        d.packed = self.packed.data_ptr()
+        d.absmax = self.absmax.data_ptr() if self.absmax is not None else None
+        d.c8 = self.c8.data_ptr() if self.double_quant else None
+        d.dq_scale = self.dq_scale.data_ptr() if self.double_quant else None
+        d.dq_mean = self.dq_mean.data_ptr() if self.double_quant else None
+        return d
+
+
+def nf4_quantize(W, packed=None, absmax=None):
+    """First-level NF4 quantization of a 2-D fp32/bf16 device tensor.
+    Returns (packed uint8 [ceil(n/2)], absmax fp32 [ceil(n/64)])."""
+    assert W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    rows, cols = W.shape
+    dtype = {torch.float32: _lib.QL_F32, torch.bfloat16: _lib.QL_BF16}[W.dtype]
+    if packed is None:
+        packed = torch.empty(lib.nf4_packed_bytes(rows, cols), dtype=torch.uint8, device=W.device)
+    if absmax is None:
+        absmax = torch.empty(lib.nf4_num_blocks(rows, cols, BLOCKSIZE), dtype=torch.float32, device=W.device)
+    _check(lib.nf4_quantize(_ptr(W), dtype, rows, cols, BLOCKSIZE, _ptr(packed), _ptr(absmax), _stream()))
+    return packed, absmax
+
+
+def nf4_double_quant(absmax):
+    """Second-level quantization of the fp32 absmax constants.
+    Returns (c8 uint8 [n1], scale fp32 [ceil(n1/256)], mean fp32 [1])."""
+    n1 = absmax.numel()
+    dev = absmax.device
+    c8 = torch.empty(n1, dtype=torch.uint8, device=dev)
+    scale = torch.empty(lib.nf4_dq_num_groups(n1, DQ_BLOCKSIZE), dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(lib.nf4_double_quant_workspace(n1), dev)
+    _check(
+        lib.nf4_double_quant(_ptr(absmax), n1, DQ_BLOCKSIZE, _ptr(c8), _ptr(scale), _ptr(mean), _ptr(ws), wsb, _stream())
+    )
+    return c8, scale, mean
+
+
+def quantize_weight(W, double_quant=True, keep_absmax=False):
+    """nf4_quantize (+ nf4_double_quant) into an NF4Weight."""
+    packed, absmax = nf4_quantize(W)
+    if not double_quant:
+        return NF4Weight(W.shape[0], W.shape[1], packed, absmax=absmax)
+    c8, scale, mean = nf4_double_quant(absmax)
+    return NF4Weight(W.shape[0], W.shape[1], packed, absmax=absmax if keep_absmax else None, c8=c8, dq_scale=scale,
+                     dq_mean=mean)
+
+
+def nf4_dequantize(w, dtype=torch.bfloat16, out=None):
+    """Expand an NF4Weight to a [rows, cols] bf16 (or fp32) device tensor."""
+    od = {torch.float32: _lib.QL_F32, torch.bfloat16: _lib.QL_BF16}[dtype]
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=dtype, device=w.packed.device)
+    d = w.descriptor()
+    _check(lib.nf4_dequantize(ctypes.byref(d), _ptr(out), od, _stream()))
+    return out
+
+
+def qlora_linear_fwd(w, X, A=None, B=None, scale=1.0, save_u=True, out=None):
+    """Y = X W'^T + scale (X A^T) B^T. Returns (Y bf16 [T, N], U fp32 [T, r] or None)."""
+    T = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = X.device
+    Y = out if out is not None else torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
+    U = torch.empty(T, r, dtype=torch.float32, device=dev) if (save_u and r > 0) else None
+    ws, wsb = _workspace(lib.qlora_linear_fwd_workspace(w.rows, w.cols, max(T, 1), r), dev)
+    d = w.descriptor()
+    _check(
+        lib.qlora_linear_fwd(ctypes.byref(d), _ptr(_bits(X)), T, _ptr(_bits(A)), _ptr(_bits(B)), r, float(scale),
+                             _ptr(Y), _ptr(U), _ptr(ws), wsb, _stream())
+    )
+    return Y, U
+
+
+def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, need_da=True, need_db=True, dA=None,
+                     dB=None, accumulate=False):
+    """Returns (dX bf16 [T, K] or None, dA fp32 [r, K] or None, dB fp32 [N, r] or None)."""
+    T = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = dY.device
+    dX = torch.empty(T, w.cols, dtype=torch.bfloat16, device=dev) if need_dx else None
+    if r > 0 and need_da and dA is None:
+        dA = torch.zeros(r, w.cols, dtype=torch.float32, device=dev)
+    if r > 0 and need_db and dB is None:
+        dB = torch.zeros(w.rows, r, dtype=torch.float32, device=dev)
+    if not need_da:
+        dA = None
+    if not need_db:
+        dB = None
+    ws, wsb = _workspace(lib.qlora_linear_bwd_workspace(w.rows, w.cols, max(T, 1), r), dev)
+    d = w.descriptor()
+    _check(
+        lib.qlora_linear_bwd(ctypes.byref(d), _ptr(_bits(X)), _ptr(_bits(dY)), T, _ptr(_bits(A)), _ptr(_bits(B)), r,
+                             float(scale), _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), 1 if accumulate else 0, _ptr(ws),
+                             wsb, _stream())
+    )
+    return dX, dA, dB
+
+
+class QLoRALinearFunction(torch.autograd.Function):
+    """autograd wrapper: forward / backward run in the HIP library; W is frozen
+    (no gradient), A and B receive fp32 gradients cast to their dtype."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, w, scale):
+        Y, U = qlora_linear_fwd(w, X.contiguous(), A.contiguous(), B.contiguous(), scale, save_u=True)
+        ctx.save_for_backward(X, A, B, U)
+        ctx.w = w
+        ctx.scale = scale
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, U = ctx.saved_tensors
+        dX, dA, dB = qlora_linear_bwd(ctx.w, X, dY.contiguous().to(torch.bfloat16), A, B, ctx.scale, U=U,
+                                      need_dx=ctx.needs_input_grad[0])
+        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None
+
+
+class KernelTimer:
+    """HIP-event timer of one library kernel (QL_KERNEL_* id): arm(), run the
+    work, read() -> (launches, total milliseconds)."""
+
+    def __init__(self, kernel_id):
+        self.kid = kernel_id
+
+    def arm(self):
+        _check(lib.qlora_timer_arm(self.kid))
+
+    def read(self):
+        n = ctypes.c_int64(0)
+        ms = ctypes.c_double(0.0)
+        _check(lib.qlora_timer_read(self.kid, ctypes.byref(n), ctypes.byref(ms)))
+        return n.value, ms.value
+
+    def disarm(self):
+        _check(lib.qlora_timer_disarm(self.kid))

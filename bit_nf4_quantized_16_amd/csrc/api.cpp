@@ -1,0 +1,438 @@
+// C ABI of the QLoRA NF4 library: argument validation (before any launch),
+// workspace carving, dispatch to the gfx950 kernels, error text and kernel
+// timers. No C++ exception crosses this file's extern "C" functions.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+#include "qlora_nf4.h"
+
+namespace qlnf4 {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+struct TimerState {
+    bool armed = false;
+    std::vector<hipEvent_t> starts, stops;
+    size_t used = 0;
+    bool open = false;
+};
+TimerState g_timers[QL_KERNEL_COUNT];
+std::mutex g_timer_mu;
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(QL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return QL_OK;
+}
+
+void timer_begin(int kid, hipStream_t stream) {
+    TimerState& t = g_timers[kid];
+    if (!t.armed) return;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    if (t.used == t.starts.size()) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return;
+        }
+        t.starts.push_back(a);
+        t.stops.push_back(b);
+    }
+    (void)hipEventRecord(t.starts[t.used], stream);
+    t.open = true;
+}
+
+void timer_end(int kid, hipStream_t stream) {
+    TimerState& t = g_timers[kid];
+    if (!t.armed || !t.open) return;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    (void)hipEventRecord(t.stops[t.used], stream);
+    ++t.used;
+    t.open = false;
+}
+
+namespace {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Sequential carving of one workspace buffer into 256-byte aligned parts.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t count) {
+        off = align_up(off, 256);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+int rank_pad64(int r) { return r <= 0 ? 0 : (r + 63) / 64 * 64; }
+
+int check_ptr(const void* p, const char* name) {
+    if (p == nullptr) return set_error(QL_ERR_NULL, "%s is NULL", name);
+    if (!aligned16(p)) return set_error(QL_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return QL_OK;
+}
+
+int check_weight(const ql_nf4_weight* w) {
+    if (w == nullptr) return set_error(QL_ERR_NULL, "weight descriptor is NULL");
+    if (w->rows <= 0 || w->cols <= 0)
+        return set_error(QL_ERR_SHAPE, "weight shape %lld x %lld", (long long)w->rows, (long long)w->cols);
+    if (w->blocksize != QL_NF4_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "blocksize %d (only 64 is offered)", w->blocksize);
+    if (w->dq_blocksize != 0 && w->dq_blocksize != QL_DQ_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "dq_blocksize %d (0 or 256)", w->dq_blocksize);
+    int s;
+    if ((s = check_ptr(w->packed, "packed")) != QL_OK) return s;
+    if (w->dq_blocksize) {
+        if ((s = check_ptr(w->c8, "c8")) != QL_OK) return s;
+        if ((s = check_ptr(w->dq_scale, "dq_scale")) != QL_OK) return s;
+        if ((s = check_ptr(w->dq_mean, "dq_mean")) != QL_OK) return s;
+    } else {
+        if ((s = check_ptr(w->absmax, "absmax")) != QL_OK) return s;
+    }
+    return QL_OK;
+}
+
+NF4Dev to_dev(const ql_nf4_weight* w) {
+    NF4Dev d;
+    d.packed = w->packed;
+    d.absmax = w->absmax;
+    d.c8 = w->c8;
+    d.scale = w->dq_scale;
+    d.mean = w->dq_mean;
+    d.dq = w->dq_blocksize != 0 ? 1 : 0;
+    return d;
+}
+
+int check_linear_shape(const ql_nf4_weight* w, int64_t T, int32_t r) {
+    if (T < 0) return set_error(QL_ERR_SHAPE, "T = %lld", (long long)T);
+    if (w->cols % 64 != 0) return set_error(QL_ERR_SHAPE, "K = %lld is not a multiple of 64", (long long)w->cols);
+    if (w->rows % 8 != 0) return set_error(QL_ERR_SHAPE, "N = %lld is not a multiple of 8", (long long)w->rows);
+    if (r < 0 || r > QL_MAX_RANK) return set_error(QL_ERR_SHAPE, "rank %d outside [0, %d]", r, QL_MAX_RANK);
+    if (T > (int64_t(1) << 31) / 1) return set_error(QL_ERR_SHAPE, "T = %lld too large", (long long)T);
+    return QL_OK;
+}
+
+// ---- forward workspace -------------------------------------------------
+struct FwdWs {
+    uint16_t* Us = nullptr;  // bf16 [T, rp64] = bf16(s U), GEMM path
+    uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path
+    float* Uf = nullptr;     // fp32 [T, r], GEMV path without U_out
+    float* part = nullptr;   // fp32 [chunks, T, N], GEMV path
+    size_t bytes = 0;
+};
+
+constexpr int64_t kGemvMaxT = 16;
+
+FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_uout) {
+    Carver c(ws);
+    FwdWs f;
+    const int rp = rank_pad64(r);
+    if (T <= kGemvMaxT) {
+        f.part = c.take<float>(static_cast<size_t>(gemv_num_chunks(K)) * T * N);
+        if (r > 0 && !have_uout) f.Uf = c.take<float>(static_cast<size_t>(T) * r);
+    } else if (r > 0) {
+        f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+        f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
+    }
+    f.bytes = align_up(c.off, 256);
+    return f;
+}
+
+// ---- backward workspace ------------------------------------------------
+struct BwdWs {
+    uint16_t* BT = nullptr;   // bf16 [r, N] = B^T
+    float* Gf = nullptr;      // fp32 [T, r] = s dY B
+    uint16_t* Gp = nullptr;   // bf16 [T, rp64]
+    uint16_t* Atp = nullptr;  // bf16 [K, rp64] = A^T padded
+    float* Uf = nullptr;      // fp32 [T, r] (recomputed U)
+    float* partA = nullptr;   // fp32 [splitsA, rpg, K]
+    float* partB = nullptr;   // fp32 [splitsB, rpg, N]
+    size_t bytes = 0;
+};
+
+BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db,
+                bool have_u) {
+    Carver c(ws);
+    BwdWs b;
+    if (r > 0) {
+        const int rp = rank_pad64(r);
+        const int rpg = lora_grad_rp(r);
+        const bool need_g = want_dx || want_da;
+        if (need_g) {
+            b.BT = c.take<uint16_t>(static_cast<size_t>(r) * N);
+            b.Gf = c.take<float>(static_cast<size_t>(T) * r);
+        }
+        if (want_dx) {
+            b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+            b.Atp = c.take<uint16_t>(static_cast<size_t>(K) * rp);
+        }
+        if (want_db && !have_u) b.Uf = c.take<float>(static_cast<size_t>(T) * r);
+        if (want_da) b.partA = c.take<float>(static_cast<size_t>(lora_grad_splits(T, K)) * rpg * K);
+        if (want_db) b.partB = c.take<float>(static_cast<size_t>(lora_grad_splits(T, N)) * rpg * N);
+    }
+    b.bytes = align_up(c.off, 256);
+    return b;
+}
+
+}  // namespace
+}  // namespace qlnf4
+
+using namespace qlnf4;
+
+extern "C" {
+
+size_t nf4_packed_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return static_cast<size_t>((rows * cols + 1) / 2);
+}
+
+int64_t nf4_num_blocks(int64_t rows, int64_t cols, int32_t blocksize) {
+    if (rows <= 0 || cols <= 0 || blocksize <= 0) return 0;
+    return ceil_div(rows * cols, blocksize);
+}
+
+int64_t nf4_dq_num_groups(int64_t n1, int32_t dq_blocksize) {
+    if (n1 <= 0 || dq_blocksize <= 0) return 0;
+    return ceil_div(n1, dq_blocksize);
+}
+
+int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, int32_t blocksize, uint8_t* packed,
+                 float* absmax, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows <= 0 || cols <= 0)
+        return set_error(QL_ERR_SHAPE, "shape %lld x %lld", (long long)rows, (long long)cols);
+    if (blocksize != QL_NF4_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "blocksize %d (only 64 is offered)", blocksize);
+    if (w_dtype != QL_F32 && w_dtype != QL_BF16) return set_error(QL_ERR_UNSUPPORTED, "input dtype %d", w_dtype);
+    int s;
+    if ((s = check_ptr(W, "W")) != QL_OK) return s;
+    if ((s = check_ptr(packed, "packed")) != QL_OK) return s;
+    if ((s = check_ptr(absmax, "absmax")) != QL_OK) return s;
+    return launch_quantize(W, w_dtype == QL_BF16, rows * cols, packed, absmax, static_cast<hipStream_t>(stream));
+}
+
+size_t nf4_double_quant_workspace(int64_t n1) {
+    if (n1 <= 0) return 0;
+    return dq_workspace_bytes(n1);
+}
+
+int nf4_double_quant(const float* absmax, int64_t n1, int32_t dq_blocksize, uint8_t* c8, float* scale, float* mean,
+                     void* ws, size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (n1 <= 0) return set_error(QL_ERR_SHAPE, "n1 = %lld", (long long)n1);
+    if (dq_blocksize != QL_DQ_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "dq_blocksize %d (only 256 is offered)", dq_blocksize);
+    int s;
+    if ((s = check_ptr(absmax, "absmax")) != QL_OK) return s;
+    if ((s = check_ptr(c8, "c8")) != QL_OK) return s;
+    if ((s = check_ptr(scale, "scale")) != QL_OK) return s;
+    if ((s = check_ptr(mean, "mean")) != QL_OK) return s;
+    const size_t need = dq_workspace_bytes(n1);
+    if (ws == nullptr || ws_bytes < need)
+        return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    return launch_double_quant(absmax, n1, c8, scale, mean, static_cast<double*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if ((s = check_weight(w)) != QL_OK) return s;
+    if (out_dtype != QL_F32 && out_dtype != QL_BF16) return set_error(QL_ERR_UNSUPPORTED, "output dtype %d", out_dtype);
+    if ((s = check_ptr(out, "out")) != QL_OK) return s;
+    return launch_dequantize(*w, out, out_dtype == QL_BF16, static_cast<hipStream_t>(stream));
+}
+
+size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    return carve_fwd(nullptr, rows, cols, T, r, false).bytes;
+}
+
+int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A, const uint16_t* B,
+                     int32_t r, float scale, uint16_t* Y, float* U_out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if ((s = check_weight(w)) != QL_OK) return s;
+    if ((s = check_linear_shape(w, T, r)) != QL_OK) return s;
+    if (T == 0) return QL_OK;
+    const int64_t N = w->rows, K = w->cols;
+    if ((s = check_ptr(X, "X")) != QL_OK) return s;
+    if ((s = check_ptr(Y, "Y")) != QL_OK) return s;
+    if (r > 0) {
+        if ((s = check_ptr(A, "A")) != QL_OK) return s;
+        if ((s = check_ptr(B, "B")) != QL_OK) return s;
+        if (U_out != nullptr && (s = check_ptr(U_out, "U_out")) != QL_OK) return s;
+    }
+    const FwdWs need = carve_fwd(nullptr, N, K, T, r, U_out != nullptr);
+    if (need.bytes > 0) {
+        if (ws == nullptr || ws_bytes < need.bytes)
+            return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
+                             need.bytes);
+        if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FwdWs f = carve_fwd(ws, N, K, T, r, U_out != nullptr);
+    const NF4Dev wd = to_dev(w);
+    if (T <= kGemvMaxT) {
+        float* U = U_out ? U_out : f.Uf;
+        if (r > 0) {
+            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U, r, r, 0.0f, nullptr, 0};
+            if ((s = launch_skinny(a, st)) != QL_OK) return s;
+        }
+        if ((s = launch_gemv(wd, X, T, N, K, f.part, st)) != QL_OK) return s;
+        return launch_gemv_reduce(f.part, gemv_num_chunks(K), T, N, U, B, r, scale, Y, st);
+    }
+    const int rp = rank_pad64(r);
+    if (r > 0) {
+        SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U_out, r, U_out ? r : 0, scale, f.Us, rp};
+        if ((s = launch_skinny(a, st)) != QL_OK) return s;
+        if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
+    }
+    return launch_gemm_fwd(wd, X, f.Us, f.Bp, rp, Y, T, N, K, st);
+}
+
+size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    return carve_bwd(nullptr, rows, cols, T, r, true, true, true, false).bytes;
+}
+
+int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float scale, const float* U_saved, uint16_t* dX, float* dA,
+                     float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if ((s = check_weight(w)) != QL_OK) return s;
+    if ((s = check_linear_shape(w, T, r)) != QL_OK) return s;
+    if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_UNSUPPORTED, "accumulate = %d", accumulate);
+    if (r == 0 && (dA != nullptr || dB != nullptr))
+        return set_error(QL_ERR_SHAPE, "dA / dB requested with rank 0");
+    if (T == 0) return QL_OK;
+    const int64_t N = w->rows, K = w->cols;
+    const bool want_dx = dX != nullptr, want_da = dA != nullptr, want_db = dB != nullptr;
+    if (!want_dx && !want_da && !want_db) return QL_OK;
+    if ((s = check_ptr(dY, "dY")) != QL_OK) return s;
+    if (want_dx && (s = check_ptr(dX, "dX")) != QL_OK) return s;
+    if (want_da && (s = check_ptr(dA, "dA")) != QL_OK) return s;
+    if (want_db && (s = check_ptr(dB, "dB")) != QL_OK) return s;
+    if (r > 0) {
+        if ((s = check_ptr(A, "A")) != QL_OK) return s;
+        if ((s = check_ptr(B, "B")) != QL_OK) return s;
+    }
+    const bool have_u = U_saved != nullptr;
+    if (have_u && (s = check_ptr(U_saved, "U_saved")) != QL_OK) return s;
+    if ((want_da || (want_db && !have_u)) && (s = check_ptr(X, "X")) != QL_OK) return s;
+    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db, have_u);
+    if (need.bytes > 0) {
+        if (ws == nullptr || ws_bytes < need.bytes)
+            return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
+                             need.bytes);
+        if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db, have_u);
+    const NF4Dev wd = to_dev(w);
+    const int rp = rank_pad64(r);
+    if (r > 0 && (want_dx || want_da)) {
+        // G = s dY B: skinny GEMM over N with Q = B^T
+        if ((s = launch_transpose_pad(B, N, r, b.BT, N, st)) != QL_OK) return s;
+        SkinnyArgs a{dY, N, b.BT, N, r, T, N, scale, b.Gf, r, r, scale, want_dx ? b.Gp : nullptr, want_dx ? rp : 0};
+        if ((s = launch_skinny(a, st)) != QL_OK) return s;
+    }
+    if (want_dx) {
+        if (r > 0 && (s = launch_transpose_pad(A, r, K, b.Atp, rp, st)) != QL_OK) return s;
+        if ((s = launch_gemm_dx(wd, dY, b.Gp, b.Atp, rp, dX, T, N, K, st)) != QL_OK) return s;
+    }
+    const int rpg = lora_grad_rp(r);
+    if (want_da) {
+        const int sp = lora_grad_splits(T, K);
+        if ((s = launch_lora_grad_partial(X, K, K, b.Gf, r, r, T, sp, b.partA, st)) != QL_OK) return s;
+        if ((s = launch_lora_grad_final(b.partA, sp, rpg, r, K, 1.0f, true, dA, accumulate, st)) != QL_OK) return s;
+    }
+    if (want_db) {
+        const float* U = U_saved;
+        if (!have_u) {
+            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, b.Uf, r, r, 0.0f, nullptr, 0};
+            if ((s = launch_skinny(a, st)) != QL_OK) return s;
+            U = b.Uf;
+        }
+        const int sp = lora_grad_splits(T, N);
+        if ((s = launch_lora_grad_partial(dY, N, N, U, r, r, T, sp, b.partB, st)) != QL_OK) return s;
+        if ((s = launch_lora_grad_final(b.partB, sp, rpg, r, N, scale, false, dB, accumulate, st)) != QL_OK) return s;
+    }
+    return QL_OK;
+}
+
+const char* qlora_status_string(int status) {
+    switch (status) {
+        case QL_OK: return "ok";
+        case QL_ERR_NULL: return "null pointer";
+        case QL_ERR_SHAPE: return "bad shape";
+        case QL_ERR_UNSUPPORTED: return "unsupported option";
+        case QL_ERR_ALIGN: return "misaligned pointer";
+        case QL_ERR_WORKSPACE: return "workspace too small";
+        case QL_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* qlora_last_error(void) { return g_last_error; }
+
+int qlora_timer_arm(int kernel_id) {
+    if (kernel_id <= 0 || kernel_id >= QL_KERNEL_COUNT) return set_error(QL_ERR_UNSUPPORTED, "kernel id %d", kernel_id);
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    g_timers[kernel_id].armed = true;
+    g_timers[kernel_id].used = 0;
+    g_timers[kernel_id].open = false;
+    return QL_OK;
+}
+
+int qlora_timer_read(int kernel_id, int64_t* launches, double* total_ms) {
+    if (kernel_id <= 0 || kernel_id >= QL_KERNEL_COUNT) return set_error(QL_ERR_UNSUPPORTED, "kernel id %d", kernel_id);
+    if (launches == nullptr || total_ms == nullptr) return set_error(QL_ERR_NULL, "output pointer is NULL");
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    TimerState& t = g_timers[kernel_id];
+    double total = 0.0;
+    for (size_t i = 0; i < t.used; ++i) {
+        if (hipEventSynchronize(t.stops[i]) != hipSuccess) return set_error(QL_ERR_HIP, "event synchronize failed");
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, t.starts[i], t.stops[i]) != hipSuccess)
+            return set_error(QL_ERR_HIP, "event elapsed time failed");
+        total += ms;
+    }
+    *launches = static_cast<int64_t>(t.used);
+    *total_ms = total;
+    return QL_OK;
+}
+
+int qlora_timer_disarm(int kernel_id) {
+    if (kernel_id <= 0 || kernel_id >= QL_KERNEL_COUNT) return set_error(QL_ERR_UNSUPPORTED, "kernel id %d", kernel_id);
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    g_timers[kernel_id].armed = false;
+    g_timers[kernel_id].used = 0;
+    g_timers[kernel_id].open = false;
+    return QL_OK;
+}
+
+}  // extern "C"

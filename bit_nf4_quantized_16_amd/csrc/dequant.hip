@@ -1,0 +1,108 @@
+// Dequantization kernel (gfx950): NF4 codes + (double-quantized) absmax ->
+// bf16 or fp32 weights. apxml.com "量化 LoRA (QLoRA) 与 4 位训练": the 4-bit
+// weight is temporarily dequantized to the compute dtype (bfloat16).
+//
+// Compiled with floating-point contraction off: a' = fl(fl(E(c8) * S) + mu)
+// and w' = fl(T[c] * a') round exactly as stated (compared bit for bit).
+#include "common.h"
+#include "internal.h"
+
+namespace qlnf4 {
+
+__constant__ float c_nf4[16] = {
+    kNF4Host[0], kNF4Host[1], kNF4Host[2],  kNF4Host[3],  kNF4Host[4],  kNF4Host[5],  kNF4Host[6],  kNF4Host[7],
+    kNF4Host[8], kNF4Host[9], kNF4Host[10], kNF4Host[11], kNF4Host[12], kNF4Host[13], kNF4Host[14], kNF4Host[15],
+};
+
+// The absmax constant of first-level block b.
+template <bool DQ>
+__device__ __forceinline__ float block_absmax(const float* __restrict__ absmax, const uint8_t* __restrict__ c8,
+                                              const float* __restrict__ scale, float mu, int64_t b) {
+    if (!DQ) return absmax[b];
+    const float prod = e4m3_decode(c8[b]) * scale[b / QL_DQ_BLOCKSIZE];
+    return prod + mu;
+}
+
+// Lane u handles elements [32 u, 32 u + 32): one 16-byte load of codes (half
+// a block), 32 outputs written as four 16-byte (bf16) or eight (fp32) stores.
+// A last partial unit (n not a multiple of 32) is done element by element.
+template <bool DQ, bool BF16_OUT>
+__global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint8_t* __restrict__ packed,
+                                                             const float* __restrict__ absmax,
+                                                             const uint8_t* __restrict__ c8,
+                                                             const float* __restrict__ scale,
+                                                             const float* __restrict__ mean, int64_t n,
+                                                             void* __restrict__ out) {
+    __shared__ float tab[16];
+    if (threadIdx.x < 16) tab[threadIdx.x] = c_nf4[threadIdx.x];
+    __syncthreads();
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t e0 = u * 32;
+    if (e0 >= n) return;
+    const float mu = DQ ? *mean : 0.0f;
+    const float a = block_absmax<DQ>(absmax, c8, scale, mu, e0 / 64);
+    if (e0 + 32 <= n) {
+        const uint4 p = *reinterpret_cast<const uint4*>(packed + e0 / 2);
+        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+        float w[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t byte = (pw[i] >> (8 * j)) & 0xFFu;
+                w[8 * i + 2 * j] = tab[byte >> 4] * a;
+                w[8 * i + 2 * j + 1] = tab[byte & 0xFu] * a;
+            }
+        }
+        if (BF16_OUT) {
+            uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint4 r;
+                r.x = pack_bf16x2(w[8 * q + 0], w[8 * q + 1]);
+                r.y = pack_bf16x2(w[8 * q + 2], w[8 * q + 3]);
+                r.z = pack_bf16x2(w[8 * q + 4], w[8 * q + 5]);
+                r.w = pack_bf16x2(w[8 * q + 6], w[8 * q + 7]);
+                o[q] = r;
+            }
+        } else {
+            float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+        }
+    } else {
+        for (int64_t e = e0; e < n; ++e) {
+            const uint32_t byte = packed[e / 2];
+            const uint32_t c = (e & 1) ? (byte & 0xFu) : (byte >> 4);
+            const float w = tab[c] * a;
+            if (BF16_OUT)
+                static_cast<uint16_t*>(out)[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(w));
+            else
+                static_cast<float*>(out)[e] = w;
+        }
+    }
+}
+
+int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStream_t stream) {
+    const int64_t n = w.rows * w.cols;
+    const int64_t units = ceil_div(n, 32);
+    const dim3 grid(static_cast<uint32_t>(ceil_div(units, 256)));
+    const bool dq = w.dq_blocksize != 0;
+    timer_begin(QL_KERNEL_DEQUANTIZE, stream);
+    if (dq && bf16_out)
+        hipLaunchKernelGGL((nf4_dequantize_kernel<true, true>), grid, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
+                           w.dq_scale, w.dq_mean, n, out);
+    else if (dq)
+        hipLaunchKernelGGL((nf4_dequantize_kernel<true, false>), grid, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
+                           w.dq_scale, w.dq_mean, n, out);
+    else if (bf16_out)
+        hipLaunchKernelGGL((nf4_dequantize_kernel<false, true>), grid, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
+                           w.dq_scale, w.dq_mean, n, out);
+    else
+        hipLaunchKernelGGL((nf4_dequantize_kernel<false, false>), grid, dim3(256), 0, stream, w.packed, w.absmax,
+                           w.c8, w.dq_scale, w.dq_mean, n, out);
+    timer_end(QL_KERNEL_DEQUANTIZE, stream);
+    return check_launch("nf4_dequantize");
+}
+
+}  // namespace qlnf4

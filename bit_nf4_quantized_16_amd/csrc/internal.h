@@ -1,0 +1,72 @@
+// Launchers shared between the kernel files and the C-ABI layer (api.cpp).
+// Every launcher takes already-validated arguments and returns a status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora_nf4.h"
+
+namespace qlnf4 {
+
+// Device view of a quantized weight (all pointers device memory).
+struct NF4Dev {
+    const uint8_t* packed;
+    const float* absmax;  // no double quantization
+    const uint8_t* c8;    // double quantization
+    const float* scale;
+    const float* mean;
+    int dq;
+};
+
+int launch_quantize(const void* W, bool bf16, int64_t n, uint8_t* packed, float* absmax, hipStream_t stream);
+size_t dq_workspace_bytes(int64_t n1);
+int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* scale, float* mean, double* ws,
+                        hipStream_t stream);
+int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStream_t stream);
+
+// out_f[t][j] = alpha_f * sum_k P[t][k] Q[j][k]   (j < ncols_f)
+// out_b[t][j] = bf16(alpha_b * same)              (j < ld_b; zero for j >= qrows)
+struct SkinnyArgs {
+    const uint16_t* P;
+    int64_t ldp;
+    const uint16_t* Q;
+    int64_t ldq;
+    int qrows;
+    int64_t T;
+    int64_t kred;
+    float alpha_f;
+    float* out_f;
+    int64_t ld_f;
+    int ncols_f;
+    float alpha_b;
+    uint16_t* out_b;
+    int64_t ld_b;
+};
+int launch_skinny(const SkinnyArgs& a, hipStream_t stream);
+
+// dst[i][j] = src[i][j] for j < cols, 0 for cols <= j < ldd.
+int launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ldd, hipStream_t stream);
+// dst[c][r] = src[r][c] for r < R, 0 for R <= r < ldd.
+int launch_transpose_pad(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, int64_t ldd, hipStream_t stream);
+
+int gemv_num_chunks(int64_t K);
+int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, float* part, hipStream_t stream);
+int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, const float* U, const uint16_t* B, int r,
+                       float scale, uint16_t* Y, hipStream_t stream);
+
+int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bp, int rp, uint16_t* Y,
+                    int64_t T, int64_t N, int64_t K, hipStream_t stream);
+int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* Atp, int rp, uint16_t* dX,
+                   int64_t T, int64_t N, int64_t K, hipStream_t stream);
+
+int lora_grad_rp(int r);
+int lora_grad_splits(int64_t T, int64_t cols);
+// part[ts][j][c] = sum_{t in split ts} V[t][j] * M[t][c]
+int launch_lora_grad_partial(const uint16_t* M, int64_t ldm, int64_t cols, const float* V, int64_t ldv, int r,
+                             int64_t T, int splits, float* part, hipStream_t stream);
+// out[j][c] (layout_jc) or out[c][j] = (acc ? out : 0) + scale * sum_ts part[ts][j][c]
+int launch_lora_grad_final(const float* part, int splits, int rp, int r, int64_t cols, float scale, bool layout_jc,
+                           float* out, int accumulate, hipStream_t stream);
+
+}  // namespace qlnf4

@@ -1,0 +1,288 @@
+// First- and second-level quantization kernels (gfx950).
+//
+// nf4_quantize: blockwise absmax + nearest NF4 code + nibble packing
+//   (tqpw.cn QLoRA notes, "NormalFloat Quantization (NF4)": normalise each
+//   block to [-1, 1], then quantize; aivaro.ru "Как работает QLoRA", §5:
+//   blocks of 64 weights with fp32 constants).
+// nf4_double_quant: mean-subtracted symmetric FP8 code of the constants at
+//   group size 256 (tqpw.cn QLoRA notes, "Double Quantization").
+//
+// Compiled with floating-point contraction off: every step here rounds
+// exactly as stated (the outputs are compared bit for bit).
+#include "common.h"
+#include "internal.h"
+
+namespace qlnf4 {
+
+__constant__ LutEntry c_lut[kLutBuckets] = {
+    lut_entry(0),  lut_entry(1),  lut_entry(2),  lut_entry(3),  lut_entry(4),  lut_entry(5),  lut_entry(6),
+    lut_entry(7),  lut_entry(8),  lut_entry(9),  lut_entry(10), lut_entry(11), lut_entry(12), lut_entry(13),
+    lut_entry(14), lut_entry(15), lut_entry(16), lut_entry(17), lut_entry(18), lut_entry(19), lut_entry(20),
+    lut_entry(21), lut_entry(22), lut_entry(23), lut_entry(24), lut_entry(25), lut_entry(26), lut_entry(27),
+    lut_entry(28), lut_entry(29), lut_entry(30), lut_entry(31), lut_entry(32),
+};
+
+// Code of a normalised value x (|x| <= 1 up to rounding) from the bucket
+// lookup held in LDS.
+__device__ __forceinline__ uint32_t nf4_code(float x, const LutEntry* lut) {
+    int b = static_cast<int>(x * 16.0f + 16.0f);
+    b = b < 0 ? 0 : (b > kLutBuckets - 1 ? kLutBuckets - 1 : b);
+    LutEntry e = lut[b];
+    return e.base + (x > e.thr ? 1u : 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Main quantize kernel. The input is cut into 1 KiB segments; within a
+// segment lane l holds the 16 bytes at offset 16 l (4 fp32 or 8 bf16 values),
+// so each load instruction of a wave is one contiguous 1 KiB. A 64-element
+// block is then 16 lanes (fp32) or 8 lanes (bf16), reduced with DPP.
+// Each wave takes kSegsPerWave consecutive segments and issues all their
+// loads before any compute.
+// ---------------------------------------------------------------------------
+constexpr int kQuantThreads = 256;
+constexpr int kSegsPerWave = 4;
+constexpr int kSegBytes = 1024;
+
+template <bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t* __restrict__ W, int64_t nseg,
+                                                                   uint8_t* __restrict__ packed,
+                                                                   float* __restrict__ absmax) {
+    constexpr int kPerLane = BF16 ? 8 : 4;           // elements per lane per segment
+    constexpr int kLanesPerBlock = 64 / kPerLane;    // 8 or 16
+    constexpr int kSegElems = 64 * kPerLane;         // 512 or 256
+
+    __shared__ LutEntry lut[kLutBuckets];
+    if (threadIdx.x < kLutBuckets) lut[threadIdx.x] = c_lut[threadIdx.x];
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6);
+    const int64_t seg0 = wave * kSegsPerWave;
+    if (seg0 >= nseg) return;
+
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 v[kSegsPerWave];
+#pragma unroll
+    for (int s = 0; s < kSegsPerWave; ++s) {
+        if (seg0 + s < nseg)
+            v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (seg0 + s) * kSegBytes) + lane);
+    }
+
+#pragma unroll
+    for (int s = 0; s < kSegsPerWave; ++s) {
+        if (seg0 + s >= nseg) break;
+        float e[kPerLane];
+        if (BF16) {
+            const uint32_t w4[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[2 * i] = __uint_as_float(w4[i] << 16);
+                e[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+            }
+        } else {
+            e[0] = __uint_as_float(v[s].x);
+            e[1] = __uint_as_float(v[s].y);
+            e[2] = __uint_as_float(v[s].z);
+            e[3] = __uint_as_float(v[s].w);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) m = fmaxf(m, fabsf(e[i]));
+        m = BF16 ? max8(m) : max16(m);
+        const float inv = m > 0.0f ? 1.0f / m : 0.0f;
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            uint32_t c = nf4_code(e[i] * inv, lut);
+            // element 2j goes to the high nibble of byte j
+            const int byte = i >> 1;
+            const int shift = byte * 8 + ((i & 1) ? 0 : 4);
+            word |= c << shift;
+        }
+        const int64_t elem0 = (seg0 + s) * kSegElems + static_cast<int64_t>(lane) * kPerLane;
+        if (BF16)
+            *reinterpret_cast<uint32_t*>(packed + elem0 / 2) = word;
+        else
+            *reinterpret_cast<uint16_t*>(packed + elem0 / 2) = static_cast<uint16_t>(word);
+        if ((lane % kLanesPerBlock) == 0) absmax[elem0 / 64] = m;
+    }
+}
+
+// Tail: the elements after the last whole segment (fewer than 512), one
+// block per lane of a single wave. Handles a short last block and an odd
+// element count (pad nibble 7).
+template <bool BF16>
+__global__ __launch_bounds__(64) void nf4_quantize_tail(const uint8_t* __restrict__ W, int64_t start, int64_t n,
+                                                        uint8_t* __restrict__ packed, float* __restrict__ absmax) {
+    __shared__ LutEntry lut[kLutBuckets];
+    if (threadIdx.x < kLutBuckets) lut[threadIdx.x] = c_lut[threadIdx.x];
+    __syncthreads();
+    const int64_t b0 = start + static_cast<int64_t>(threadIdx.x) * 64;
+    if (b0 >= n) return;
+    const int64_t len = (n - b0) < 64 ? (n - b0) : 64;
+    auto load = [&](int64_t i) -> float {
+        if (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(W)[i]);
+        return reinterpret_cast<const float*>(W)[i];
+    };
+    float m = 0.0f;
+    for (int64_t i = 0; i < len; ++i) m = fmaxf(m, fabsf(load(b0 + i)));
+    const float inv = m > 0.0f ? 1.0f / m : 0.0f;
+    for (int64_t i = 0; i < len; i += 2) {
+        uint32_t hi = nf4_code(load(b0 + i) * inv, lut);
+        uint32_t lo = (i + 1 < len) ? nf4_code(load(b0 + i + 1) * inv, lut) : 7u;
+        packed[(b0 + i) / 2] = static_cast<uint8_t>((hi << 4) | lo);
+    }
+    absmax[b0 / 64] = m;
+}
+
+int launch_quantize(const void* W, bool bf16, int64_t n, uint8_t* packed, float* absmax, hipStream_t stream) {
+    const int per_lane = bf16 ? 8 : 4;
+    const int64_t seg_elems = 64 * per_lane;
+    const int64_t nseg = n / seg_elems;
+    const uint8_t* wb = static_cast<const uint8_t*>(W);
+    timer_begin(QL_KERNEL_QUANTIZE, stream);
+    if (nseg > 0) {
+        const int64_t waves = ceil_div(nseg, kSegsPerWave);
+        const int64_t grid = ceil_div(waves, kQuantThreads / 64);
+        if (bf16)
+            hipLaunchKernelGGL(nf4_quantize_main<true>, dim3(static_cast<uint32_t>(grid)), dim3(kQuantThreads), 0,
+                               stream, wb, nseg, packed, absmax);
+        else
+            hipLaunchKernelGGL(nf4_quantize_main<false>, dim3(static_cast<uint32_t>(grid)), dim3(kQuantThreads), 0,
+                               stream, wb, nseg, packed, absmax);
+    }
+    timer_end(QL_KERNEL_QUANTIZE, stream);
+    const int64_t start = nseg * seg_elems;
+    if (start < n) {
+        if (bf16)
+            hipLaunchKernelGGL(nf4_quantize_tail<true>, dim3(1), dim3(64), 0, stream, wb, start, n, packed, absmax);
+        else
+            hipLaunchKernelGGL(nf4_quantize_tail<false>, dim3(1), dim3(64), 0, stream, wb, start, n, packed, absmax);
+    }
+    return check_launch("nf4_quantize");
+}
+
+// ---------------------------------------------------------------------------
+// Double quantization
+// ---------------------------------------------------------------------------
+constexpr int kTreeThreads = 256;
+constexpr int kTreePerThread = 16;
+constexpr int kTreeChunk = kTreeThreads * kTreePerThread;  // 4096
+
+// One level of the contiguous pairwise fp64 tree: workgroup g sums the
+// aligned chunk [4096 g, 4096 g + 4096) (zero beyond n) in tree order: pairs
+// inside each thread's 16 values, then xor-butterfly across lanes (lane t
+// and t^d hold the same sum, so the butterfly is the tree), then the four
+// wave sums as (w0 + w1) + (w2 + w3). With a single workgroup the root is
+// the tree sum of everything and the mean is written.
+template <bool F32_IN>
+__global__ __launch_bounds__(kTreeThreads) void dq_tree_level(const void* __restrict__ in, int64_t n,
+                                                              double* __restrict__ out, float* __restrict__ mean,
+                                                              int64_t n_total) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTreeChunk + threadIdx.x * kTreePerThread;
+    double v[kTreePerThread];
+#pragma unroll
+    for (int i = 0; i < kTreePerThread; ++i) {
+        const int64_t idx = base + i;
+        double x = 0.0;
+        if (idx < n) x = F32_IN ? static_cast<double>(static_cast<const float*>(in)[idx])
+                                : static_cast<const double*>(in)[idx];
+        v[i] = x;
+    }
+#pragma unroll
+    for (int w = kTreePerThread / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+    double s = v[0];
+    for (int d = 1; d < 64; d <<= 1) s = s + __shfl_xor(s, d, 64);
+    __shared__ double ws[kTreeThreads / 64];
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double t = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+        out[blockIdx.x] = t;
+        if (mean != nullptr) *mean = static_cast<float>(t / static_cast<double>(n_total));
+    }
+}
+
+// Symmetric E4M3FN code of (a - mean) per group of 256 constants; one wave
+// per group, four groups per workgroup.
+__global__ __launch_bounds__(256) void dq_encode(const float* __restrict__ absmax, int64_t n1,
+                                                 const float* __restrict__ mean_p, uint8_t* __restrict__ c8,
+                                                 float* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (g * QL_DQ_BLOCKSIZE >= n1) return;
+    const float mu = *mean_p;
+    const int64_t i0 = g * QL_DQ_BLOCKSIZE + lane * 4;
+    float d[4];
+    bool valid[4];
+    if (i0 + 3 < n1) {
+        float4 a = *reinterpret_cast<const float4*>(absmax + i0);
+        d[0] = a.x - mu; d[1] = a.y - mu; d[2] = a.z - mu; d[3] = a.w - mu;
+        valid[0] = valid[1] = valid[2] = valid[3] = true;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            valid[i] = (i0 + i) < n1;
+            d[i] = valid[i] ? absmax[i0 + i] - mu : 0.0f;
+        }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, valid[i] ? fabsf(d[i]) : 0.0f);
+    m = wave_max(m);
+    const float S = m / 448.0f;
+    uint32_t code[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) code[i] = (S > 0.0f) ? e4m3_encode_rne(d[i] / S) : 0u;
+    if (i0 + 3 < n1) {
+        *reinterpret_cast<uint32_t*>(c8 + i0) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (valid[i]) c8[i0 + i] = static_cast<uint8_t>(code[i]);
+    }
+    if (lane == 0) scale[g] = S;
+}
+
+size_t dq_workspace_bytes(int64_t n1) {
+    size_t total = 0;
+    int64_t c = n1;
+    do {
+        c = ceil_div(c, kTreeChunk);
+        total += static_cast<size_t>(c);
+    } while (c > 1);
+    return total * sizeof(double);
+}
+
+int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* scale, float* mean, double* ws,
+                        hipStream_t stream) {
+    int64_t count = n1;
+    const void* in = absmax;
+    bool f32 = true;
+    double* out = ws;
+    while (true) {
+        const int64_t grid = ceil_div(count, kTreeChunk);
+        float* mean_out = (grid == 1) ? mean : nullptr;
+        if (f32)
+            hipLaunchKernelGGL(dq_tree_level<true>, dim3(static_cast<uint32_t>(grid)), dim3(kTreeThreads), 0, stream,
+                               in, count, out, mean_out, n1);
+        else
+            hipLaunchKernelGGL(dq_tree_level<false>, dim3(static_cast<uint32_t>(grid)), dim3(kTreeThreads), 0,
+                               stream, in, count, out, mean_out, n1);
+        if (grid == 1) break;
+        in = out;
+        f32 = false;
+        count = grid;
+        out += grid;
+    }
+    const int64_t groups = ceil_div(n1, QL_DQ_BLOCKSIZE);
+    timer_begin(QL_KERNEL_DQ_ENCODE, stream);
+    hipLaunchKernelGGL(dq_encode, dim3(static_cast<uint32_t>(ceil_div(groups, 4))), dim3(256), 0, stream, absmax, n1,
+                       mean, c8, scale);
+    timer_end(QL_KERNEL_DQ_ENCODE, stream);
+    return check_launch("nf4_double_quant");
+}
+
+}  // namespace qlnf4

@@ -1,0 +1,239 @@
+/*
+ * qlora_nf4.h — C ABI of the MI355X (gfx950) QLoRA frozen-base linear layer.
+ *
+ * The library quantizes a frozen weight to blockwise 4-bit NormalFloat (NF4)
+ * with double quantization of its absmax constants, and runs the LoRA linear
+ * layer on it:
+ *
+ *     forward   H  = X * dequant(W)^T + s * (X * A^T) * B^T,   s = alpha / r
+ *     backward  G  = s * dY * B
+ *               dX = dY * dequant(W) + G * A
+ *               dA = G^T * X
+ *               dB = s * dY^T * (X * A^T)
+ *
+ * Sources (web pages on QLoRA, cited by title and section):
+ *   [tqpw]   tqpw.cn QLoRA notes, "Method" > "NormalFloat Quantization (NF4)"
+ *            and "Double Quantization"
+ *   [aivaro] aivaro.ru "Как работает QLoRA (Quantized LoRA) для training?"
+ *   [apxml]  apxml.com "量化 LoRA (QLoRA) 与 4 位训练"
+ *   [codex]  ai-reference-codex "QLoRA 与 PEFT 全家"
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major. W is [rows = N, cols = K] (out x in features,
+ *     aivaro §2: W in R^{d x k}); X is [T, K]; A is [r, K]; B is [N, r];
+ *     H and dY are [T, N].
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - Every pointer except the ql_nf4_weight descriptor itself is a device
+ *     pointer. The caller owns all buffers; the library never allocates,
+ *     frees or keeps a pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *     asynchronous on it; buffers must stay alive until the work completes.
+ *     Calls are re-entrant; calls that share output or workspace buffers on
+ *     different streams race.
+ *   - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
+ *   - All arguments are validated before anything is launched; on an error
+ *     nothing is written. No C++ exception crosses this interface.
+ *     qlora_last_error() gives a message for the calling thread.
+ *   - Results are bitwise reproducible run to run (no floating-point
+ *     atomics).
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define QL_OK 0
+#define QL_ERR_NULL (-1)        /* a required pointer is NULL             */
+#define QL_ERR_SHAPE (-2)       /* a size is out of range                 */
+#define QL_ERR_UNSUPPORTED (-3) /* blocksize, dtype or option not offered */
+#define QL_ERR_ALIGN (-4)       /* a device pointer is not 16-B aligned   */
+#define QL_ERR_WORKSPACE (-5)   /* workspace missing or too small         */
+#define QL_ERR_HIP (-6)         /* the HIP runtime reported an error      */
+
+/* ---- element types ----------------------------------------------------- */
+#define QL_F32 0
+#define QL_BF16 1
+
+/* First-level block size: 64 weights share one absmax constant
+ * ([aivaro] §5; [tqpw] "Double Quantization": NF4 at g64). */
+#define QL_NF4_BLOCKSIZE 64
+/* Second-level group size: 256 absmax constants share one fp32 scale
+ * ([tqpw] "Double Quantization": FP8 at g256). */
+#define QL_DQ_BLOCKSIZE 256
+/* Largest LoRA rank the kernels take ([aivaro] §10 uses r = 8..64). */
+#define QL_MAX_RANK 128
+
+/*
+ * A quantized frozen weight. The struct itself is host memory; its pointers
+ * are device pointers.
+ *   packed   [ceil(rows*cols/2)] bytes: the NF4 code of element e of the
+ *            row-major flattening sits in byte e/2, high nibble for even e.
+ *            Code c means the c-th of the sixteen NF4 values in ascending
+ *            order ([tqpw] NF4: the printed list).
+ *   Without double quantization (dq_blocksize == 0):
+ *     absmax [ceil(rows*cols/64)] fp32, one per block of 64 elements.
+ *   With double quantization (dq_blocksize == 256):
+ *     c8       [nblocks] OCP FP8 E4M3FN codes of (absmax - mean) / scale
+ *     dq_scale [ceil(nblocks/256)] fp32
+ *     dq_mean  [1] fp32
+ */
+typedef struct ql_nf4_weight {
+    int64_t rows;
+    int64_t cols;
+    int32_t blocksize;    /* must be 64 */
+    int32_t dq_blocksize; /* 256, or 0 for no double quantization */
+    const uint8_t* packed;
+    const float* absmax;
+    const uint8_t* c8;
+    const float* dq_scale;
+    const float* dq_mean;
+} ql_nf4_weight;
+
+/* ---- sizes ------------------------------------------------------------- */
+/* Bytes of the packed codes for rows x cols weights. */
+size_t nf4_packed_bytes(int64_t rows, int64_t cols);
+/* Number of first-level blocks (= absmax constants = c8 codes). */
+int64_t nf4_num_blocks(int64_t rows, int64_t cols, int32_t blocksize);
+/* Number of second-level groups (= dq_scale entries) for n1 constants. */
+int64_t nf4_dq_num_groups(int64_t n1, int32_t dq_blocksize);
+
+/*
+ * nf4_quantize — first-level blockwise NF4 quantization ([tqpw] NF4: weights
+ * are normalised to [-1, 1] per block and mapped to the nearest NF4 value;
+ * [aivaro] §5: blocks of 64 weights, fp32 constants).
+ *
+ *   W        [rows, cols] row-major, fp32 (w_dtype QL_F32) or bf16 (QL_BF16)
+ *   packed   out, nf4_packed_bytes(rows, cols) bytes
+ *   absmax   out, nf4_num_blocks(rows, cols, 64) fp32
+ *
+ * Per block of 64 consecutive elements of the row-major flattening (the last
+ * block may be shorter): a = max|w|; x = fl32(w * fl32(1/a)); code = the
+ * index of the nearest NF4 value to x, the lower index on an exact tie; a
+ * block with a = 0 gets code 7 (the value 0). An odd element count pads the
+ * last low nibble with 7. Inputs must be finite; a block whose absmax is
+ * subnormal gets unspecified codes (no crash).
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (rows or cols <= 0), QL_ERR_UNSUPPORTED
+ * (blocksize != 64, unknown dtype), QL_ERR_ALIGN, QL_ERR_HIP.
+ */
+int nf4_quantize(const void* W, int w_dtype, int64_t rows, int64_t cols, int32_t blocksize,
+                 uint8_t* packed, float* absmax, void* stream);
+
+/*
+ * nf4_double_quant — second-level quantization of the fp32 absmax constants
+ * ([tqpw] "Double Quantization": FP8 at group size 256 after subtracting the
+ * mean, then symmetric; [apxml]: constants go from 32 to 8 bits).
+ *
+ *   absmax   [n1] fp32 (from nf4_quantize)
+ *   c8       out [n1] E4M3FN codes
+ *   scale    out [ceil(n1/256)] fp32
+ *   mean     out [1] fp32
+ *   ws       workspace of nf4_double_quant_workspace(n1) bytes
+ *
+ * mean = fl32(S / n1), S the fp64 sum of the constants over a contiguous
+ * pairwise tree (zero-padded to a power of two, neighbours added level by
+ * level); d = fl32(a - mean); per group s = max|d|, scale = fl32(s / 448);
+ * c8 = E4M3FN(fl32(d / scale)) rounded to nearest even with the sign kept; a
+ * group with scale 0 gets codes 0x00.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (n1 <= 0), QL_ERR_UNSUPPORTED
+ * (dq_blocksize != 256), QL_ERR_ALIGN, QL_ERR_WORKSPACE, QL_ERR_HIP.
+ */
+size_t nf4_double_quant_workspace(int64_t n1);
+int nf4_double_quant(const float* absmax, int64_t n1, int32_t dq_blocksize, uint8_t* c8,
+                     float* scale, float* mean, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nf4_dequantize — expand the quantized weight to the compute dtype ([apxml]:
+ * the 4-bit weight is temporarily dequantized to bfloat16 for the matmul).
+ *
+ *   out   [rows, cols] row-major, bf16 (out_dtype QL_BF16) or fp32 (QL_F32)
+ *
+ * a' = fl32(fl32(E4M3(c8) * scale) + mean) with double quantization, else
+ * a' = absmax; w' = fl32(NF4[code] * a'), then rounded to bf16 to nearest
+ * even for the bf16 output.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_UNSUPPORTED, QL_ERR_ALIGN,
+ * QL_ERR_HIP.
+ */
+int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* stream);
+
+/*
+ * qlora_linear_fwd — forward of the frozen-base LoRA linear layer ([apxml]:
+ * h = dequant(W_NF4) x + B A x; [aivaro] §2: B in R^{d x r}, A in R^{r x k};
+ * the scale s = alpha / r is the LoRA scaling factor).
+ *
+ *   X      [T, K] bf16        A  [r, K] bf16      B  [N, r] bf16
+ *   Y      out [T, N] bf16:   Y = X W'^T + s (X A^T) B^T, fp32 accumulation
+ *   U_out  optional out [T, r] fp32 = X A^T (saved for the backward), or NULL
+ *   ws     workspace of qlora_linear_fwd_workspace(...) bytes (may be NULL
+ *          when that size is 0)
+ *
+ * r == 0 (A and B may then be NULL) runs the base matmul alone. T <= 16 takes
+ * the dequant-GEMV kernels, larger T the dequant-in-LDS MFMA GEMM.
+ * K must be a multiple of 64. Y must not alias any input.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (T < 0, K % 64 != 0, r < 0 or
+ * r > QL_MAX_RANK), QL_ERR_UNSUPPORTED, QL_ERR_ALIGN, QL_ERR_WORKSPACE,
+ * QL_ERR_HIP. T == 0 is a no-op.
+ */
+size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
+int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float scale, uint16_t* Y, float* U_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd — backward of the layer ([aivaro] §7: gradients flow
+ * through the 4-bit weight, dequantized on the fly, and only the adapters
+ * are updated).
+ *
+ *   dY       [T, N] bf16 upstream gradient
+ *   U_saved  optional [T, r] fp32 = X A^T from the forward; NULL recomputes it
+ *   dX       optional out [T, K] bf16 = dY W' + G A, G = s dY B
+ *   dA       optional out [r, K] fp32 = G^T X
+ *   dB       optional out [N, r] fp32 = s dY^T U
+ *   accumulate  0: dA and dB are overwritten; 1: the gradients are added to
+ *               their current contents (gradient accumulation)
+ *
+ * Any of dX, dA, dB may be NULL to skip it. X is needed for dA and when
+ * U_saved is NULL. K must be a multiple of 64. Outputs must not alias inputs.
+ * Errors: as qlora_linear_fwd.
+ */
+size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
+int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T,
+                     const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                     const float* U_saved, uint16_t* dX, float* dA, float* dB, int accumulate,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---- diagnostics ------------------------------------------------------- */
+/* Static text for a status code. */
+const char* qlora_status_string(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* qlora_last_error(void);
+
+/*
+ * Kernel timers (a profiling aid). While a timer is armed for a kernel, the
+ * library records a pair of HIP events on the launch stream around every
+ * launch of that kernel. qlora_timer_read() waits for the recorded events and
+ * returns the number of launches and their summed duration. Kernel ids are
+ * the QL_KERNEL_* values. Not meant to be armed from several threads at once.
+ */
+#define QL_KERNEL_QUANTIZE 1
+#define QL_KERNEL_DQ_ENCODE 2
+#define QL_KERNEL_DEQUANTIZE 3
+#define QL_KERNEL_GEMV 4
+#define QL_KERNEL_GEMM_FWD 5
+#define QL_KERNEL_GEMM_DX 6
+#define QL_KERNEL_LORA_GRAD 7
+#define QL_KERNEL_COUNT 8
+int qlora_timer_arm(int kernel_id);
+int qlora_timer_read(int kernel_id, int64_t* launches, double* total_ms);
+int qlora_timer_disarm(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,176 @@
+"""The C-ABI library loads, exports every function include/qlora_nf4.h
+declares, and rejects bad arguments before launching anything (so these
+run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+LIB = os.path.join(ROOT, "bit_nf4_quantized_16_amd", "libqlora_nf4.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_nf4_quantized_16_amd import _lib
+
+    return _lib.load(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 16
+    from bit_nf4_quantized_16_amd import _lib
+
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, "binding lacks " + n
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        s = lib.qlora_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.qlora_status_string(-99).decode() == "unknown status"
+
+
+def test_size_helpers(lib):
+    assert lib.nf4_packed_bytes(4096, 4096) == 4096 * 4096 // 2
+    assert lib.nf4_packed_bytes(3, 5) == 8
+    assert lib.nf4_num_blocks(4096, 4096, 64) == 262144
+    assert lib.nf4_num_blocks(1, 65, 64) == 2
+    assert lib.nf4_dq_num_groups(262144, 256) == 1024
+    assert lib.nf4_dq_num_groups(257, 256) == 2
+    assert lib.nf4_double_quant_workspace(1024) >= 8
+    assert lib.qlora_linear_fwd_workspace(4096, 4096, 1024, 16) > 0
+    assert lib.qlora_linear_bwd_workspace(4096, 4096, 1024, 16) > 0
+
+
+# fake, 16-byte aligned device addresses: validation never dereferences them
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10004)
+
+
+def _err(lib):
+    return lib.qlora_last_error().decode()
+
+
+def test_quantize_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    assert lib.nf4_quantize(None, L.QL_F32, 4, 64, 64, P2, P3, None) == L.QL_ERR_NULL
+    assert "W" in _err(lib)
+    assert lib.nf4_quantize(P, L.QL_F32, 0, 64, 64, P2, P3, None) == L.QL_ERR_SHAPE
+    assert lib.nf4_quantize(P, L.QL_F32, 4, -1, 64, P2, P3, None) == L.QL_ERR_SHAPE
+    assert lib.nf4_quantize(P, L.QL_F32, 4, 64, 32, P2, P3, None) == L.QL_ERR_UNSUPPORTED
+    assert lib.nf4_quantize(P, 7, 4, 64, 64, P2, P3, None) == L.QL_ERR_UNSUPPORTED
+    assert lib.nf4_quantize(MIS, L.QL_F32, 4, 64, 64, P2, P3, None) == L.QL_ERR_ALIGN
+    assert lib.nf4_quantize(P, L.QL_BF16, 4, 64, 64, None, P3, None) == L.QL_ERR_NULL
+
+
+def test_double_quant_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    need = lib.nf4_double_quant_workspace(1000)
+    assert lib.nf4_double_quant(P, 0, 256, P2, P3, P, P, need, None) == L.QL_ERR_SHAPE
+    assert lib.nf4_double_quant(P, 1000, 128, P2, P3, P, P, need, None) == L.QL_ERR_UNSUPPORTED
+    assert lib.nf4_double_quant(P, 1000, 256, None, P3, P, P, need, None) == L.QL_ERR_NULL
+    assert lib.nf4_double_quant(P, 1000, 256, P2, P3, P, P, need - 1, None) == L.QL_ERR_WORKSPACE
+    assert lib.nf4_double_quant(P, 1000, 256, P2, P3, P, None, need, None) == L.QL_ERR_WORKSPACE
+    assert lib.nf4_double_quant(P, 1000, 256, P2, P3, MIS, P, need, None) == L.QL_ERR_ALIGN
+
+
+def _weight(L, rows=256, cols=256, dq=256, **over):
+    w = L.QlNf4Weight()
+    w.rows, w.cols, w.blocksize, w.dq_blocksize = rows, cols, 64, dq
+    w.packed, w.absmax, w.c8, w.dq_scale, w.dq_mean = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    for k, v in over.items():
+        setattr(w, k, v)
+    return ctypes.byref(w)
+
+
+def test_dequantize_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    assert lib.nf4_dequantize(None, P, L.QL_BF16, None) == L.QL_ERR_NULL
+    assert lib.nf4_dequantize(_weight(L, rows=0), P, L.QL_BF16, None) == L.QL_ERR_SHAPE
+    assert lib.nf4_dequantize(_weight(L, blocksize=128), P, L.QL_BF16, None) == L.QL_ERR_UNSUPPORTED
+    assert lib.nf4_dequantize(_weight(L, dq_blocksize=64), P, L.QL_BF16, None) == L.QL_ERR_UNSUPPORTED
+    assert lib.nf4_dequantize(_weight(L, c8=None), P, L.QL_BF16, None) == L.QL_ERR_NULL
+    assert lib.nf4_dequantize(_weight(L, dq=0, absmax=None), P, L.QL_BF16, None) == L.QL_ERR_NULL
+    assert lib.nf4_dequantize(_weight(L, packed=0x10008), P, L.QL_BF16, None) == L.QL_ERR_ALIGN
+    assert lib.nf4_dequantize(_weight(L), P, 5, None) == L.QL_ERR_UNSUPPORTED
+    assert lib.nf4_dequantize(_weight(L), None, L.QL_BF16, None) == L.QL_ERR_NULL
+
+
+def test_linear_fwd_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    need = lib.qlora_linear_fwd_workspace(256, 256, 64, 8)
+    ok = dict(X=P, T=64, A=P2, B=P3, r=8, Y=P, U=None, ws=P, wsb=need)
+
+    def call(w=None, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.qlora_linear_fwd(w if w is not None else _weight(L), a["X"], a["T"], a["A"], a["B"], a["r"],
+                                    2.0, a["Y"], a["U"], a["ws"], a["wsb"], None)
+
+    assert call(w=_weight(L, cols=96)) == L.QL_ERR_SHAPE  # K % 64
+    assert call(w=_weight(L, rows=100)) == L.QL_ERR_SHAPE  # N % 8
+    assert call(T=-1) == L.QL_ERR_SHAPE
+    assert call(r=129) == L.QL_ERR_SHAPE
+    assert call(r=-1) == L.QL_ERR_SHAPE
+    assert call(X=None) == L.QL_ERR_NULL
+    assert call(A=None) == L.QL_ERR_NULL
+    assert call(Y=MIS) == L.QL_ERR_ALIGN
+    assert call(wsb=need - 1) == L.QL_ERR_WORKSPACE
+    assert call(ws=None) == L.QL_ERR_WORKSPACE
+    assert call(T=0) == L.QL_OK  # empty batch: no-op, nothing launched
+
+
+def test_linear_bwd_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    need = lib.qlora_linear_bwd_workspace(256, 256, 64, 8)
+
+    def call(w=None, X=P, dY=P2, T=64, A=P3, B=P, r=8, U=None, dX=P, dA=P2, dB=P3, acc=0, ws=P, wsb=need):
+        return lib.qlora_linear_bwd(w if w is not None else _weight(L), X, dY, T, A, B, r, 2.0, U, dX, dA, dB, acc,
+                                    ws, wsb, None)
+
+    assert call(w=_weight(L, cols=100)) == L.QL_ERR_SHAPE
+    assert call(acc=2) == L.QL_ERR_UNSUPPORTED
+    assert call(r=0) == L.QL_ERR_SHAPE  # dA/dB requested without adapters
+    assert call(dY=None) == L.QL_ERR_NULL
+    assert call(X=None) == L.QL_ERR_NULL  # dA needs X
+    assert call(dA=MIS) == L.QL_ERR_ALIGN
+    assert call(wsb=100) == L.QL_ERR_WORKSPACE
+    assert call(T=0) == L.QL_OK
+    assert call(dX=None, dA=None, dB=None) == L.QL_OK  # nothing requested
+
+
+def test_timer_ids(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    assert lib.qlora_timer_arm(0) == L.QL_ERR_UNSUPPORTED
+    assert lib.qlora_timer_arm(99) == L.QL_ERR_UNSUPPORTED
+    assert lib.qlora_timer_arm(L.QL_KERNEL_GEMM_FWD) == L.QL_OK
+    n = ctypes.c_int64(-1)
+    ms = ctypes.c_double(-1)
+    assert lib.qlora_timer_read(L.QL_KERNEL_GEMM_FWD, ctypes.byref(n), ctypes.byref(ms)) == L.QL_OK
+    assert n.value == 0 and ms.value == 0.0
+    assert lib.qlora_timer_disarm(L.QL_KERNEL_GEMM_FWD) == L.QL_OK

@@ -1,0 +1,176 @@
+"""GPU parity of the LoRA linear layer on the NF4 base (forward: dequant-GEMV
+for T <= 16, dequant-in-LDS MFMA GEMM above; backward: transposed dequant
+GEMM for dX and the LoRA gradients) against the fp64 CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, bf16_to_np, f32_to_np, normwise_rel_err, oracle_weight
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import bit_nf4_quantized_16_amd as qn
+
+    assert torch.cuda.is_available()
+    return qn
+
+
+def _run(qn, case, W=None, dq=True, accumulate_from=None):
+    """Quantize case.W on the GPU, run forward and backward, compare all
+    outputs with the oracle. Returns the errors."""
+    W = case.W if W is None else W
+    w = qn.quantize_weight(W.contiguous().cuda(), double_quant=dq)
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    s = case.scale
+    Y, U = qn.qlora_linear_fwd(w, X, A, B, s)
+    dX, dA, dB = qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U)
+    torch.cuda.synchronize()
+    ref = oracle_weight(W.numpy(), double_quant=dq)
+    Xn, dYn, An, Bn = (bf16_to_np(t) for t in (case.X, case.dY, case.A, case.B))
+    H, Uo = oracle.lora_forward(Xn, ref["wd"], An, Bn, s)
+    dXo, dAo, dBo, _, _ = oracle.lora_backward(Xn, dYn, ref["wd"], An, Bn, s)
+    errs = dict(
+        H=normwise_rel_err(bf16_to_np(Y), H),
+        U=normwise_rel_err(f32_to_np(U), Uo),
+        dX=normwise_rel_err(bf16_to_np(dX), dXo),
+        dA=normwise_rel_err(f32_to_np(dA), dAo),
+        dB=normwise_rel_err(f32_to_np(dB), dBo),
+    )
+    for k, v in errs.items():
+        assert v <= TOL, "%s: %s error %.3e > %.0e (%s)" % (case.name, k, v, TOL, errs)
+    return errs, (w, X, dY, A, B, Y, dX, dA, dB)
+
+
+def test_tiny_256_config(qn):
+    errs, _ = _run(qn, workloads.tiny_256())
+    # the oracle's reduction is fp64 and the inputs bf16: the remaining error is
+    # the bf16 rounding of the outputs, far inside the bar
+    assert errs["H"] < 5e-3 and errs["dX"] < 5e-3
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 17, 31, 128, 300])
+def test_token_counts_cross_gemv_and_gemm(qn, T):
+    W = workloads.normal_weight(256, 320, 0.02, seed=T)
+    case = workloads.lora_case("T%d" % T, W, T, 8, 16.0, 1 / 320, 0.05, seed=T)
+    _run(qn, case)
+
+
+@pytest.mark.parametrize("N,K,T,r", [(200, 320, 300, 5), (136, 64, 129, 1), (8, 128, 3, 3), (520, 1088, 257, 70),
+                                     (264, 192, 40, 128), (64, 64, 1, 16)])
+def test_ragged_shapes_and_ranks(qn, N, K, T, r):
+    W = workloads.normal_weight(N, K, 0.02, seed=N + K)
+    case = workloads.lora_case("N%dK%dT%dr%d" % (N, K, T, r), W, T, r, 2.0 * r, 1 / K, 0.05, seed=N * 7 + T)
+    _run(qn, case)
+
+
+def test_without_double_quant(qn):
+    case = workloads.tiny_256()
+    _run(qn, case, dq=False)
+    W = workloads.normal_weight(384, 512, 0.02, seed=5)
+    _run(qn, workloads.lora_case("nodq_gemm", W, 200, 16, 32.0, 1 / 512, 0.05, seed=5), dq=False)
+
+
+@pytest.mark.parametrize("T", [4, 96])
+def test_zero_base_isolates_the_lora_branch(qn, T):
+    # an all-zero W quantizes to code 7 (value 0): H = s U B^T and dX = G A
+    # exactly in the oracle, so a broken LoRA branch cannot hide under the base
+    W = torch.zeros(256, 256)
+    case = workloads.lora_case("zeroW", W, T, 8, 16.0, 1 / 16, 0.5, seed=11)
+    errs, _ = _run(qn, case)
+    assert errs["H"] < 1e-2 and errs["dX"] < 1e-2
+
+
+@pytest.mark.parametrize("T", [4, 160])
+def test_big_adapter_variant(qn, T):
+    W = workloads.normal_weight(256, 256, 0.02, seed=12)
+    case = workloads.lora_case("bigB", W, T, 8, 16.0, 1 / 16, 1.0, seed=12)
+    _run(qn, case)
+
+
+@pytest.mark.parametrize("T", [8, 256])
+def test_rank_zero_is_the_base_matmul(qn, T):
+    W = workloads.normal_weight(256, 512, 0.02, seed=13)
+    w = qn.quantize_weight(W.cuda())
+    X = workloads.bf16_normal((T, 512), 1.0, 14).cuda()
+    dY = workloads.bf16_normal((T, 256), 1.0, 15).cuda()
+    Y, U = qn.qlora_linear_fwd(w, X)
+    dX, dA, dB = qn.qlora_linear_bwd(w, None, dY)
+    assert U is None and dA is None and dB is None
+    ref = oracle_weight(W.numpy())
+    assert normwise_rel_err(bf16_to_np(Y), bf16_to_np(X).astype(np.float64) @ ref["wd"].T) <= TOL
+    assert normwise_rel_err(bf16_to_np(dX), bf16_to_np(dY).astype(np.float64) @ ref["wd"]) <= TOL
+
+
+@pytest.mark.parametrize("T", [16, 512])
+def test_fused_matmul_matches_torch_on_dequantized_weight(qn, T):
+    """Library-routine check: the fused kernels against torch.matmul on the
+    nf4_dequantize output (same W', fp32 matmul), at a tight tolerance."""
+    W = workloads.normal_weight(1024, 2048, 0.02, seed=16)
+    w = qn.quantize_weight(W.cuda())
+    Wd = qn.nf4_dequantize(w).float()
+    X = workloads.bf16_normal((T, 2048), 1.0, 17).cuda()
+    dY = workloads.bf16_normal((T, 1024), 1.0, 18).cuda()
+    Y, _ = qn.qlora_linear_fwd(w, X)
+    dX, _, _ = qn.qlora_linear_bwd(w, None, dY)
+    Yr = X.float() @ Wd.T
+    dXr = dY.float() @ Wd
+    assert normwise_rel_err(bf16_to_np(Y), Yr.cpu().numpy()) < 4e-3
+    assert normwise_rel_err(bf16_to_np(dX), dXr.cpu().numpy()) < 4e-3
+
+
+def test_bitwise_deterministic(qn):
+    W = workloads.normal_weight(512, 512, 0.02, seed=19)
+    case = workloads.lora_case("det", W, 300, 16, 32.0, 1 / 512, 0.05, seed=19)
+    _, o1 = _run(qn, case)
+    _, o2 = _run(qn, case)
+    for a, b in zip(o1[5:], o2[5:]):
+        assert torch.equal(a, b)
+
+
+def test_gradient_accumulation(qn):
+    W = workloads.normal_weight(256, 256, 0.02, seed=20)
+    case = workloads.lora_case("acc", W, 64, 8, 16.0, 1 / 256, 0.05, seed=20)
+    w = qn.quantize_weight(W.cuda())
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    _, dA1, dB1 = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, need_dx=False)
+    dA = dA1.clone()
+    dB = dB1.clone()
+    qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, need_dx=False, dA=dA, dB=dB, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dA, dA1 + dA1) and torch.equal(dB, dB1 + dB1)
+
+
+def test_autograd_function(qn):
+    W = workloads.normal_weight(256, 256, 0.02, seed=21)
+    case = workloads.lora_case("autograd", W, 48, 8, 16.0, 1 / 256, 0.05, seed=21)
+    w = qn.quantize_weight(W.cuda())
+    X = case.X.cuda().requires_grad_(True)
+    A = case.A.cuda().requires_grad_(True)
+    B = case.B.cuda().requires_grad_(True)
+    Y = qn.QLoRALinearFunction.apply(X, A, B, w, case.scale)
+    Y.backward(case.dY.cuda())
+    ref = oracle_weight(W.numpy())
+    Xn, dYn, An, Bn = (bf16_to_np(t) for t in (case.X, case.dY, case.A, case.B))
+    dXo, dAo, dBo, _, _ = oracle.lora_backward(Xn, dYn, ref["wd"], An, Bn, case.scale)
+    assert normwise_rel_err(bf16_to_np(X.grad), dXo) <= TOL
+    assert normwise_rel_err(bf16_to_np(A.grad), dAo) <= TOL
+    assert normwise_rel_err(bf16_to_np(B.grad), dBo) <= TOL
+
+
+def test_frozen_base_is_not_written(qn):
+    W = workloads.normal_weight(256, 256, 0.02, seed=22)
+    case = workloads.lora_case("frozen", W, 64, 8, 16.0, 1 / 256, 0.05, seed=22)
+    w = qn.quantize_weight(W.cuda())
+    before = [t.clone() for t in (w.packed, w.c8, w.dq_scale, w.dq_mean)]
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    Y, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, U=U)
+    torch.cuda.synchronize()
+    for a, b in zip(before, (w.packed, w.c8, w.dq_scale, w.dq_mean)):
+        assert torch.equal(a, b)

@@ -1,0 +1,180 @@
+"""GPU parity of the storage format: nf4_quantize, nf4_double_quant and
+nf4_dequantize against the CPU oracle, bit for bit, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import bf16_bits_np, f32_to_np, oracle_weight, u8_to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import bit_nf4_quantized_16_amd as qn
+
+    assert torch.cuda.is_available()
+    return qn
+
+
+def _check_quantize(qn, W_cpu, dtype=torch.float32):
+    Wd = W_cpu.to(dtype).contiguous().cuda()
+    packed, absmax = qn.nf4_quantize(Wd)
+    torch.cuda.synchronize()
+    Wnp = W_cpu.to(dtype).float().numpy()
+    p_ref, a_ref = oracle.quantize(Wnp)
+    got_p, got_a = u8_to_np(packed), f32_to_np(absmax)
+    assert got_a.size == a_ref.size and got_p.size == p_ref.size
+    bad = np.nonzero(got_p != p_ref)[0]
+    assert bad.size == 0, "packed mismatch at bytes %s" % bad[:10]
+    assert np.array_equal(got_a.view(np.uint32), a_ref.view(np.uint32))
+    return packed, absmax
+
+
+SHAPES = [(256, 256), (1, 1), (1, 2), (1, 63), (1, 64), (1, 65), (3, 100), (7, 33), (5, 1000), (513, 77),
+          (2, 256), (2, 257), (1, 1024 + 64 * 3 + 5), (64, 4096), (37, 511)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_matches_oracle(qn, shape, dtype):
+    W = workloads.normal_weight(shape[0], shape[1], 0.02, seed=shape[0] * 1000 + shape[1])
+    _check_quantize(qn, W, dtype)
+
+
+def test_quantize_tiny_256_config(qn):
+    case = workloads.tiny_256()
+    _check_quantize(qn, case.W)
+
+
+def test_quantize_attn_7b_with_outliers_full(qn):
+    W = workloads.normal_weight(4096, 4096, 0.02, seed=1, outlier_frac=1e-3, outlier_scale=20.0)
+    _check_quantize(qn, W)
+    _check_quantize(qn, W, torch.bfloat16)
+
+
+def test_quantize_every_fp32_near_every_midpoint(qn):
+    # blocks whose absmax is exactly 1 (element 0), so the normalised value is
+    # the weight itself; all fp32 values within 3000 ulps of each midpoint,
+    # and of each code value, plus signed zeros and subnormals
+    T = oracle.NF4_PRINTED.astype(np.float64)
+    vals = []
+    for j in range(15):
+        m = np.float32((T[j] + T[j + 1]) / 2).view(np.int32)
+        r = (np.arange(-3000, 3001, dtype=np.int64) + int(m)).astype(np.int32).view(np.float32)
+        vals.append(r[np.abs(r) <= 1])
+    for t in T:
+        r = (np.arange(-300, 301, dtype=np.int64) + int(np.float32(t).view(np.int32))).astype(np.int32)
+        v = r.view(np.float32)
+        vals.append(v[np.abs(v) <= 1])
+    vals.append(np.array([0.0, -0.0, 1e-45, -1e-45, 1e-39, -1e-39], dtype=np.float32))
+    x = np.concatenate(vals)
+    per = 63
+    nb = -(-x.size // per)
+    buf = np.zeros((nb, 64), dtype=np.float32)
+    buf[:, 0] = 1.0
+    flat = np.zeros(nb * per, dtype=np.float32)
+    flat[: x.size] = x
+    buf[:, 1:] = flat.reshape(nb, per)
+    _check_quantize(qn, torch.from_numpy(buf))
+
+
+def test_quantize_special_blocks(qn):
+    rng = np.random.default_rng(7)
+    W = (rng.standard_normal((64, 640)) * 0.02).astype(np.float32)
+    W[0, :64] = 0.0  # all-zero block
+    W[1, :64] = -0.0
+    W[2, 64:128] = 3.0  # constant block
+    W[3, :64] = np.float32(2.0**-100) * rng.standard_normal(64).astype(np.float32)  # tiny but normal
+    W[4, 128:192] = np.array([1e30, -1e30] * 32, dtype=np.float32)  # huge
+    W[5, :] = np.where(rng.random(640) < 0.5, 1.0, -1.0)
+    _check_quantize(qn, torch.from_numpy(W))
+
+
+def test_quantize_power_of_two_grid_roundtrip(qn):
+    # W = T[c] * 2^e: the quantizer must recover the codes exactly
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 16, size=(128, 64)).astype(np.uint8)
+    codes[:, 0] = 15
+    e = rng.integers(-30, 10, size=128)
+    W = (oracle.NF4_PRINTED[codes] * (2.0 ** e)[:, None].astype(np.float32)).astype(np.float32)
+    packed, absmax = _check_quantize(qn, torch.from_numpy(W.reshape(16, 512)))
+    assert np.array_equal(oracle.unpack_nibbles(u8_to_np(packed), W.size), codes.ravel())
+
+
+def _check_dq(qn, absmax_np):
+    a = torch.from_numpy(absmax_np).cuda()
+    c8, scale, mean = qn.nf4_double_quant(a)
+    torch.cuda.synchronize()
+    c_ref, s_ref, m_ref = oracle.double_quant(absmax_np)
+    assert f32_to_np(mean)[0].view(np.uint32) == np.float32(m_ref).view(np.uint32)
+    assert np.array_equal(f32_to_np(scale).view(np.uint32), s_ref.view(np.uint32))
+    got = u8_to_np(c8)
+    bad = np.nonzero(got != c_ref)[0]
+    assert bad.size == 0, "c8 mismatch at %s: got %s want %s" % (bad[:8], got[bad[:8]], c_ref[bad[:8]])
+
+
+@pytest.mark.parametrize("n1", [1, 2, 5, 255, 256, 257, 1024, 4095, 4096, 4097, 12345, 262144, 704512])
+def test_double_quant_matches_oracle(qn, n1):
+    rng = np.random.default_rng(n1)
+    a = np.abs(rng.standard_normal(n1) * 0.02 + 0.05).astype(np.float32) + np.float32(1e-3)
+    _check_dq(qn, a)
+
+
+def test_double_quant_special_groups(qn):
+    a = np.full(1024, 0.0371, dtype=np.float32)  # constant: scale 0, codes 0
+    a[512:768] = np.array([1.0] * 127 + [3.0] * 127 + [2.0 - 2**-22, 2.0 + 2**-22], dtype=np.float32)
+    _check_dq(qn, a)
+    _check_dq(qn, np.zeros(300, dtype=np.float32))
+
+
+def test_double_quant_three_level_tree_mean(qn):
+    # more than 4096^2 constants takes three levels of the tree
+    n1 = 4096 * 4096 + 4097
+    rng = np.random.default_rng(99)
+    a = (rng.random(n1, dtype=np.float32) * 0.1 + 0.01).astype(np.float32)
+    t = torch.from_numpy(a).cuda()
+    c8, scale, mean = qn.nf4_double_quant(t)
+    torch.cuda.synchronize()
+    m_ref = np.float32(oracle.pairwise_tree_sum(a) / np.float64(n1))
+    assert f32_to_np(mean)[0].view(np.uint32) == m_ref.view(np.uint32)
+    # the per-group code is independent per group: check the first, the last
+    # and a sample of groups against the oracle run on them with the same mean
+    groups = [0, 1, 777, 50_000, (n1 - 1) // 256]
+    for g in groups:
+        seg = a[g * 256 : (g + 1) * 256]
+        d = (seg - m_ref).astype(np.float32)
+        s = np.float32(np.max(np.abs(d)) / np.float32(448.0))
+        want = oracle.e4m3fn_encode((d / s).astype(np.float32))
+        assert f32_to_np(scale)[g].view(np.uint32) == s.view(np.uint32)
+        assert np.array_equal(u8_to_np(c8)[g * 256 : g * 256 + seg.size], want)
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (1, 1), (3, 100), (7, 33), (513, 77), (1, 1024 + 64 * 3 + 5)])
+@pytest.mark.parametrize("dq", [True, False])
+def test_dequantize_matches_oracle(qn, shape, dq):
+    W = workloads.normal_weight(shape[0], shape[1], 0.02, seed=17 + shape[0])
+    w = qn.quantize_weight(W.cuda(), double_quant=dq)
+    ref = oracle_weight(W.numpy(), double_quant=dq)
+    got_bf16 = bf16_bits_np(qn.nf4_dequantize(w, torch.bfloat16))
+    got_f32 = f32_to_np(qn.nf4_dequantize(w, torch.float32))
+    assert np.array_equal(got_bf16, ref["wd_bits"])
+    wf = oracle.dequantize(ref["packed"], ref["a_eff"], W.numel(), out="f32").reshape(shape)
+    assert np.array_equal(got_f32.view(np.uint32), wf.view(np.uint32))
+
+
+def test_storage_path_attn_7b_full(qn):
+    """Quantize + double quant + dequantize of the 4096x4096 projection with
+    outliers, every byte and every bf16 compared."""
+    W = workloads.normal_weight(4096, 4096, 0.02, seed=1, outlier_frac=1e-3, outlier_scale=20.0)
+    w = qn.quantize_weight(W.cuda(), double_quant=True)
+    ref = oracle_weight(W.numpy())
+    assert np.array_equal(u8_to_np(w.packed), ref["packed"])
+    assert np.array_equal(u8_to_np(w.c8), ref["c8"])
+    assert np.array_equal(f32_to_np(w.dq_scale).view(np.uint32), ref["scale"].view(np.uint32))
+    assert f32_to_np(w.dq_mean)[0].view(np.uint32) == np.float32(ref["mean"]).view(np.uint32)
+    assert np.array_equal(bf16_bits_np(qn.nf4_dequantize(w)), ref["wd_bits"])
+    assert np.all(ref["a_eff"] > 0)
