@@ -137,7 +137,7 @@ int check_linear_shape(const ql_nf4_weight* w, int64_t T, int32_t r) {
 // ---- forward workspace -------------------------------------------------
 struct FwdWs {
     uint16_t* Us = nullptr;  // bf16 [T, rp64] = bf16(s U), GEMM path
-    uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path
+    uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
     float* Uf = nullptr;     // fp32 [T, r], GEMV path without U_out
     float* part = nullptr;   // fp32 [chunks, T, N], GEMV path
     size_t bytes = 0;
@@ -154,7 +154,7 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_
         if (r > 0 && !have_uout) f.Uf = c.take<float>(static_cast<size_t>(T) * r);
     } else if (r > 0) {
         f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
-        f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
+        if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
     }
     f.bytes = align_up(c.off, 256);
     return f;
@@ -165,7 +165,6 @@ struct BwdWs {
     uint16_t* BT = nullptr;   // bf16 [r, N] = B^T
     float* Gf = nullptr;      // fp32 [T, r] = s dY B
     uint16_t* Gp = nullptr;   // bf16 [T, rp64]
-    uint16_t* Atp = nullptr;  // bf16 [K, rp64] = A^T padded
     float* Uf = nullptr;      // fp32 [T, r] (recomputed U)
     float* partA = nullptr;   // fp32 [splitsA, rpg, K]
     float* partB = nullptr;   // fp32 [splitsB, rpg, N]
@@ -186,7 +185,6 @@ BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_
         }
         if (want_dx) {
             b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
-            b.Atp = c.take<uint16_t>(static_cast<size_t>(K) * rp);
         }
         if (want_db && !have_u) b.Uf = c.take<float>(static_cast<size_t>(T) * r);
         if (want_da) b.partA = c.take<float>(static_cast<size_t>(lora_grad_splits(T, K)) * rpg * K);
@@ -305,12 +303,20 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         return launch_gemv_reduce(f.part, gemv_num_chunks(K), T, N, U, B, r, scale, Y, st);
     }
     const int rp = rank_pad64(r);
+    const uint16_t* Bsrc = B;
+    int64_t ld_b = r;
+    int r_b = r;
     if (r > 0) {
         SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U_out, r, U_out ? r : 0, scale, f.Us, rp};
         if ((s = launch_skinny(a, st)) != QL_OK) return s;
-        if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
+        if (r % 8 != 0) {  // rows of B are not 16-byte aligned: pad them
+            if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
+            Bsrc = f.Bp;
+            ld_b = rp;
+            r_b = rp;
+        }
     }
-    return launch_gemm_fwd(wd, X, f.Us, f.Bp, rp, Y, T, N, K, st);
+    return launch_gemm_fwd(wd, X, f.Us, Bsrc, ld_b, r_b, rp, Y, T, N, K, st);
 }
 
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
@@ -361,8 +367,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if ((s = launch_skinny(a, st)) != QL_OK) return s;
     }
     if (want_dx) {
-        if (r > 0 && (s = launch_transpose_pad(A, r, K, b.Atp, rp, st)) != QL_OK) return s;
-        if ((s = launch_gemm_dx(wd, dY, b.Gp, b.Atp, rp, dX, T, N, K, st)) != QL_OK) return s;
+        if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, st)) != QL_OK) return s;
     }
     const int rpg = lora_grad_rp(r);
     if (want_da) {

@@ -14,63 +14,9 @@
 // in this file so that a' = fl(fl(E(c8) S) + mu) rounds identically).
 #include "common.h"
 #include "internal.h"
+#include "mm_common.h"
 
 namespace qlnf4 {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__constant__ float c_nf4_mm[16] = {
-    kNF4Host[0], kNF4Host[1], kNF4Host[2],  kNF4Host[3],  kNF4Host[4],  kNF4Host[5],  kNF4Host[6],  kNF4Host[7],
-    kNF4Host[8], kNF4Host[9], kNF4Host[10], kNF4Host[11], kNF4Host[12], kNF4Host[13], kNF4Host[14], kNF4Host[15],
-};
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Raw per-block constant: the E4M3 code and its group scale (double
-// quantization) or the fp32 absmax itself. Loaded early, decoded late.
-struct BlockConst {
-    uint32_t c8;
-    float s;
-};
-
-__device__ __forceinline__ BlockConst load_block_const(const NF4Dev& w, int64_t b) {
-    BlockConst r;
-    if (w.dq) {
-        r.c8 = w.c8[b];
-        r.s = w.scale[b / QL_DQ_BLOCKSIZE];
-    } else {
-        r.c8 = 0;
-        r.s = w.absmax[b];
-    }
-    return r;
-}
-
-__device__ __forceinline__ float block_value(const BlockConst& c, int dq, float mu) {
-    if (!dq) return c.s;
-    const float prod = e4m3_decode(c.c8) * c.s;
-    return prod + mu;
-}
-
-// Eight consecutive codes (one u32 of packed bytes, element 2j in the high
-// nibble of byte j) -> eight bf16 values T[c] * a, low element first.
-__device__ __forceinline__ uint4 dequant8(uint32_t w, float a, const float* tab) {
-    uint4 r;
-    r.x = pack_bf16x2(tab[(w >> 4) & 15u] * a, tab[w & 15u] * a);
-    r.y = pack_bf16x2(tab[(w >> 12) & 15u] * a, tab[(w >> 8) & 15u] * a);
-    r.z = pack_bf16x2(tab[(w >> 20) & 15u] * a, tab[(w >> 16) & 15u] * a);
-    r.w = pack_bf16x2(tab[(w >> 28) & 15u] * a, tab[(w >> 24) & 15u] * a);
-    return r;
-}
-
-__device__ __forceinline__ void dequant8_f32(uint32_t w, float a, const float* tab, float* out) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        out[2 * j] = tab[(w >> (8 * j + 4)) & 15u] * a;
-        out[2 * j + 1] = tab[(w >> (8 * j)) & 15u] * a;
-    }
-}
 
 // ===========================================================================
 // Skinny GEMM (LoRA down-projections): out[t][j] = alpha * sum_k P[t][k] Q[j][k]
@@ -287,315 +233,6 @@ int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, con
     hipLaunchKernelGGL(gemv_reduce_kernel, dim3(static_cast<uint32_t>(ceil_div(T * N, 256))), dim3(256), 0, stream,
                        part, nchunks, T, N, U, B, r, scale, Y);
     return check_launch("GEMV reduce");
-}
-
-// ===========================================================================
-// Dequant-in-LDS GEMM (bf16 MFMA 32x32x16, fp32 accumulation).
-// Workgroup tile 128 (output features / K-out) x 128 (tokens), reduction
-// step 64, four waves of 64x64, LDS double buffer with 16-byte row padding.
-// The LoRA term is appended as extra reduction steps over the padded rank
-// (forward: s U x B^T; dX: G x A), so the epilogue is a plain bf16 store.
-// ===========================================================================
-constexpr int kTM = 128;  // rows of the MFMA A side (n for fwd, k for dX)
-constexpr int kTT = 128;  // tokens
-constexpr int kTK = 64;   // reduction step
-constexpr int kLd = kTK + 8;
-
-struct GemmFwdArgs {
-    NF4Dev w;
-    const uint16_t* X;
-    const uint16_t* Us;
-    const uint16_t* Bp;
-    uint16_t* Y;
-    int64_t T, N, K;
-    int rp;
-    int tiles_n;
-};
-
-// Four waves (wa = wave >> 1 picks the A-side half, wt = wave & 1 the token
-// half) each compute 2x2 MFMA tiles of 32x32 from the LDS tiles sA (A side,
-// row-major along the reduction) and sB (tokens).
-__device__ __forceinline__ void mma_step(const uint16_t* sA, const uint16_t* sB, f32x16 (&acc)[2][2], int lane,
-                                         int wa, int wt) {
-#pragma unroll
-    for (int ks = 0; ks < kTK / 16; ++ks) {
-        const int col = ks * 16 + 8 * (lane >> 5);
-        bf16x8_t av[2], bv[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-            av[a] = as_bf16x8(*reinterpret_cast<const uint4*>(sA + (wa * 64 + a * 32 + (lane & 31)) * kLd + col));
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            bv[b] = as_bf16x8(*reinterpret_cast<const uint4*>(sB + (wt * 64 + b * 32 + (lane & 31)) * kLd + col));
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
-    }
-}
-
-// Store D[m][t] (m along the A side) to out[t][m] as bf16, 4 consecutive m
-// per 8-byte store. D layout: acc element r -> m = 8 (r/4) + 4 (lane/32) +
-// r%4, t = lane%32.
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[2][2], uint16_t* out, int64_t ld, int64_t m0,
-                                           int64_t t0, int64_t M, int64_t T, int lane, int wa, int wt) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t m = m0 + wa * 64 + a * 32 + 8 * q + 4 * (lane >> 5);
-                const int64_t t = t0 + wt * 64 + b * 32 + (lane & 31);
-                if (t < T && m < M) {
-                    uint2 v;
-                    v.x = pack_bf16x2(acc[a][b][4 * q], acc[a][b][4 * q + 1]);
-                    v.y = pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-                    *reinterpret_cast<uint2*>(out + t * ld + m) = v;
-                }
-            }
-}
-
-__global__ __launch_bounds__(256, 2) void gemm_fwd_kernel(GemmFwdArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTM * kLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kTT * kLd];
-    __shared__ float tab[16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wa = wave >> 1, wt = wave & 1;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x % p.tiles_n) * kTM;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x / p.tiles_n) * kTT;
-    const int ksteps = static_cast<int>(p.K / kTK);
-    const int nsteps = ksteps + p.rp / kTK;
-    const float mu = p.w.dq ? *p.w.mean : 0.0f;
-    if (tid < 16) tab[tid] = c_nf4_mm[tid];
-
-    const int crow = tid >> 3, cc = 8 * (tid & 7);  // copy pattern: 4 rows x 16 B per thread
-    const int wrow = tid >> 1, wh = tid & 1;         // dequant pattern: 32 codes per thread
-    uint4 rb[4], ra[4];
-    BlockConst bc;
-
-    auto gload = [&](int s) {
-        if (s < ksteps) {
-            const int64_t k0 = static_cast<int64_t>(s) * kTK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t t = t0 + crow + 32 * i;
-                rb[i] = (t < p.T) ? *reinterpret_cast<const uint4*>(p.X + t * p.K + k0 + cc) : make_uint4(0, 0, 0, 0);
-            }
-            const int64_t n = n0 + wrow;
-            if (n < p.N) {
-                const int64_t e = n * p.K + k0 + 32 * wh;
-                ra[0] = *reinterpret_cast<const uint4*>(p.w.packed + e / 2);
-                bc = load_block_const(p.w, e / 64);
-            } else {
-                ra[0] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-                bc.c8 = 0;
-                bc.s = 0.0f;
-            }
-        } else {
-            const int64_t j0 = static_cast<int64_t>(s - ksteps) * kTK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t t = t0 + crow + 32 * i;
-                const int64_t n = n0 + crow + 32 * i;
-                rb[i] = (t < p.T) ? *reinterpret_cast<const uint4*>(p.Us + t * p.rp + j0 + cc) : make_uint4(0, 0, 0, 0);
-                ra[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(p.Bp + n * p.rp + j0 + cc) : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto sstore = [&](int s, int buf) {
-        uint16_t* A = sA[buf];
-        uint16_t* B = sB[buf];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + (crow + 32 * i) * kLd + cc) = rb[i];
-        if (s < ksteps) {
-            const float a = (n0 + wrow < p.N) ? block_value(bc, p.w.dq, mu) : 0.0f;
-            const uint32_t words[4] = {ra[0].x, ra[0].y, ra[0].z, ra[0].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint4*>(A + wrow * kLd + 32 * wh + 8 * q) = dequant8(words[q], a, tab);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(A + (crow + 32 * i) * kLd + cc) = ra[i];
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    gload(0);
-    __syncthreads();  // tab
-    sstore(0, 0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) gload(s + 1);
-        mma_step(sA[s & 1], sB[s & 1], acc, lane, wa, wt);
-        if (s + 1 < nsteps) sstore(s + 1, (s + 1) & 1);
-        __syncthreads();
-    }
-    store_tile(acc, p.Y, p.N, n0, t0, p.N, p.T, lane, wa, wt);
-}
-
-int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bp, int rp, uint16_t* Y,
-                    int64_t T, int64_t N, int64_t K, hipStream_t stream) {
-    GemmFwdArgs a;
-    a.w = w;
-    a.X = X;
-    a.Us = Us;
-    a.Bp = Bp;
-    a.Y = Y;
-    a.T = T;
-    a.N = N;
-    a.K = K;
-    a.rp = rp;
-    a.tiles_n = static_cast<int>(ceil_div(N, kTM));
-    const int64_t tiles = static_cast<int64_t>(a.tiles_n) * ceil_div(T, kTT);
-    timer_begin(QL_KERNEL_GEMM_FWD, stream);
-    hipLaunchKernelGGL(gemm_fwd_kernel, dim3(static_cast<uint32_t>(tiles)), dim3(256), 0, stream, a);
-    timer_end(QL_KERNEL_GEMM_FWD, stream);
-    return check_launch("dequant GEMM forward");
-}
-
-// dX = dY W' + G A. The MFMA A side is K-out: W' is needed transposed, so
-// each thread expands a 4 (n) x 8 (k) patch of codes and writes it as eight
-// 4-element columns into the k-major LDS tile.
-struct GemmDxArgs {
-    NF4Dev w;
-    const uint16_t* dY;
-    const uint16_t* Gp;
-    const uint16_t* Atp;
-    uint16_t* dX;
-    int64_t T, N, K;
-    int rp;
-    int tiles_k;
-};
-
-__global__ __launch_bounds__(256, 2) void gemm_dx_kernel(GemmDxArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTM * kLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kTT * kLd];
-    __shared__ float tab[16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wa = wave >> 1, wt = wave & 1;
-    const int64_t kb = static_cast<int64_t>(blockIdx.x % p.tiles_k) * kTM;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x / p.tiles_k) * kTT;
-    const int msteps = static_cast<int>(ceil_div(p.N, kTK));
-    const int nsteps = msteps + p.rp / kTK;
-    const float mu = p.w.dq ? *p.w.mean : 0.0f;
-    if (tid < 16) tab[tid] = c_nf4_mm[tid];
-
-    const int crow = tid >> 3, cc = 8 * (tid & 7);
-    const int rg = tid & 15, kc = tid >> 4;  // 4 rows (n) x 8 columns (k) of codes
-    uint4 rb[4], ra[4];
-    uint32_t wq[4];
-    BlockConst bc[4];
-
-    auto gload = [&](int s) {
-        if (s < msteps) {
-            const int64_t nb = static_cast<int64_t>(s) * kTK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t t = t0 + crow + 32 * i;
-                const int64_t n = nb + cc;
-                rb[i] = (t < p.T && n < p.N) ? *reinterpret_cast<const uint4*>(p.dY + t * p.N + n)
-                                             : make_uint4(0, 0, 0, 0);
-            }
-            const int64_t k = kb + 8 * kc;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = nb + 4 * rg + q;
-                if (n < p.N && k < p.K) {
-                    const int64_t e = n * p.K + k;
-                    wq[q] = *reinterpret_cast<const uint32_t*>(p.w.packed + e / 2);
-                    bc[q] = load_block_const(p.w, e / 64);
-                } else {
-                    wq[q] = 0x77777777u;
-                    bc[q].c8 = 0;
-                    bc[q].s = 0.0f;
-                }
-            }
-        } else {
-            const int64_t j0 = static_cast<int64_t>(s - msteps) * kTK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t t = t0 + crow + 32 * i;
-                const int64_t k = kb + crow + 32 * i;
-                rb[i] = (t < p.T) ? *reinterpret_cast<const uint4*>(p.Gp + t * p.rp + j0 + cc) : make_uint4(0, 0, 0, 0);
-                ra[i] = (k < p.K) ? *reinterpret_cast<const uint4*>(p.Atp + k * p.rp + j0 + cc) : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto sstore = [&](int s, int buf) {
-        uint16_t* A = sA[buf];
-        uint16_t* B = sB[buf];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(B + (crow + 32 * i) * kLd + cc) = rb[i];
-        if (s < msteps) {
-            const int64_t nb = static_cast<int64_t>(s) * kTK;
-            float v[4][8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bool ok = (nb + 4 * rg + q < p.N) && (kb + 8 * kc < p.K);
-                const float a = ok ? block_value(bc[q], p.w.dq, mu) : 0.0f;
-                dequant8_f32(wq[q], a, tab, v[q]);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint2 col;
-                col.x = pack_bf16x2(v[0][e], v[1][e]);
-                col.y = pack_bf16x2(v[2][e], v[3][e]);
-                *reinterpret_cast<uint2*>(A + (8 * kc + e) * kLd + 4 * rg) = col;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(A + (crow + 32 * i) * kLd + cc) = ra[i];
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    gload(0);
-    __syncthreads();
-    sstore(0, 0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) gload(s + 1);
-        mma_step(sA[s & 1], sB[s & 1], acc, lane, wa, wt);
-        if (s + 1 < nsteps) sstore(s + 1, (s + 1) & 1);
-        __syncthreads();
-    }
-    store_tile(acc, p.dX, p.K, kb, t0, p.K, p.T, lane, wa, wt);
-}
-
-int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* Atp, int rp, uint16_t* dX,
-                   int64_t T, int64_t N, int64_t K, hipStream_t stream) {
-    GemmDxArgs a;
-    a.w = w;
-    a.dY = dY;
-    a.Gp = Gp;
-    a.Atp = Atp;
-    a.dX = dX;
-    a.T = T;
-    a.N = N;
-    a.K = K;
-    a.rp = rp;
-    a.tiles_k = static_cast<int>(ceil_div(K, kTM));
-    const int64_t tiles = static_cast<int64_t>(a.tiles_k) * ceil_div(T, kTT);
-    timer_begin(QL_KERNEL_GEMM_DX, stream);
-    hipLaunchKernelGGL(gemm_dx_kernel, dim3(static_cast<uint32_t>(tiles)), dim3(256), 0, stream, a);
-    timer_end(QL_KERNEL_GEMM_DX, stream);
-    return check_launch("dequant GEMM dX");
 }
 
 // ===========================================================================

@@ -1,0 +1,400 @@
+// Dequant-in-LDS GEMMs of the frozen-base LoRA layer (gfx950, bf16 MFMA
+// 32x32x16, fp32 accumulation).
+//
+//   forward  Y[t][n]  = sum_k X[t][k] W'[n][k]  + sum_j sU[t][j] B[n][j]
+//   dX       dX[t][k] = sum_n dY[t][n] W'[n][k] + sum_j G[t][j] A[j][k]
+//
+// apxml.com "量化 LoRA (QLoRA) 与 4 位训练": the 4-bit weight is dequantized to
+// bf16 for the matmul and the adapter output is added; aivaro.ru "Как работает
+// QLoRA", §7: the backward dequantizes the 4-bit weight on the fly as well.
+//
+// One kernel template serves both. The MFMA "A side" is the output feature
+// dimension (n for the forward, k for dX); the "B side" is the tokens. A
+// workgroup of four waves owns a TA x TT output tile (2 x 2 waves). Each
+// reduction step of 64 reads a token tile and an expanded bf16 weight tile
+// from LDS; both are double buffered. The token tile arrives by direct
+// global-to-LDS loads (no registers; 128-byte rows with an XOR swizzle of the
+// 16-byte chunks instead of padding, so the operand reads hit distinct
+// banks). The weight codes are loaded into registers two steps ahead, and
+// step s+1's codes are expanded to bf16 and stored inside step s's MFMA
+// stream, so dequantization overlaps the matrix cores. Load addresses are
+// clamped into the matrix, so the step body has no branches; rows past the
+// edge feed only outputs that are not stored, except past-the-end reduction
+// rows of dX, whose weight rows are expanded with a zero absmax.
+// The weight tile is row-major in both directions (a thread expands one
+// block, or half of one, with a single absmax); dX reads its A operand
+// through ds_read_b64_tr_b16, which hands each lane a column segment. The
+// LoRA term follows as rp/64 extra reduction steps over the rank.
+#include <cstdlib>
+#include <cstring>
+
+#include "mm_common.h"
+
+namespace qlnf4 {
+
+constexpr int kStep = 64;
+
+struct TileArgs {
+    NF4Dev w;
+    const uint16_t* act;  // forward: X [T, K]; dX: dY [T, N]
+    int64_t ld_act;
+    const uint16_t* lt;  // token-side LoRA operand [T, rp]: forward bf16(s U), dX bf16(G)
+    const uint16_t* la;  // A-side LoRA operand: forward B [N, r_la] (row stride ld_la); dX A [r_la, K]
+    int64_t ld_la;
+    int r_la;
+    int rp;
+    uint16_t* out;  // forward: Y [T, N]; dX: dX [T, K]
+    int64_t T, N, K;
+    int tiles_a, tiles_t;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+#define QL_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i%4 of the 4-element rows addressed by lanes 4e + i/4 (e = 0..3).
+__device__ __forceinline__ v4i16 ld_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((QL_LDS v4i16*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+// 16-byte chunk c of token-tile row r is stored at chunk c ^ swz(r): rows r
+// and r+8 (same banks in a 32-bank LDS) and rows r and r+2 (same banks in a
+// 64-bank LDS) get different chunk positions.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int TA, int TT, int WA, int WT, bool DX>
+struct TileShape {
+    static constexpr int NW = WA * WT, NTHR = 64 * NW;      // waves, threads
+    static constexpr int MW = TA / WA, TW = TT / WT;         // wave tile
+    static constexpr int SA = MW / 32, ST = TW / 32;         // 32x32 MFMA sub-tiles per wave
+    static constexpr int DMA = TT / 8 / NW;                  // 1 KiB token loads per wave per step
+    static constexpr int CPT = TA * kStep / NTHR;            // codes per thread per step
+    static constexpr int CC = CPT / 32;                      // 16-B code chunks per thread
+    static constexpr int ROWS_A = DX ? kStep : TA;           // weight-tile rows (reduction rows for dX)
+    static constexpr int LDA = DX ? TA + 8 : kStep + 8;      // weight-tile LDS row (bf16, padded)
+    static constexpr int TPR = DX ? TA / CPT : kStep / CPT;  // threads per weight-tile row
+    static_assert(CPT == 32 || CPT == 64, "a thread expands one block or half of one");
+    static_assert(DMA >= 1 && TT % (8 * NW) == 0, "token tile split");
+};
+
+template <int CC>
+struct Codes {
+    uint4 c[CC];
+    BlockConst bc;
+};
+
+template <int TA, int TT, int WA, int WT, bool DX, bool DQ>
+__global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_kernel(TileArgs p) {
+    using S = TileShape<TA, TT, WA, WT, DX>;
+    constexpr int SA = S::SA, ST = S::ST, CPT = S::CPT, CC = S::CC, LDA = S::LDA, TPR = S::TPR;
+    constexpr int MW = S::MW, TW = S::TW, NW = S::NW, NTHR = S::NTHR;
+
+    // two stages of each tile, as separate arrays so that the compiler can tell
+    // the stage being loaded from the stage being read
+    __shared__ __attribute__((aligned(16))) uint16_t sA0[S::ROWS_A * LDA];
+    __shared__ __attribute__((aligned(16))) uint16_t sA1[S::ROWS_A * LDA];
+    __shared__ __attribute__((aligned(16))) uint16_t sX0[TT * kStep];
+    __shared__ __attribute__((aligned(16))) uint16_t sX1[TT * kStep];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wa = wave / WT, wt = wave % WT;
+    // With eight waves, the two waves that share a SIMD (w and w+4) run the
+    // two halves of a step in opposite order, so one expands codes (VALU)
+    // while the other feeds the matrix core.
+    const bool expand_first = (NW == 8) && ((wave >> 2) & 1);
+
+    // Workgroups are handed to the eight XCDs round robin; give each XCD a
+    // contiguous range of tiles, token-major, so one XCD's L2 serves the same
+    // activation rows to all its workgroups.
+    const int ntiles = p.tiles_a * p.tiles_t;
+    const int g = blockIdx.x, qx = ntiles / 8, rem = ntiles % 8, x = g % 8;
+    const int logical = x * qx + (x < rem ? x : rem) + g / 8;
+    const int64_t m0 = static_cast<int64_t>(logical % p.tiles_a) * TA;
+    const int64_t t0 = static_cast<int64_t>(logical / p.tiles_a) * TT;
+    const int64_t MA = DX ? p.K : p.N;
+    const int64_t RED = DX ? p.N : p.K;
+    const int msteps = static_cast<int>(ceil_div(RED, kStep));
+    const float mu = DQ ? *p.w.mean : 0.0f;
+
+    // ---- token tile: direct loads into LDS --------------------------------
+    // Wave w issues loads q = NW i + w (i < DMA); load q fills rows 8q..8q+7.
+    auto dma = [&](int step, uint16_t* sX) {
+        const int64_t r0 = static_cast<int64_t>(step) * kStep;
+#pragma unroll
+        for (int i = 0; i < S::DMA; ++i) {
+            const int q = NW * i + wave;
+            const int row = 8 * q + (lane >> 3);
+            const int lc = (lane & 7) ^ swz(row);
+            const int64_t t = min(t0 + row, p.T - 1);
+            const int64_t col = min(r0 + 8 * lc, RED - 8);
+            __builtin_amdgcn_global_load_lds(p.act + t * p.ld_act + col, (QL_LDS void*)(sX + q * 512), 16, 0, 0);
+        }
+    };
+
+    // ---- weight codes: registers, two steps ahead ----------------------------
+    const int wrow = tid / TPR, wcol = (tid % TPR) * CPT;
+    auto gcodes = [&](int step, Codes<CC>& cs) {
+        const int64_t r0 = static_cast<int64_t>(step) * kStep;
+        int64_t e;
+        if constexpr (DX) {
+            const int64_t n = min(r0 + wrow, p.N - 1);
+            e = n * p.K + min(m0 + wcol, p.K - CPT);
+        } else {
+            const int64_t n = min(m0 + wrow, p.N - 1);
+            e = n * p.K + r0 + wcol;
+        }
+#pragma unroll
+        for (int cc = 0; cc < CC; ++cc) cs.c[cc] = ld16(p.w.packed + e / 2 + 16 * cc);
+        const int64_t b = e / 64;
+        if constexpr (DQ) {
+            cs.bc.c8 = p.w.c8[b];
+            cs.bc.s = p.w.scale[b / QL_DQ_BLOCKSIZE];
+        } else {
+            cs.bc.c8 = 0;
+            cs.bc.s = p.w.absmax[b];
+        }
+    };
+
+    // ---- expand one step's codes into a weight stage -----------------------
+    auto expand = [&](int step, const Codes<CC>& cs, uint16_t* sA) {
+        float a = block_value(cs.bc, DQ ? 1 : 0, mu);
+        if constexpr (DX) a = (static_cast<int64_t>(step) * kStep + wrow < p.N) ? a : 0.0f;
+        const Lut16 L = make_lut(a);
+        uint16_t* dst = sA + wrow * LDA + wcol;
+#pragma unroll
+        for (int cc = 0; cc < CC; ++cc) {
+            const uint32_t words[4] = {cs.c[cc].x, cs.c[cc].y, cs.c[cc].z, cs.c[cc].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) st16(dst + 32 * cc + 8 * q, dequant8_lut(words[q], L));
+        }
+    };
+
+    f32x16 acc[SA][ST];
+#pragma unroll
+    for (int a = 0; a < SA; ++a)
+#pragma unroll
+        for (int b = 0; b < ST; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    auto load_a = [&](const uint16_t* sA, int a, int ks) -> bf16x8_t {
+        if constexpr (!DX) {
+            return as_bf16x8(ld16(sA + (wa * MW + a * 32 + (lane & 31)) * LDA + ks * 16 + 8 * (lane >> 5)));
+        } else {
+            // rows (reduction) 16 ks + 8 (lane/32) + 0..7 of column (k out) lane%32
+            const int grp = lane >> 4, j = lane & 15;
+            const uint16_t* base =
+                sA + (ks * 16 + 8 * (grp >> 1) + (j >> 2)) * LDA + wa * MW + a * 32 + 16 * (grp & 1) + 4 * (j & 3);
+            const v4i16 lo = ld_tr16(base);
+            const v4i16 hi = ld_tr16(base + 4 * LDA);
+            const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8_t, v);
+        }
+    };
+    auto load_b = [&](const uint16_t* sX, int b, int ks) -> bf16x8_t {
+        const int row = wt * TW + b * 32 + (lane & 31);
+        const int chunk = (2 * ks + (lane >> 5)) ^ swz(row);
+        return as_bf16x8(ld16(sX + row * kStep + 8 * chunk));
+    };
+    auto compute = [&](const uint16_t* sA, const uint16_t* sX) {
+#pragma unroll
+        for (int ks = 0; ks < kStep / 16; ++ks) {
+            bf16x8_t av[SA], bv[ST];
+#pragma unroll
+            for (int a = 0; a < SA; ++a) av[a] = load_a(sA, a, ks);
+#pragma unroll
+            for (int b = 0; b < ST; ++b) bv[b] = load_b(sX, b, ks);
+#pragma unroll
+            for (int a = 0; a < SA; ++a)
+#pragma unroll
+                for (int b = 0; b < ST; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+    };
+
+    // Pipeline (two steps per iteration, stages named statically):
+    //   step s:   token loads for s+1 -> the other stage; codes for s+2 -> the
+    //             free register set; MFMAs on stage s; expand step s+1.
+    Codes<CC> cs0, cs1;
+    dma(0, sX0);
+    gcodes(0, cs0);
+    gcodes(min(1, msteps - 1), cs1);
+    expand(0, cs0, sA0);
+    __syncthreads();
+    for (int s = 0; s < msteps; s += 2) {
+        dma(min(s + 1, msteps - 1), sX1);
+        gcodes(min(s + 2, msteps - 1), cs0);
+        if (expand_first) {
+            expand(s + 1, cs1, sA1);
+            compute(sA0, sX0);
+        } else {
+            compute(sA0, sX0);
+            expand(s + 1, cs1, sA1);
+        }
+        __syncthreads();
+        if (s + 1 >= msteps) break;
+        dma(min(s + 2, msteps - 1), sX0);
+        gcodes(min(s + 3, msteps - 1), cs1);
+        if (expand_first) {
+            expand(s + 2, cs0, sA0);
+            compute(sA1, sX1);
+        } else {
+            compute(sA1, sX1);
+            expand(s + 2, cs0, sA0);
+        }
+        __syncthreads();
+    }
+
+    // LoRA term: rp/64 more reduction steps over the rank, staged directly.
+    for (int ls = 0; ls < p.rp / kStep; ++ls) {
+        const int64_t j0 = static_cast<int64_t>(ls) * kStep;
+#pragma unroll
+        for (int i = 0; i < TT * 8 / NTHR; ++i) {
+            const int c = tid + NTHR * i;
+            const int row = c >> 3, lc = c & 7;
+            const int64_t t = t0 + row;
+            const uint4 v = (t < p.T) ? ld16(p.lt + t * p.rp + j0 + 8 * lc) : make_uint4(0, 0, 0, 0);
+            st16(sX0 + row * kStep + 8 * (lc ^ swz(row)), v);
+        }
+        if constexpr (!DX) {
+            // B rows n, 64 rank columns
+#pragma unroll
+            for (int i = 0; i < TA * 8 / NTHR; ++i) {
+                const int c = tid + NTHR * i;
+                const int64_t n = m0 + (c >> 3);
+                const int64_t j = j0 + 8 * (c & 7);
+                const uint4 v = (n < p.N && j < p.r_la) ? ld16(p.la + n * p.ld_la + j) : make_uint4(0, 0, 0, 0);
+                st16(sA0 + (c >> 3) * LDA + 8 * (c & 7), v);
+            }
+        } else {
+            // A rows j (reduction), TA columns k: the same row-major layout as W'
+#pragma unroll
+            for (int i = 0; i < TA * 8 / NTHR; ++i) {
+                const int c = tid + NTHR * i;
+                const int row = c / (TA / 8), col = 8 * (c % (TA / 8));
+                const int64_t j = j0 + row;
+                const int64_t k = m0 + col;
+                const uint4 v = (j < p.r_la && k < p.K) ? ld16(p.la + j * p.ld_la + k) : make_uint4(0, 0, 0, 0);
+                st16(sA0 + row * LDA + col, v);
+            }
+        }
+        __syncthreads();
+        compute(sA0, sX0);
+        __syncthreads();
+    }
+
+    // Epilogue: D[m][t] -> out[t][m] in bf16; acc element r of sub-tile (a, b)
+    // sits at m = 32a + 8(r/4) + 4(lane/32) + r%4, t = 32b + lane%32.
+#pragma unroll
+    for (int a = 0; a < SA; ++a)
+#pragma unroll
+        for (int b = 0; b < ST; ++b)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int64_t m = m0 + wa * MW + a * 32 + 8 * qq + 4 * (lane >> 5);
+                const int64_t t = t0 + wt * TW + b * 32 + (lane & 31);
+                if (t < p.T && m < MA) {
+                    uint2 v;
+                    v.x = pack_bf16x2(acc[a][b][4 * qq], acc[a][b][4 * qq + 1]);
+                    v.y = pack_bf16x2(acc[a][b][4 * qq + 2], acc[a][b][4 * qq + 3]);
+                    *reinterpret_cast<uint2*>(p.out + t * MA + m) = v;
+                }
+            }
+}
+
+namespace {
+
+int cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cached = n;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
+// Tile edge for an MA x T output: the larger tile moves less LDS traffic per
+// flop, the smaller one fills the chip on small grids. QLORA_NF4_GEMM_TILE=128
+// or 256 forces one (tests run both).
+int pick_tile(int64_t MA, int64_t T) {
+    const char* e = std::getenv("QLORA_NF4_GEMM_TILE");
+    if (e && std::strcmp(e, "128") == 0) return 128;
+    if (e && std::strcmp(e, "256") == 0) return 256;
+    const int64_t cus = cu_count();
+    const int64_t n256 = ceil_div(MA, 256) * ceil_div(T, 256);
+    const int64_t n128 = ceil_div(MA, 128) * ceil_div(T, 128);
+    const double c256 = static_cast<double>(ceil_div(n256, cus)) * 65536.0;
+    const double c128 = static_cast<double>(ceil_div(n128, 2 * cus)) * 2.0 * 16384.0 / 0.75;
+    return c128 < c256 ? 128 : 256;
+}
+
+template <bool DX>
+int launch_tiles(TileArgs& a, int kid, const char* what, hipStream_t stream) {
+    const int64_t MA = DX ? a.K : a.N;
+    const int tile = pick_tile(MA, a.T);
+    a.tiles_a = static_cast<int>(ceil_div(MA, tile));
+    a.tiles_t = static_cast<int>(ceil_div(a.T, tile));
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.tiles_a) * a.tiles_t));
+    timer_begin(kid, stream);
+    if (tile == 256) {
+        if (a.w.dq)
+            hipLaunchKernelGGL((tile_gemm_kernel<256, 256, 4, 2, DX, true>), grid, dim3(512), 0, stream, a);
+        else
+            hipLaunchKernelGGL((tile_gemm_kernel<256, 256, 4, 2, DX, false>), grid, dim3(512), 0, stream, a);
+    } else {
+        if (a.w.dq)
+            hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, false>), grid, dim3(256), 0, stream, a);
+    }
+    timer_end(kid, stream);
+    return check_launch(what);
+}
+
+}  // namespace
+
+int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bsrc, int64_t ld_b,
+                    int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, hipStream_t stream) {
+    TileArgs a;
+    a.w = w;
+    a.act = X;
+    a.ld_act = K;
+    a.lt = Us;
+    a.la = Bsrc;
+    a.ld_la = ld_b;
+    a.r_la = r_b;
+    a.rp = rp;
+    a.out = Y;
+    a.T = T;
+    a.N = N;
+    a.K = K;
+    return launch_tiles<false>(a, QL_KERNEL_GEMM_FWD, "dequant GEMM forward", stream);
+}
+
+int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
+                   uint16_t* dX, int64_t T, int64_t N, int64_t K, hipStream_t stream) {
+    TileArgs a;
+    a.w = w;
+    a.act = dY;
+    a.ld_act = N;
+    a.lt = Gp;
+    a.la = A;
+    a.ld_la = K;
+    a.r_la = r;
+    a.rp = rp;
+    a.out = dX;
+    a.T = T;
+    a.N = N;
+    a.K = K;
+    return launch_tiles<true>(a, QL_KERNEL_GEMM_DX, "dequant GEMM dX", stream);
+}
+
+}  // namespace qlnf4

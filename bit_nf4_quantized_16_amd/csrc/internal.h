@@ -55,10 +55,13 @@ int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_
 int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, const float* U, const uint16_t* B, int r,
                        float scale, uint16_t* Y, hipStream_t stream);
 
-int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bp, int rp, uint16_t* Y,
-                    int64_t T, int64_t N, int64_t K, hipStream_t stream);
-int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* Atp, int rp, uint16_t* dX,
-                   int64_t T, int64_t N, int64_t K, hipStream_t stream);
+// Forward: Y = X W'^T + Us Bsrc^T over the padded rank rp (Us [T, rp] bf16 =
+// bf16(s U), zero beyond r; Bsrc [N, r_b] with row stride ld_b, 16-B rows).
+int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bsrc, int64_t ld_b,
+                    int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, hipStream_t stream);
+// dX = dY W' + Gp A over the padded rank rp (Gp [T, rp] bf16, A [r, K]).
+int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
+                   uint16_t* dX, int64_t T, int64_t N, int64_t K, hipStream_t stream);
 
 int lora_grad_rp(int r);
 int lora_grad_splits(int64_t T, int64_t cols);

@@ -1,0 +1,121 @@
+// Device helpers shared by the matmul kernels: MFMA operand types, the
+// per-block constant of a quantized weight, and the expansion of NF4 codes to
+// bf16 (w' = bf16(fl32(T[c] * a')), the value nf4_dequantize produces).
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace qlnf4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+static __constant__ float c_nf4_mm[16] = {
+    kNF4Host[0], kNF4Host[1], kNF4Host[2],  kNF4Host[3],  kNF4Host[4],  kNF4Host[5],  kNF4Host[6],  kNF4Host[7],
+    kNF4Host[8], kNF4Host[9], kNF4Host[10], kNF4Host[11], kNF4Host[12], kNF4Host[13], kNF4Host[14], kNF4Host[15],
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Raw per-block constant: the E4M3 code and its group scale (double
+// quantization) or the fp32 absmax itself. Loaded early, decoded late.
+struct BlockConst {
+    uint32_t c8;
+    float s;
+};
+
+__device__ __forceinline__ BlockConst load_block_const(const NF4Dev& w, int64_t b) {
+    BlockConst r;
+    if (w.dq) {
+        r.c8 = w.c8[b];
+        r.s = w.scale[b / QL_DQ_BLOCKSIZE];
+    } else {
+        r.c8 = 0;
+        r.s = w.absmax[b];
+    }
+    return r;
+}
+
+__device__ __forceinline__ float block_value(const BlockConst& c, int dq, float mu) {
+    if (!dq) return c.s;
+    const float prod = e4m3_decode(c.c8) * c.s;
+    return prod + mu;
+}
+
+// Eight consecutive codes (one u32 of packed bytes, element 2j in the high
+// nibble of byte j) -> eight bf16 values T[c] * a, low element first.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float a, const float* tab) {
+    uint4 r;
+    r.x = pack_bf16x2(tab[(w >> 4) & 15u] * a, tab[w & 15u] * a);
+    r.y = pack_bf16x2(tab[(w >> 12) & 15u] * a, tab[(w >> 8) & 15u] * a);
+    r.z = pack_bf16x2(tab[(w >> 20) & 15u] * a, tab[(w >> 16) & 15u] * a);
+    r.w = pack_bf16x2(tab[(w >> 28) & 15u] * a, tab[(w >> 24) & 15u] * a);
+    return r;
+}
+
+__device__ __forceinline__ void dequant8_f32(uint32_t w, float a, const float* tab, float* out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        out[2 * j] = tab[(w >> (8 * j + 4)) & 15u] * a;
+        out[2 * j + 1] = tab[(w >> (8 * j)) & 15u] * a;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-only NF4 expansion. For one block (one absmax a), the sixteen
+// products bf16(T[c] * a) are built once; their low bytes sit in lo[0..3]
+// and their high bytes in hi[0..3] (entry c at byte c%4 of word c/4). A code
+// then selects its two bytes with v_perm_b32 (8-entry byte lookup) and bit 3
+// of the code picks the upper or lower half with v_bfi_b32. No LDS traffic.
+// ---------------------------------------------------------------------------
+struct Lut16 {
+    uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ Lut16 make_lut(float a) {
+    uint32_t p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = pack_bf16x2(kNF4Host[2 * i] * a, kNF4Host[2 * i + 1] * a);
+    Lut16 L;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        L.lo[w] = __builtin_amdgcn_perm(p[2 * w + 1], p[2 * w], 0x06040200u);
+        L.hi[w] = __builtin_amdgcn_perm(p[2 * w + 1], p[2 * w], 0x07050301u);
+    }
+    return L;
+}
+
+// Bytes of entry (code & 7) of the lower or upper 8 entries of t, chosen per
+// byte by mask (0xFF where the code is >= 8).
+__device__ __forceinline__ uint32_t lut_bytes(const uint32_t (&t)[4], uint32_t sel7, uint32_t mask) {
+    const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], sel7);
+    const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], sel7);
+    return (hi & mask) | (lo & ~mask);
+}
+
+// Eight codes (one u32 of packed bytes, element 2j in the high nibble of byte
+// j) -> eight bf16 values, element 0 in the low half of .x.
+__device__ __forceinline__ uint4 dequant8_lut(uint32_t w, const Lut16& L) {
+    const uint32_t se = (w >> 4) & 0x07070707u;  // even elements, low 3 bits of the code
+    const uint32_t so = w & 0x07070707u;         // odd elements
+    const uint32_t be = w & 0x80808080u;         // bit 3 of the even codes, at bit 7 of each byte
+    const uint32_t bo = (w << 4) & 0x80808080u;  // bit 3 of the odd codes
+    const uint32_t me = (be << 1) - (be >> 7);   // 0xFF per byte where set
+    const uint32_t mo = (bo << 1) - (bo >> 7);
+    const uint32_t le = lut_bytes(L.lo, se, me), he = lut_bytes(L.hi, se, me);
+    const uint32_t lo = lut_bytes(L.lo, so, mo), ho = lut_bytes(L.hi, so, mo);
+    const uint32_t xa = __builtin_amdgcn_perm(he, le, 0x05010400u);  // e0 | e2 << 16
+    const uint32_t xb = __builtin_amdgcn_perm(he, le, 0x07030602u);  // e4 | e6 << 16
+    const uint32_t ya = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // e1 | e3 << 16
+    const uint32_t yb = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // e5 | e7 << 16
+    uint4 r;
+    r.x = __builtin_amdgcn_perm(ya, xa, 0x05040100u);
+    r.y = __builtin_amdgcn_perm(ya, xa, 0x07060302u);
+    r.z = __builtin_amdgcn_perm(yb, xb, 0x05040100u);
+    r.w = __builtin_amdgcn_perm(yb, xb, 0x07060302u);
+    return r;
+}
+
+}  // namespace qlnf4

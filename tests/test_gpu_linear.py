@@ -174,3 +174,15 @@ def test_frozen_base_is_not_written(qn):
     torch.cuda.synchronize()
     for a, b in zip(before, (w.packed, w.c8, w.dq_scale, w.dq_mean)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("tile", ["128", "256"])
+@pytest.mark.parametrize("N,K,T,r", [(200, 320, 300, 5), (520, 1088, 257, 70), (256, 256, 17, 8), (768, 512, 600, 16),
+                                     (264, 192, 40, 128), (1024, 320, 513, 64)])
+def test_both_gemm_tiles(qn, monkeypatch, tile, N, K, T, r):
+    """The forward and dX GEMMs come in a 128x128 and a 256x256 tile; force
+    each (the launcher otherwise picks by shape) on ragged multi-tile cases."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", tile)
+    W = workloads.normal_weight(N, K, 0.02, seed=N + 3 * K)
+    case = workloads.lora_case("tile%s_N%dK%dT%dr%d" % (tile, N, K, T, r), W, T, r, 2.0 * r, 1 / K, 0.05, seed=T)
+    _run(qn, case)
