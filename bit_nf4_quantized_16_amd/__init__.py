@@ -182,9 +182,9 @@ def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, 
     dev = dY.device
     dX = torch.empty(T, w.cols, dtype=torch.bfloat16, device=dev) if need_dx else None
     if r > 0 and need_da and dA is None:
-        dA = torch.zeros(r, w.cols, dtype=torch.float32, device=dev)
+        dA = (torch.zeros if accumulate else torch.empty)(r, w.cols, dtype=torch.float32, device=dev)
     if r > 0 and need_db and dB is None:
-        dB = torch.zeros(w.rows, r, dtype=torch.float32, device=dev)
+        dB = (torch.zeros if accumulate else torch.empty)(w.rows, r, dtype=torch.float32, device=dev)
     if not need_da:
         dA = None
     if not need_db:

@@ -162,33 +162,31 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_
 
 // ---- backward workspace ------------------------------------------------
 struct BwdWs {
-    uint16_t* BT = nullptr;   // bf16 [r, N] = B^T
-    float* Gf = nullptr;      // fp32 [T, r] = s dY B
-    uint16_t* Gp = nullptr;   // bf16 [T, rp64]
-    float* Uf = nullptr;      // fp32 [T, r] (recomputed U)
-    float* partA = nullptr;   // fp32 [splitsA, rpg, K]
-    float* partB = nullptr;   // fp32 [splitsB, rpg, N]
+    uint16_t* BT = nullptr;  // bf16 [r, N] = B^T (for G = s dY B)
+    uint16_t* Gp = nullptr;  // bf16 [T, rp64] = G, dX's LoRA operand
+    uint16_t* Gt = nullptr;  // bf16 [rp16, T] = G^T, dA's MFMA operand
+    uint16_t* Ut = nullptr;  // bf16 [rp16, T] = U^T, dB's MFMA operand
+    float* partA = nullptr;  // fp32 [splitsA, rp16, K]
+    float* partB = nullptr;  // fp32 [splitsB, rp16, N]
     size_t bytes = 0;
 };
 
-BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db,
-                bool have_u) {
+BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db) {
     Carver c(ws);
     BwdWs b;
     if (r > 0) {
         const int rp = rank_pad64(r);
-        const int rpg = lora_grad_rp(r);
-        const bool need_g = want_dx || want_da;
-        if (need_g) {
-            b.BT = c.take<uint16_t>(static_cast<size_t>(r) * N);
-            b.Gf = c.take<float>(static_cast<size_t>(T) * r);
+        const int rp16 = lora_grad_rp(r);
+        if (want_dx || want_da) b.BT = c.take<uint16_t>(static_cast<size_t>(r) * N);
+        if (want_dx) b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+        if (want_da) {
+            b.Gt = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
+            b.partA = c.take<float>(static_cast<size_t>(lora_grad_splits(T, K)) * rp16 * K);
         }
-        if (want_dx) {
-            b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+        if (want_db) {
+            b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
+            b.partB = c.take<float>(static_cast<size_t>(lora_grad_splits(T, N)) * rp16 * N);
         }
-        if (want_db && !have_u) b.Uf = c.take<float>(static_cast<size_t>(T) * r);
-        if (want_da) b.partA = c.take<float>(static_cast<size_t>(lora_grad_splits(T, K)) * rpg * K);
-        if (want_db) b.partB = c.take<float>(static_cast<size_t>(lora_grad_splits(T, N)) * rpg * N);
     }
     b.bytes = align_up(c.off, 256);
     return b;
@@ -296,7 +294,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
     if (T <= kGemvMaxT) {
         float* U = U_out ? U_out : f.Uf;
         if (r > 0) {
-            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U, r, r, 0.0f, nullptr, 0};
+            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U, r, r, 0.0f, nullptr, 0, nullptr, 0, 0};
             if ((s = launch_skinny(a, st)) != QL_OK) return s;
         }
         if ((s = launch_gemv(wd, X, T, N, K, f.part, st)) != QL_OK) return s;
@@ -307,7 +305,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
     int64_t ld_b = r;
     int r_b = r;
     if (r > 0) {
-        SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U_out, r, U_out ? r : 0, scale, f.Us, rp};
+        SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U_out, r, U_out ? r : 0, scale, f.Us, rp, nullptr, 0, 0};
         if ((s = launch_skinny(a, st)) != QL_OK) return s;
         if (r % 8 != 0) {  // rows of B are not 16-byte aligned: pad them
             if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
@@ -321,7 +319,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
 
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
     if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
-    return carve_bwd(nullptr, rows, cols, T, r, true, true, true, false).bytes;
+    return carve_bwd(nullptr, rows, cols, T, r, true, true, true).bytes;
 }
 
 int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
@@ -349,7 +347,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
     const bool have_u = U_saved != nullptr;
     if (have_u && (s = check_ptr(U_saved, "U_saved")) != QL_OK) return s;
     if ((want_da || (want_db && !have_u)) && (s = check_ptr(X, "X")) != QL_OK) return s;
-    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db, have_u);
+    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db);
     if (need.bytes > 0) {
         if (ws == nullptr || ws_bytes < need.bytes)
             return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
@@ -357,34 +355,36 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db, have_u);
+    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db);
     const NF4Dev wd = to_dev(w);
     const int rp = rank_pad64(r);
+    const int rp16 = lora_grad_rp(r);
     if (r > 0 && (want_dx || want_da)) {
-        // G = s dY B: skinny GEMM over N with Q = B^T
+        // G = s dY B: skinny GEMM over N with Q = B^T; bf16 copies for dX (row
+        // major, padded to rp64) and for dA (transposed)
         if ((s = launch_transpose_pad(B, N, r, b.BT, N, st)) != QL_OK) return s;
-        SkinnyArgs a{dY, N, b.BT, N, r, T, N, scale, b.Gf, r, r, scale, want_dx ? b.Gp : nullptr, want_dx ? rp : 0};
+        SkinnyArgs a{dY,      N, b.BT, N, r, T, N, scale, nullptr, 0, 0, scale, want_dx ? b.Gp : nullptr,
+                     want_dx ? rp : 0, want_da ? b.Gt : nullptr, want_da ? rp16 : 0, lora_vt_ld(T)};
         if ((s = launch_skinny(a, st)) != QL_OK) return s;
     }
     if (want_dx) {
         if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, st)) != QL_OK) return s;
     }
-    const int rpg = lora_grad_rp(r);
     if (want_da) {
         const int sp = lora_grad_splits(T, K);
-        if ((s = launch_lora_grad_partial(X, K, K, b.Gf, r, r, T, sp, b.partA, st)) != QL_OK) return s;
-        if ((s = launch_lora_grad_final(b.partA, sp, rpg, r, K, 1.0f, true, dA, accumulate, st)) != QL_OK) return s;
+        if ((s = launch_lora_grad_partial(X, K, K, b.Gt, rp16, T, sp, b.partA, st)) != QL_OK) return s;
+        if ((s = launch_lora_grad_final(b.partA, sp, rp16, r, K, 1.0f, true, dA, accumulate, st)) != QL_OK) return s;
     }
     if (want_db) {
-        const float* U = U_saved;
-        if (!have_u) {
-            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, b.Uf, r, r, 0.0f, nullptr, 0};
+        if (have_u) {
+            if ((s = launch_transpose_f32_bf16(U_saved, T, r, rp16, b.Ut, st)) != QL_OK) return s;
+        } else {
+            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, nullptr, 0, 0, 1.0f, nullptr, 0, b.Ut, rp16, lora_vt_ld(T)};
             if ((s = launch_skinny(a, st)) != QL_OK) return s;
-            U = b.Uf;
         }
         const int sp = lora_grad_splits(T, N);
-        if ((s = launch_lora_grad_partial(dY, N, N, U, r, r, T, sp, b.partB, st)) != QL_OK) return s;
-        if ((s = launch_lora_grad_final(b.partB, sp, rpg, r, N, scale, false, dB, accumulate, st)) != QL_OK) return s;
+        if ((s = launch_lora_grad_partial(dY, N, N, b.Ut, rp16, T, sp, b.partB, st)) != QL_OK) return s;
+        if ((s = launch_lora_grad_final(b.partB, sp, rp16, r, N, scale, false, dB, accumulate, st)) != QL_OK) return s;
     }
     return QL_OK;
 }

@@ -56,8 +56,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wave][4 * g + r][16 * c + li] = acc[c][r];
     __syncthreads();
-    const int64_t ncols_b = p.out_b ? p.ld_b : 0;
-    const int64_t ncols = (ncols_b > NT * 16) ? ncols_b : NT * 16;
+    int64_t ncols = p.out_b ? p.ld_b : 0;
+    if (p.out_bt && p.rows_bt > ncols) ncols = p.rows_bt;
+    if (ncols < NT * 16) ncols = NT * 16;
     for (int64_t e = threadIdx.x; e < 16 * ncols; e += 256) {
         const int tl = static_cast<int>(e / ncols);
         const int j = static_cast<int>(e % ncols);
@@ -69,6 +70,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
         if (p.out_b && j < p.ld_b) {
             const float v = (j < p.qrows) ? p.alpha_b * sum : 0.0f;
             p.out_b[t * p.ld_b + j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+        }
+        if (p.out_bt && j < p.rows_bt) {
+            const float v = (j < p.qrows) ? p.alpha_b * sum : 0.0f;
+            p.out_bt[j * p.ld_bt + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
         }
     }
 }
@@ -240,74 +245,160 @@ int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, con
 // M (X for dA, dY for dB), RP accumulators over the rank; the token range is
 // split across workgroups and the splits are added in order afterwards.
 // ===========================================================================
-int lora_grad_rp(int r) {
-    if (r <= 16) return 16;
-    if (r <= 32) return 32;
-    if (r <= 64) return 64;
-    return 128;
-}
+int lora_grad_rp(int r) { return (r + 15) / 16 * 16; }
+
+constexpr int kGradCols = 64;  // columns of M per workgroup
+constexpr int kGradRows = 32;  // token rows per MFMA step
+constexpr int kGradLd = kGradCols + 8;
 
 int lora_grad_splits(int64_t T, int64_t cols) {
-    const int64_t col_tiles = ceil_div(cols, 256);
-    int64_t s = ceil_div(512, col_tiles);
-    const int64_t max_s = ceil_div(T, 64);
+    const int64_t col_blocks = ceil_div(cols, kGradCols);
+    int64_t s = ceil_div(512, col_blocks);  // aim for >= 512 workgroups
+    const int64_t max_s = ceil_div(T, 4 * kGradRows);
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
     return static_cast<int>(s);
 }
 
-template <int RP>
-__global__ __launch_bounds__(256) void lora_grad_partial_kernel(const uint16_t* __restrict__ M, int64_t ldm,
-                                                                int64_t cols, const float* __restrict__ V, int64_t ldv,
-                                                                int r, int64_t T, int64_t t_per,
-                                                                float* __restrict__ part) {
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+typedef short v4i16_g __attribute__((ext_vector_type(4)));
+typedef short v8i16_g __attribute__((ext_vector_type(8)));
+
+// LoRA weight gradient partials with bf16 MFMA 16x16x32 (reduction over
+// tokens): part[ts][j][c] = sum_{t in split ts} Vt[j][t] * M[t][c], j < 16 RT.
+// A workgroup owns 64 columns of M and one token split; its four waves take
+// 32-row chunks in turn. Each wave stages its chunk in a private LDS tile and
+// reads the B operand (8 consecutive tokens of one column per lane) with
+// ds_read_b64_tr_b16; the A operand comes from Vt [rows, T] directly. The
+// four waves' sums are added in a fixed order.
+template <int RT>
+__global__ __launch_bounds__(256) void lora_grad_mfma_kernel(const uint16_t* __restrict__ M, int64_t ldm, int64_t C,
+                                                             const uint16_t* __restrict__ Vt, int64_t ldv,
+                                                             int64_t T, int64_t t_per, float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) uint16_t sm[4][kGradRows * kGradLd];
+    __shared__ float red[4][16][kGradCols];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, g = lane >> 4;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kGradCols;
     const int ts = blockIdx.y;
     const int64_t tb = ts * t_per;
     const int64_t te = (tb + t_per < T) ? tb + t_per : T;
-    float acc[RP];
+    f32x4 acc[RT][4];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) acc[j] = 0.0f;
-    const bool cin = c < cols;
-    for (int64_t t = tb; t < te; ++t) {
-        const float x = cin ? bf16_to_f32(M[t * ldm + c]) : 0.0f;
-        const float* v = V + t * ldv;
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int j = 0; j < RP; ++j)
-            if (j < r) acc[j] = __builtin_fmaf(v[j], x, acc[j]);
+        for (int cb = 0; cb < 4; ++cb) acc[rt][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint16_t* tile = sm[wave];
+    auto load_chunk = [&](int64_t t, uint4 (&v)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (lane >> 3) + 8 * i;
+            const int64_t c = c0 + 8 * (lane & 7);
+            v[i] = (t + row < te && c < C) ? *reinterpret_cast<const uint4*>(M + (t + row) * ldm + c)
+                                           : make_uint4(0, 0, 0, 0);
+        }
+    };
+    uint4 cur[4];
+    int64_t t = tb + kGradRows * wave;
+    if (t < te) load_chunk(t, cur);
+    for (; t < te; t += 4 * kGradRows) {
+        uint4 nxt[4];
+        const int64_t tn = t + 4 * kGradRows;
+        if (tn < te) load_chunk(tn, nxt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(tile + ((lane >> 3) + 8 * i) * kGradLd + 8 * (lane & 7)) = cur[i];
+        // B operands: rows 8g + 0..7 of column 16 cb + li (two transposing reads)
+        bf16x8_t bv[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const uint16_t* base = tile + (8 * g + (li >> 2)) * kGradLd + 16 * cb + 4 * (li & 3);
+            const v4i16_g lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_g*)(reinterpret_cast<uintptr_t>(base)));
+            const v4i16_g hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_g*)(reinterpret_cast<uintptr_t>(base + 4 * kGradLd)));
+            const v8i16_g v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            bv[cb] = __builtin_bit_cast(bf16x8_t, v);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int64_t tt = t + 8 * g;
+            const uint16_t* vrow = Vt + (16 * rt + li) * ldv;
+            uint4 av;
+            if (tt + 8 <= te) {
+                av = *reinterpret_cast<const uint4*>(vrow + tt);
+            } else {  // last partial chunk of the split: element by element
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = (tt + e < te) ? vrow[tt + e] : 0u;
+                av = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            }
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                acc[rt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), bv[cb], acc[rt][cb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
     }
-    if (cin) {
+    // fixed-order sum of the four waves, one 16-row tile at a time
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int j = 0; j < RP; ++j) part[(static_cast<int64_t>(ts) * RP + j) * cols + c] = acc[j];
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][4 * g + r][16 * cb + li] = acc[rt][cb][r];
+        __syncthreads();
+        for (int e = tid; e < 16 * kGradCols; e += 256) {
+            const int j = e / kGradCols, c = e % kGradCols;
+            const float v = ((red[0][j][c] + red[1][j][c]) + red[2][j][c]) + red[3][j][c];
+            if (c0 + c < C) part[(static_cast<int64_t>(ts) * RT * 16 + 16 * rt + j) * C + c0 + c] = v;
+        }
+        __syncthreads();
     }
 }
 
-int launch_lora_grad_partial(const uint16_t* M, int64_t ldm, int64_t cols, const float* V, int64_t ldv, int r,
-                             int64_t T, int splits, float* part, hipStream_t stream) {
-    const int64_t t_per = ceil_div(T, splits);
-    const dim3 grid(static_cast<uint32_t>(ceil_div(cols, 256)), static_cast<uint32_t>(splits));
-    const int rp = lora_grad_rp(r);
+int64_t lora_vt_ld(int64_t T) { return ceil_div(T, 8) * 8; }
+
+int launch_lora_grad_partial(const uint16_t* M, int64_t ldm, int64_t cols, const uint16_t* Vt, int rp16, int64_t T,
+                             int splits, float* part, hipStream_t stream) {
+    const int64_t ldv = lora_vt_ld(T);
+    const int64_t t_per = ceil_div(ceil_div(T, splits), 4 * kGradRows) * 4 * kGradRows;
+    const dim3 grid(static_cast<uint32_t>(ceil_div(cols, kGradCols)), static_cast<uint32_t>(splits));
     timer_begin(QL_KERNEL_LORA_GRAD, stream);
-    switch (rp) {
-        case 16:
-            hipLaunchKernelGGL(lora_grad_partial_kernel<16>, grid, dim3(256), 0, stream, M, ldm, cols, V, ldv, r, T,
-                               t_per, part);
-            break;
-        case 32:
-            hipLaunchKernelGGL(lora_grad_partial_kernel<32>, grid, dim3(256), 0, stream, M, ldm, cols, V, ldv, r, T,
-                               t_per, part);
-            break;
-        case 64:
-            hipLaunchKernelGGL(lora_grad_partial_kernel<64>, grid, dim3(256), 0, stream, M, ldm, cols, V, ldv, r, T,
-                               t_per, part);
-            break;
+    switch (rp16 / 16) {
+#define QL_GRAD_CASE(R_)                                                                                        \
+    case R_:                                                                                                    \
+        hipLaunchKernelGGL(lora_grad_mfma_kernel<R_>, grid, dim3(256), 0, stream, M, ldm, cols, Vt, ldv, T,      \
+                           t_per, part);                                                                        \
+        break;
+        QL_GRAD_CASE(1)
+        QL_GRAD_CASE(2)
+        QL_GRAD_CASE(3)
+        QL_GRAD_CASE(4)
+        QL_GRAD_CASE(5)
+        QL_GRAD_CASE(6)
+        QL_GRAD_CASE(7)
+        QL_GRAD_CASE(8)
+#undef QL_GRAD_CASE
         default:
-            hipLaunchKernelGGL(lora_grad_partial_kernel<128>, grid, dim3(256), 0, stream, M, ldm, cols, V, ldv, r, T,
-                               t_per, part);
-            break;
+            return set_error(QL_ERR_SHAPE, "LoRA gradient: rank %d out of range", rp16);
     }
     timer_end(QL_KERNEL_LORA_GRAD, stream);
     return check_launch("LoRA gradient");
+}
+
+// Vt[j][t] = bf16(U[t][j]) for j < r, 0 for r <= j < rows (fp32 [T, r] in).
+__global__ void transpose_f32_bf16_kernel(const float* __restrict__ U, int64_t T, int r, int rows, int64_t ldv,
+                                          uint16_t* __restrict__ Vt) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= static_cast<int64_t>(rows) * T) return;
+    const int64_t j = idx / T, t = idx % T;
+    const float v = (j < r) ? U[t * r + j] : 0.0f;
+    Vt[j * ldv + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+int launch_transpose_f32_bf16(const float* U, int64_t T, int r, int rows, uint16_t* Vt, hipStream_t stream) {
+    hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3(static_cast<uint32_t>(ceil_div(static_cast<int64_t>(rows) * T, 256))),
+                       dim3(256), 0, stream, U, T, r, rows, lora_vt_ld(T), Vt);
+    return check_launch("U transpose");
 }
 
 __global__ void lora_grad_final_kernel(const float* __restrict__ part, int splits, int rp, int r, int64_t cols,

@@ -27,6 +27,7 @@ int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStrea
 
 // out_f[t][j] = alpha_f * sum_k P[t][k] Q[j][k]   (j < ncols_f)
 // out_b[t][j] = bf16(alpha_b * same)              (j < ld_b; zero for j >= qrows)
+// out_bt[j][t] = the same bf16 values transposed   (j < rows_bt)
 struct SkinnyArgs {
     const uint16_t* P;
     int64_t ldp;
@@ -42,6 +43,9 @@ struct SkinnyArgs {
     float alpha_b;
     uint16_t* out_b;
     int64_t ld_b;
+    uint16_t* out_bt;  // optional: out_bt[j * ld_bt + t] = bf16(alpha_b * sum), j < rows_bt
+    int rows_bt;
+    int64_t ld_bt;
 };
 int launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 
@@ -63,11 +67,14 @@ int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, cons
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
                    uint16_t* dX, int64_t T, int64_t N, int64_t K, hipStream_t stream);
 
-int lora_grad_rp(int r);
+int lora_grad_rp(int r);  // rank rounded up to 16
+int64_t lora_vt_ld(int64_t T);  // row stride of the transposed [rp16, T] operands
 int lora_grad_splits(int64_t T, int64_t cols);
-// part[ts][j][c] = sum_{t in split ts} V[t][j] * M[t][c]
-int launch_lora_grad_partial(const uint16_t* M, int64_t ldm, int64_t cols, const float* V, int64_t ldv, int r,
-                             int64_t T, int splits, float* part, hipStream_t stream);
+// part[ts][j][c] = sum_{t in split ts} Vt[j][t] * M[t][c] (Vt bf16 [rp16, T])
+int launch_lora_grad_partial(const uint16_t* M, int64_t ldm, int64_t cols, const uint16_t* Vt, int rp16, int64_t T,
+                             int splits, float* part, hipStream_t stream);
+// Vt[j][t] = bf16(U[t][j]), zero rows from r to rows
+int launch_transpose_f32_bf16(const float* U, int64_t T, int r, int rows, uint16_t* Vt, hipStream_t stream);
 // out[j][c] (layout_jc) or out[c][j] = (acc ? out : 0) + scale * sum_ts part[ts][j][c]
 int launch_lora_grad_final(const float* part, int splits, int rp, int r, int64_t cols, float scale, bool layout_jc,
                            float* out, int accumulate, hipStream_t stream);
