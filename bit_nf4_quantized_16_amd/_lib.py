@@ -76,7 +76,7 @@ SIGNATURES = {
 def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
-            "libqlora_nf4.so is not built (%s); run `python -m bit_nf4_quantized_16_amd.build` "
+            "libqlora_nf4.so is not built (%s); run `python bit_nf4_quantized_16_amd/build.py` "
             "or __graft_entry__.build()" % path
         )
     lib = ctypes.CDLL(path)

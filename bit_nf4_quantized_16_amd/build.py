@@ -1,6 +1,8 @@
 """Build libqlora_nf4.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m bit_nf4_quantized_16_amd.build [--jobs N] [--verbose]
+    python bit_nf4_quantized_16_amd/build.py [--jobs N] [--verbose]
+
+(run as a script: importing the package loads the library being rebuilt)
 
 Every source is compiled for gfx950 only, with floating-point contraction
 off (the quantization outputs are compared bit for bit) and without packed

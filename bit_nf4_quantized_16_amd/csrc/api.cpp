@@ -140,6 +140,7 @@ struct FwdWs {
     uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
     float* Uf = nullptr;     // fp32 [T, r], GEMV path without U_out
     float* part = nullptr;   // fp32 [chunks, T, N], GEMV path
+    float* split = nullptr;  // fp32 split-K partials of the GEMM path
     size_t bytes = 0;
 };
 
@@ -152,9 +153,13 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_
     if (T <= kGemvMaxT) {
         f.part = c.take<float>(static_cast<size_t>(gemv_num_chunks(K)) * T * N);
         if (r > 0 && !have_uout) f.Uf = c.take<float>(static_cast<size_t>(T) * r);
-    } else if (r > 0) {
-        f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
-        if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
+    } else {
+        if (r > 0) {
+            f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+            if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
+        }
+        const size_t sb = gemm_split_bytes(N, T, K);
+        if (sb) f.split = c.take<float>(sb / sizeof(float));
     }
     f.bytes = align_up(c.off, 256);
     return f;
@@ -168,6 +173,7 @@ struct BwdWs {
     uint16_t* Ut = nullptr;  // bf16 [rp16, T] = U^T, dB's MFMA operand
     float* partA = nullptr;  // fp32 [splitsA, rp16, K]
     float* partB = nullptr;  // fp32 [splitsB, rp16, N]
+    float* split = nullptr;  // fp32 split-K partials of the dX GEMM
     size_t bytes = 0;
 };
 
@@ -187,6 +193,10 @@ BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_
             b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
             b.partB = c.take<float>(static_cast<size_t>(lora_grad_splits(T, N)) * rp16 * N);
         }
+    }
+    if (want_dx) {
+        const size_t sb = gemm_split_bytes(K, T, N);
+        if (sb) b.split = c.take<float>(sb / sizeof(float));
     }
     b.bytes = align_up(c.off, 256);
     return b;
@@ -314,7 +324,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
             r_b = rp;
         }
     }
-    return launch_gemm_fwd(wd, X, f.Us, Bsrc, ld_b, r_b, rp, Y, T, N, K, st);
+    return launch_gemm_fwd(wd, X, f.Us, Bsrc, ld_b, r_b, rp, Y, T, N, K, f.split, st);
 }
 
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
@@ -368,7 +378,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if ((s = launch_skinny(a, st)) != QL_OK) return s;
     }
     if (want_dx) {
-        if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, st)) != QL_OK) return s;
+        if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, b.split, st)) != QL_OK) return s;
     }
     if (want_da) {
         const int sp = lora_grad_splits(T, K);

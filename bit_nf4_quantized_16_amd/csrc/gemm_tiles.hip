@@ -25,6 +25,7 @@
 // block, or half of one, with a single absmax); dX reads its A operand
 // through ds_read_b64_tr_b16, which hands each lane a column segment. The
 // LoRA term follows as rp/64 extra reduction steps over the rank.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -46,6 +47,8 @@ struct TileArgs {
     uint16_t* out;  // forward: Y [T, N]; dX: dX [T, K]
     int64_t T, N, K;
     int tiles_a, tiles_t;
+    int splits;   // > 1: the reduction is split over gridDim.y workgroups
+    float* part;  // split partial tiles, fp32 [splits, T, MA]
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -117,7 +120,13 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     const int64_t t0 = static_cast<int64_t>(logical / p.tiles_a) * TT;
     const int64_t MA = DX ? p.K : p.N;
     const int64_t RED = DX ? p.N : p.K;
-    const int msteps = static_cast<int>(ceil_div(RED, kStep));
+    const int nsteps_all = static_cast<int>(ceil_div(RED, kStep));
+    // split-K: this workgroup covers reduction steps [sb, se)
+    const int split = blockIdx.y;
+    const int spp = (nsteps_all + p.splits - 1) / p.splits;
+    const int sb = split * spp;
+    const int se = min(nsteps_all, sb + spp);
+    const int msteps = se;
     const float mu = DQ ? *p.w.mean : 0.0f;
 
     // ---- token tile: direct loads into LDS --------------------------------
@@ -220,12 +229,13 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     //   step s:   token loads for s+1 -> the other stage; codes for s+2 -> the
     //             free register set; MFMAs on stage s; expand step s+1.
     Codes<CC> cs0, cs1;
-    dma(0, sX0);
-    gcodes(0, cs0);
-    gcodes(min(1, msteps - 1), cs1);
-    expand(0, cs0, sA0);
+    if (sb < se) {
+    dma(sb, sX0);
+    gcodes(sb, cs0);
+    gcodes(min(sb + 1, msteps - 1), cs1);
+    expand(sb, cs0, sA0);
     __syncthreads();
-    for (int s = 0; s < msteps; s += 2) {
+    for (int s = sb; s < msteps; s += 2) {
         dma(min(s + 1, msteps - 1), sX1);
         gcodes(min(s + 2, msteps - 1), cs0);
         if (expand_first) {
@@ -248,9 +258,11 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         }
         __syncthreads();
     }
+    }  // sb < se
 
-    // LoRA term: rp/64 more reduction steps over the rank, staged directly.
-    for (int ls = 0; ls < p.rp / kStep; ++ls) {
+    // LoRA term: rp/64 more reduction steps over the rank, staged directly
+    // (by the first split only).
+    for (int ls = 0; ls < (split == 0 ? p.rp / kStep : 0); ++ls) {
         const int64_t j0 = static_cast<int64_t>(ls) * kStep;
 #pragma unroll
         for (int i = 0; i < TT * 8 / NTHR; ++i) {
@@ -297,7 +309,11 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
             for (int qq = 0; qq < 4; ++qq) {
                 const int64_t m = m0 + wa * MW + a * 32 + 8 * qq + 4 * (lane >> 5);
                 const int64_t t = t0 + wt * TW + b * 32 + (lane & 31);
-                if (t < p.T && m < MA) {
+                if (t < p.T && m < MA && p.splits > 1) {
+                    float4 v = make_float4(acc[a][b][4 * qq], acc[a][b][4 * qq + 1], acc[a][b][4 * qq + 2],
+                                           acc[a][b][4 * qq + 3]);
+                    *reinterpret_cast<float4*>(p.part + (static_cast<int64_t>(split) * p.T + t) * MA + m) = v;
+                } else if (t < p.T && m < MA) {
                     uint2 v;
                     v.x = pack_bf16x2(acc[a][b][4 * qq], acc[a][b][4 * qq + 1]);
                     v.y = pack_bf16x2(acc[a][b][4 * qq + 2], acc[a][b][4 * qq + 3]);
@@ -321,28 +337,34 @@ int cu_count() {
     return cached;
 }
 
-// Tile edge for an MA x T output: the larger tile moves less LDS traffic per
-// flop, the smaller one fills the chip on small grids. QLORA_NF4_GEMM_TILE=128
-// or 256 forces one (tests run both).
-int pick_tile(int64_t MA, int64_t T) {
-    const char* e = std::getenv("QLORA_NF4_GEMM_TILE");
-    if (e && std::strcmp(e, "128") == 0) return 128;
-    if (e && std::strcmp(e, "256") == 0) return 256;
-    const int64_t cus = cu_count();
-    const int64_t n256 = ceil_div(MA, 256) * ceil_div(T, 256);
-    const int64_t n128 = ceil_div(MA, 128) * ceil_div(T, 128);
-    const double c256 = static_cast<double>(ceil_div(n256, cus)) * 65536.0;
-    const double c128 = static_cast<double>(ceil_div(n128, 2 * cus)) * 2.0 * 16384.0 / 0.75;
-    return c128 < c256 ? 128 : 256;
+__global__ void split_reduce_kernel(const float* __restrict__ part, int splits, int64_t n4, uint16_t* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    float4 s = reinterpret_cast<const float4*>(part)[i];
+    for (int k = 1; k < splits; ++k) {
+        const float4 v = reinterpret_cast<const float4*>(part)[k * n4 + i];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    uint2 o;
+    o.x = pack_bf16x2(s.x, s.y);
+    o.y = pack_bf16x2(s.z, s.w);
+    reinterpret_cast<uint2*>(out)[i] = o;
 }
 
 template <bool DX>
-int launch_tiles(TileArgs& a, int kid, const char* what, hipStream_t stream) {
+int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStream_t stream) {
     const int64_t MA = DX ? a.K : a.N;
-    const int tile = pick_tile(MA, a.T);
+    const GemmPlan pl = plan_gemm(MA, a.T, DX ? a.N : a.K);
+    const int tile = pl.tile;
     a.tiles_a = static_cast<int>(ceil_div(MA, tile));
     a.tiles_t = static_cast<int>(ceil_div(a.T, tile));
-    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.tiles_a) * a.tiles_t));
+    a.splits = pl.splits;
+    a.part = split_ws;
+    if (a.splits > 1 && split_ws == nullptr) return set_error(QL_ERR_WORKSPACE, "%s: split workspace missing", what);
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.tiles_a) * a.tiles_t), static_cast<uint32_t>(a.splits));
     timer_begin(kid, stream);
     if (tile == 256) {
         if (a.w.dq)
@@ -355,14 +377,54 @@ int launch_tiles(TileArgs& a, int kid, const char* what, hipStream_t stream) {
         else
             hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, false>), grid, dim3(256), 0, stream, a);
     }
+    if (a.splits > 1) {
+        const int64_t n4 = a.T * MA / 4;
+        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<uint32_t>(ceil_div(n4, 256))), dim3(256), 0, stream,
+                           split_ws, a.splits, n4, a.out);
+    }
     timer_end(kid, stream);
     return check_launch(what);
 }
 
 }  // namespace
 
+// Tile and split plan for an MA x T output with a reduction of RED. The
+// 256x256 tile (eight waves) moves the least LDS traffic per flop; when its
+// grid cannot fill the chip the reduction is split (partial fp32 tiles added
+// in a fixed order afterwards) or, for short reductions, the 128x128 tile is
+// used. QLORA_NF4_GEMM_TILE=128 or 256 forces the tile (tests run both),
+// QLORA_NF4_GEMM_SPLITS=n forces the split count of the 256 tile.
+GemmPlan plan_gemm(int64_t MA, int64_t T, int64_t RED) {
+    GemmPlan pl;
+    const char* e = std::getenv("QLORA_NF4_GEMM_TILE");
+    const char* es = std::getenv("QLORA_NF4_GEMM_SPLITS");
+    const int64_t cus = cu_count();
+    const int64_t steps = ceil_div(RED, 64);
+    const int64_t n256 = ceil_div(MA, 256) * ceil_div(T, 256);
+    const int64_t n128 = ceil_div(MA, 128) * ceil_div(T, 128);
+    int64_t splits = 1;
+    if (n256 < cus) splits = std::min<int64_t>(cus / n256, steps / 16);
+    if (splits < 1) splits = 1;
+    if (es) splits = std::max<int64_t>(1, std::min<int64_t>(std::atoi(es), steps));
+    splits = ceil_div(steps, ceil_div(steps, splits));  // no empty split
+    // relative cost in 256-tile step units: rounds x steps per round
+    const double c256 = static_cast<double>(ceil_div(n256 * splits, cus)) * ceil_div(steps, splits) +
+                        (splits > 1 ? 0.15 * steps : 0.0);
+    const double c128 = static_cast<double>(ceil_div(n128, 2 * cus)) * steps * 0.5 / 0.7;
+    pl.tile = (c128 < c256) ? 128 : 256;
+    if (e && std::strcmp(e, "128") == 0) pl.tile = 128;
+    if (e && std::strcmp(e, "256") == 0) pl.tile = 256;
+    pl.splits = (pl.tile == 256) ? static_cast<int>(splits) : 1;
+    return pl;
+}
+
+size_t gemm_split_bytes(int64_t MA, int64_t T, int64_t RED) {
+    const GemmPlan pl = plan_gemm(MA, T, RED);
+    return pl.splits > 1 ? static_cast<size_t>(pl.splits) * T * MA * sizeof(float) : 0;
+}
+
 int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bsrc, int64_t ld_b,
-                    int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, hipStream_t stream) {
+                    int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream) {
     TileArgs a;
     a.w = w;
     a.act = X;
@@ -376,11 +438,11 @@ int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, cons
     a.T = T;
     a.N = N;
     a.K = K;
-    return launch_tiles<false>(a, QL_KERNEL_GEMM_FWD, "dequant GEMM forward", stream);
+    return launch_tiles<false>(a, split_ws, QL_KERNEL_GEMM_FWD, "dequant GEMM forward", stream);
 }
 
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
-                   uint16_t* dX, int64_t T, int64_t N, int64_t K, hipStream_t stream) {
+                   uint16_t* dX, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream) {
     TileArgs a;
     a.w = w;
     a.act = dY;
@@ -394,7 +456,7 @@ int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, cons
     a.T = T;
     a.N = N;
     a.K = K;
-    return launch_tiles<true>(a, QL_KERNEL_GEMM_DX, "dequant GEMM dX", stream);
+    return launch_tiles<true>(a, split_ws, QL_KERNEL_GEMM_DX, "dequant GEMM dX", stream);
 }
 
 }  // namespace qlnf4

@@ -59,13 +59,23 @@ int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_
 int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, const float* U, const uint16_t* B, int r,
                        float scale, uint16_t* Y, hipStream_t stream);
 
+// Tile / split-K plan of the dequant GEMMs for an MA x T output with a
+// reduction of RED, and the fp32 workspace its split partials need.
+struct GemmPlan {
+    int tile;
+    int splits;
+};
+GemmPlan plan_gemm(int64_t MA, int64_t T, int64_t RED);
+size_t gemm_split_bytes(int64_t MA, int64_t T, int64_t RED);
+
 // Forward: Y = X W'^T + Us Bsrc^T over the padded rank rp (Us [T, rp] bf16 =
 // bf16(s U), zero beyond r; Bsrc [N, r_b] with row stride ld_b, 16-B rows).
 int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bsrc, int64_t ld_b,
-                    int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, hipStream_t stream);
+                    int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, float* split_ws,
+                    hipStream_t stream);
 // dX = dY W' + Gp A over the padded rank rp (Gp [T, rp] bf16, A [r, K]).
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
-                   uint16_t* dX, int64_t T, int64_t N, int64_t K, hipStream_t stream);
+                   uint16_t* dX, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream);
 
 int lora_grad_rp(int r);  // rank rounded up to 16
 int64_t lora_vt_ld(int64_t T);  // row stride of the transposed [rp16, T] operands

@@ -186,3 +186,15 @@ def test_both_gemm_tiles(qn, monkeypatch, tile, N, K, T, r):
     W = workloads.normal_weight(N, K, 0.02, seed=N + 3 * K)
     case = workloads.lora_case("tile%s_N%dK%dT%dr%d" % (tile, N, K, T, r), W, T, r, 2.0 * r, 1 / K, 0.05, seed=T)
     _run(qn, case)
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "5"])
+@pytest.mark.parametrize("N,K,T,r", [(512, 1024, 200, 16), (264, 2048, 300, 5), (1024, 640, 96, 64)])
+def test_split_reduction(qn, monkeypatch, splits, N, K, T, r):
+    """Split-K for grids too small to fill the chip: forced split counts of
+    the 256x256 tile, ragged shapes, both GEMMs."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    monkeypatch.setenv("QLORA_NF4_GEMM_SPLITS", splits)
+    W = workloads.normal_weight(N, K, 0.02, seed=N + K + int(splits))
+    case = workloads.lora_case("split%s_N%dK%dT%d" % (splits, N, K, T), W, T, r, 2.0 * r, 1 / K, 0.05, seed=T + 1)
+    _run(qn, case)
