@@ -139,8 +139,8 @@ struct FwdWs {
     uint16_t* Us = nullptr;  // bf16 [T, rp64] = bf16(s U), GEMM path
     uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
     float* Uf = nullptr;     // fp32 [T, r], GEMV path without U_out
-    float* part = nullptr;   // fp32 [chunks, T, N], GEMV path
     float* split = nullptr;  // fp32 split-K partials of the GEMM path
+    float* sk = nullptr;     // fp32 partials of the U = X A^T pre-pass
     size_t bytes = 0;
 };
 
@@ -150,8 +150,8 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_
     Carver c(ws);
     FwdWs f;
     const int rp = rank_pad64(r);
+    if (r > 0) f.sk = c.take<float>(skinny_workspace_bytes(T, K, r) / sizeof(float));
     if (T <= kGemvMaxT) {
-        f.part = c.take<float>(static_cast<size_t>(gemv_num_chunks(K)) * T * N);
         if (r > 0 && !have_uout) f.Uf = c.take<float>(static_cast<size_t>(T) * r);
     } else {
         if (r > 0) {
@@ -174,13 +174,18 @@ struct BwdWs {
     float* partA = nullptr;  // fp32 [splitsA, rp16, K]
     float* partB = nullptr;  // fp32 [splitsB, rp16, N]
     float* split = nullptr;  // fp32 split-K partials of the dX GEMM
+    float* skG = nullptr;    // fp32 partials of G = s dY B
+    float* skU = nullptr;    // fp32 partials of U = X A^T (recomputed)
     size_t bytes = 0;
 };
 
-BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db) {
+BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db,
+                bool have_u) {
     Carver c(ws);
     BwdWs b;
     if (r > 0) {
+        if (want_dx || want_da) b.skG = c.take<float>(skinny_workspace_bytes(T, N, r) / sizeof(float));
+        if (want_db && !have_u) b.skU = c.take<float>(skinny_workspace_bytes(T, K, r) / sizeof(float));
         const int rp = rank_pad64(r);
         const int rp16 = lora_grad_rp(r);
         if (want_dx || want_da) b.BT = c.take<uint16_t>(static_cast<size_t>(r) * N);
@@ -305,10 +310,9 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         float* U = U_out ? U_out : f.Uf;
         if (r > 0) {
             SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U, r, r, 0.0f, nullptr, 0, nullptr, 0, 0};
-            if ((s = launch_skinny(a, st)) != QL_OK) return s;
+            if ((s = launch_skinny(a, f.sk, st)) != QL_OK) return s;
         }
-        if ((s = launch_gemv(wd, X, T, N, K, f.part, st)) != QL_OK) return s;
-        return launch_gemv_reduce(f.part, gemv_num_chunks(K), T, N, U, B, r, scale, Y, st);
+        return launch_gemv(wd, X, T, N, K, U, B, r, scale, Y, st);
     }
     const int rp = rank_pad64(r);
     const uint16_t* Bsrc = B;
@@ -316,7 +320,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
     int r_b = r;
     if (r > 0) {
         SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U_out, r, U_out ? r : 0, scale, f.Us, rp, nullptr, 0, 0};
-        if ((s = launch_skinny(a, st)) != QL_OK) return s;
+        if ((s = launch_skinny(a, f.sk, st)) != QL_OK) return s;
         if (r % 8 != 0) {  // rows of B are not 16-byte aligned: pad them
             if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
             Bsrc = f.Bp;
@@ -329,7 +333,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
 
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
     if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
-    return carve_bwd(nullptr, rows, cols, T, r, true, true, true).bytes;
+    return carve_bwd(nullptr, rows, cols, T, r, true, true, true, false).bytes;
 }
 
 int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
@@ -357,7 +361,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
     const bool have_u = U_saved != nullptr;
     if (have_u && (s = check_ptr(U_saved, "U_saved")) != QL_OK) return s;
     if ((want_da || (want_db && !have_u)) && (s = check_ptr(X, "X")) != QL_OK) return s;
-    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db);
+    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db, have_u);
     if (need.bytes > 0) {
         if (ws == nullptr || ws_bytes < need.bytes)
             return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
@@ -365,7 +369,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db);
+    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db, have_u);
     const NF4Dev wd = to_dev(w);
     const int rp = rank_pad64(r);
     const int rp16 = lora_grad_rp(r);
@@ -375,7 +379,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if ((s = launch_transpose_pad(B, N, r, b.BT, N, st)) != QL_OK) return s;
         SkinnyArgs a{dY,      N, b.BT, N, r, T, N, scale, nullptr, 0, 0, scale, want_dx ? b.Gp : nullptr,
                      want_dx ? rp : 0, want_da ? b.Gt : nullptr, want_da ? rp16 : 0, lora_vt_ld(T)};
-        if ((s = launch_skinny(a, st)) != QL_OK) return s;
+        if ((s = launch_skinny(a, b.skG, st)) != QL_OK) return s;
     }
     if (want_dx) {
         if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, b.split, st)) != QL_OK) return s;
@@ -390,7 +394,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
             if ((s = launch_transpose_f32_bf16(U_saved, T, r, rp16, b.Ut, st)) != QL_OK) return s;
         } else {
             SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, nullptr, 0, 0, 1.0f, nullptr, 0, b.Ut, rp16, lora_vt_ld(T)};
-            if ((s = launch_skinny(a, st)) != QL_OK) return s;
+            if ((s = launch_skinny(a, b.skU, st)) != QL_OK) return s;
         }
         const int sp = lora_grad_splits(T, N);
         if ((s = launch_lora_grad_partial(dY, N, N, b.Ut, rp16, T, sp, b.partB, st)) != QL_OK) return s;

@@ -6,6 +6,7 @@
 // and w' = fl(T[c] * a') round exactly as stated (compared bit for bit).
 #include "common.h"
 #include "internal.h"
+#include "mm_common.h"
 
 namespace qlnf4 {
 
@@ -83,21 +84,61 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint8_t* __re
     }
 }
 
+// bf16 output: lane u expands block u (64 codes, two 16-byte loads) with the
+// register lookup of the block's sixteen bf16 products (the same values as
+// bf16(fl32(T[c] * a'))) and writes 128 bytes; a last partial block is done
+// element by element.
+template <bool DQ>
+__global__ __launch_bounds__(256) void nf4_dequantize_bf16_kernel(const uint8_t* __restrict__ packed,
+                                                                  const float* __restrict__ absmax,
+                                                                  const uint8_t* __restrict__ c8,
+                                                                  const float* __restrict__ scale,
+                                                                  const float* __restrict__ mean, int64_t n,
+                                                                  uint16_t* __restrict__ out) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t e0 = b * 64;
+    if (e0 >= n) return;
+    const float mu = DQ ? *mean : 0.0f;
+    const float a = block_absmax<DQ>(absmax, c8, scale, mu, b);
+    if (e0 + 64 <= n) {
+        const uint4 p0 = *reinterpret_cast<const uint4*>(packed + e0 / 2);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(packed + e0 / 2 + 16);
+        const Lut16 L = make_lut(a);
+        uint4* o = reinterpret_cast<uint4*>(out + e0);
+        o[0] = dequant8_lut(p0.x, L);
+        o[1] = dequant8_lut(p0.y, L);
+        o[2] = dequant8_lut(p0.z, L);
+        o[3] = dequant8_lut(p0.w, L);
+        o[4] = dequant8_lut(p1.x, L);
+        o[5] = dequant8_lut(p1.y, L);
+        o[6] = dequant8_lut(p1.z, L);
+        o[7] = dequant8_lut(p1.w, L);
+    } else {
+        for (int64_t e = e0; e < n; ++e) {
+            const uint32_t byte = packed[e / 2];
+            const uint32_t c = (e & 1) ? (byte & 0xFu) : (byte >> 4);
+            const float w = c_nf4[c] * a;
+            out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(w));
+        }
+    }
+}
+
 int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStream_t stream) {
     const int64_t n = w.rows * w.cols;
     const int64_t units = ceil_div(n, 32);
     const dim3 grid(static_cast<uint32_t>(ceil_div(units, 256)));
+    const dim3 grid64(static_cast<uint32_t>(ceil_div(ceil_div(n, 64), 256)));
     const bool dq = w.dq_blocksize != 0;
     timer_begin(QL_KERNEL_DEQUANTIZE, stream);
     if (dq && bf16_out)
-        hipLaunchKernelGGL((nf4_dequantize_kernel<true, true>), grid, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
-                           w.dq_scale, w.dq_mean, n, out);
+        hipLaunchKernelGGL(nf4_dequantize_bf16_kernel<true>, grid64, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
+                           w.dq_scale, w.dq_mean, n, static_cast<uint16_t*>(out));
     else if (dq)
         hipLaunchKernelGGL((nf4_dequantize_kernel<true, false>), grid, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
                            w.dq_scale, w.dq_mean, n, out);
     else if (bf16_out)
-        hipLaunchKernelGGL((nf4_dequantize_kernel<false, true>), grid, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
-                           w.dq_scale, w.dq_mean, n, out);
+        hipLaunchKernelGGL(nf4_dequantize_bf16_kernel<false>, grid64, dim3(256), 0, stream, w.packed, w.absmax, w.c8,
+                           w.dq_scale, w.dq_mean, n, static_cast<uint16_t*>(out));
     else
         hipLaunchKernelGGL((nf4_dequantize_kernel<false, false>), grid, dim3(256), 0, stream, w.packed, w.absmax,
                            w.c8, w.dq_scale, w.dq_mean, n, out);

@@ -12,6 +12,8 @@
 // decode-size T expands them straight into MFMA operand registers.
 // W' is the same bf16 value as nf4_dequantize produces (contraction is off
 // in this file so that a' = fl(fl(E(c8) S) + mu) rounds identically).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 #include "mm_common.h"
@@ -20,25 +22,36 @@ namespace qlnf4 {
 
 // ===========================================================================
 // Skinny GEMM (LoRA down-projections): out[t][j] = alpha * sum_k P[t][k] Q[j][k]
-// with j < 16*NT <= 128. One workgroup per 16 rows of P; its four waves split
-// the reduction and their partial tiles are added in a fixed order.
-// MFMA 16x16x32 bf16: A operand = P rows, B operand = Q rows.
+// with j < 16*NT <= 128. HBM-bound (it streams P once): the grid is 64-row
+// blocks of P x KS slices of the reduction, so that at least ~512 workgroups
+// are in flight; each wave owns 16 rows (MFMA 16x16x32 bf16, A operand = P
+// rows, B operand = Q rows) and writes fp32 partial sums; a second kernel adds
+// the KS partials in order and writes every requested output form.
 // ===========================================================================
+constexpr int kSkinnyRows = 64;
+
+int skinny_splits(int64_t T, int64_t kred) {
+    const int64_t blocks = ceil_div(T, kSkinnyRows);
+    int64_t ks = ceil_div(512, blocks);
+    const int64_t max_ks = std::max<int64_t>(1, kred / 256);
+    return static_cast<int>(std::min(ks, max_ks));
+}
+
 template <int NT>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
-    __shared__ float red[4][16][NT * 16];
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p, int ks_count, float* __restrict__ part) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, g = lane >> 4;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
-    const int64_t kw = ((p.kred + 127) / 128) * 32;  // per-wave share, multiple of 32
-    const int64_t kbeg = wave * kw;
-    const int64_t kend = (kbeg + kw < p.kred) ? kbeg + kw : p.kred;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kSkinnyRows + 16 * wave;
+    const int ks = blockIdx.y;
+    const int64_t kw = ceil_div(ceil_div(p.kred, ks_count), 32) * 32;
+    const int64_t kbeg = ks * kw;
+    const int64_t kend = std::min<int64_t>(kbeg + kw, p.kred);
     f32x4 acc[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool trow = (t0 + li) < p.T;
-    const uint16_t* prow = p.P + (t0 + li) * p.ldp;
-    for (int64_t k = kbeg; k < kend; k += 32) {
+    const uint16_t* prow = p.P + std::min<int64_t>(t0 + li, p.T - 1) * p.ldp;
+    auto step = [&](int64_t k) {
         const int64_t kk = k + 8 * g;
         const bool kin = kk < kend;
         uint4 av = make_uint4(0, 0, 0, 0);
@@ -50,41 +63,53 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
             if (j < p.qrows && kin) bv = *reinterpret_cast<const uint4*>(p.Q + j * p.ldq + kk);
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc[c], 0, 0, 0);
         }
+    };
+    int64_t k = kbeg;
+    for (; k + 64 <= kend; k += 64) {
+        step(k);
+        step(k + 32);
     }
+    for (; k < kend; k += 32) step(k);
+    // partial [ks][t][16 NT]: D[t = 4 g + r][j = 16 c + li]
+    const int64_t tl = t0 + 4 * g;
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][4 * g + r][16 * c + li] = acc[c][r];
-    __syncthreads();
-    int64_t ncols = p.out_b ? p.ld_b : 0;
-    if (p.out_bt && p.rows_bt > ncols) ncols = p.rows_bt;
-    if (ncols < NT * 16) ncols = NT * 16;
-    for (int64_t e = threadIdx.x; e < 16 * ncols; e += 256) {
-        const int tl = static_cast<int>(e / ncols);
-        const int j = static_cast<int>(e % ncols);
-        const int64_t t = t0 + tl;
-        if (t >= p.T) continue;
-        float sum = 0.0f;
-        if (j < NT * 16) sum = ((red[0][tl][j] + red[1][tl][j]) + red[2][tl][j]) + red[3][tl][j];
-        if (p.out_f && j < p.ncols_f) p.out_f[t * p.ld_f + j] = p.alpha_f * sum;
-        if (p.out_b && j < p.ld_b) {
-            const float v = (j < p.qrows) ? p.alpha_b * sum : 0.0f;
-            p.out_b[t * p.ld_b + j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-        }
-        if (p.out_bt && j < p.rows_bt) {
-            const float v = (j < p.qrows) ? p.alpha_b * sum : 0.0f;
-            p.out_bt[j * p.ld_bt + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-        }
-    }
+        for (int r = 0; r < 4; ++r)
+            if (tl + r < p.T) part[(static_cast<int64_t>(ks) * p.T + tl + r) * (16 * NT) + 16 * c + li] = acc[c][r];
 }
 
-int launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
+__global__ void skinny_reduce_kernel(SkinnyArgs p, int ks_count, int width, int64_t ncols,
+                                     const float* __restrict__ part) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= p.T * ncols) return;
+    const int64_t t = idx / ncols;
+    const int j = static_cast<int>(idx % ncols);
+    float sum = 0.0f;
+    if (j < width)
+        for (int k = 0; k < ks_count; ++k) sum += part[(static_cast<int64_t>(k) * p.T + t) * width + j];
+    if (p.out_f && j < p.ncols_f) p.out_f[t * p.ld_f + j] = p.alpha_f * sum;
+    const float vb = (j < p.qrows) ? p.alpha_b * sum : 0.0f;
+    const uint16_t hb = __builtin_bit_cast(uint16_t, static_cast<__bf16>(vb));
+    if (p.out_b && j < p.ld_b) p.out_b[t * p.ld_b + j] = hb;
+    if (p.out_bt && j < p.rows_bt) p.out_bt[j * p.ld_bt + t] = hb;
+}
+
+size_t skinny_workspace_bytes(int64_t T, int64_t kred, int qrows) {
+    const int nt = (qrows + 15) / 16;
+    return static_cast<size_t>(skinny_splits(T, kred)) * T * 16 * nt * sizeof(float);
+}
+
+int launch_skinny(const SkinnyArgs& a, float* part, hipStream_t stream) {
     const int nt = (a.qrows + 15) / 16;
-    const dim3 grid(static_cast<uint32_t>(ceil_div(a.T, 16)));
+    if (nt < 1 || nt > 8) return set_error(QL_ERR_SHAPE, "skinny GEMM: rank %d out of range", a.qrows);
+    if (part == nullptr) return set_error(QL_ERR_WORKSPACE, "skinny GEMM: workspace missing");
+    const int ks = skinny_splits(a.T, a.kred);
+    const dim3 grid(static_cast<uint32_t>(ceil_div(a.T, kSkinnyRows)), static_cast<uint32_t>(ks));
     switch (nt) {
-#define QL_SKINNY_CASE(N_)                                                          \
-    case N_:                                                                        \
-        hipLaunchKernelGGL(skinny_kernel<N_>, grid, dim3(256), 0, stream, a);      \
+#define QL_SKINNY_CASE(N_)                                                               \
+    case N_:                                                                             \
+        hipLaunchKernelGGL(skinny_kernel<N_>, grid, dim3(256), 0, stream, a, ks, part); \
         break;
         QL_SKINNY_CASE(1)
         QL_SKINNY_CASE(2)
@@ -95,9 +120,13 @@ int launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
         QL_SKINNY_CASE(7)
         QL_SKINNY_CASE(8)
 #undef QL_SKINNY_CASE
-        default:
-            return set_error(QL_ERR_SHAPE, "skinny GEMM: rank %d out of range", a.qrows);
     }
+    int64_t ncols = 16 * nt;
+    if (a.out_b && a.ld_b > ncols) ncols = a.ld_b;
+    if (a.out_bt && a.rows_bt > ncols) ncols = a.rows_bt;
+    if (a.out_f && a.ncols_f > ncols) ncols = a.ncols_f;
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(static_cast<uint32_t>(ceil_div(a.T * ncols, 256))), dim3(256), 0,
+                       stream, a, ks, 16 * nt, ncols, part);
     return check_launch("lora skinny GEMM");
 }
 
@@ -133,111 +162,103 @@ int launch_transpose_pad(const uint16_t* src, int64_t R, int64_t C, uint16_t* ds
 }
 
 // ===========================================================================
-// Dequant-GEMV for T <= 16 (decode). Workgroup = 64 output rows x one
-// 512-wide chunk of K; each wave owns 16 rows. Lane (i = l%16, g = l/16)
-// streams 16 bytes = 32 codes of row i per 128-wide step and expands them
-// straight into four MFMA A operands (the k order inside the step is
-// permuted identically for the x operand, which is read from LDS).
-// Partial sums per chunk go to a workspace; a second kernel adds the chunks
-// in order plus the LoRA term and rounds to bf16.
+// Dequant-GEMV for T <= 16 (decode), one kernel. A workgroup of eight waves
+// owns 16 output rows; wave w covers the w-th eighth of K. Lane (i = l%16,
+// g = l/16) streams 16 bytes = 32 codes of row i per 128-wide step (all of
+// the wave's code loads are issued before any math) and expands them in
+// registers (the v_perm lookup) into four MFMA 16x16x32 A operands; the x
+// operand (lane: token l%16, the matching 8 k) is read through L2, where all
+// workgroups share it. The eight partial tiles are added in a fixed order in
+// LDS, then s U B^T is added and the row is rounded to bf16.
 // ===========================================================================
-constexpr int kGemvRows = 64;
-constexpr int kGemvChunk = 512;
-constexpr int kGemvLd = kGemvChunk + 8;
+constexpr int kGemvRows = 16;
+constexpr int kGemvWaves = 8;
+constexpr int kGemvMaxSteps = 8;  // 128-wide steps per wave: K <= 8 * 8 * 128 = 8192 per pass
 
-int gemv_num_chunks(int64_t K) { return static_cast<int>(ceil_div(K, kGemvChunk)); }
-
-__global__ __launch_bounds__(256) void gemv_kernel(NF4Dev w, const uint16_t* __restrict__ X, int64_t T, int64_t N,
-                                                   int64_t K, float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) uint16_t sx[16 * kGemvLd];
-    __shared__ float tab[16];
+template <bool DQ>
+__global__ __launch_bounds__(512) void gemv_kernel(NF4Dev w, const uint16_t* __restrict__ X, int64_t T, int64_t N,
+                                                   int64_t K, const float* __restrict__ U,
+                                                   const uint16_t* __restrict__ B, int r, float scale,
+                                                   uint16_t* __restrict__ Y) {
+    __shared__ float red[kGemvWaves][kGemvRows][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kGemvRows;
-    const int chunk = blockIdx.y;
-    const int64_t kc0 = static_cast<int64_t>(chunk) * kGemvChunk;
-    if (tid < 16) tab[tid] = c_nf4_mm[tid];
-    // x chunk [16 x 512] -> LDS, zero outside [0,T) x [0,K)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i;
-        const int t = idx >> 6, c = idx & 63;
-        const int64_t k = kc0 + 8 * c;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < T && k < K) v = *reinterpret_cast<const uint4*>(X + t * K + k);
-        *reinterpret_cast<uint4*>(sx + t * kGemvLd + 8 * c) = v;
-    }
-    // this lane's row and its four 16-byte code loads, issued up front
-    const int64_t row = n0 + 16 * wave + li;
-    const float mu = w.dq ? *w.mean : 0.0f;
-    uint4 pk[4];
-    BlockConst bc[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int64_t k = kc0 + 128 * st + 32 * g;
-        if (row < N && k < K) {
-            const int64_t e = row * K + k;
-            pk[st] = *reinterpret_cast<const uint4*>(w.packed + e / 2);
-            bc[st] = load_block_const(w, e / 64);
-        } else {
-            pk[st] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-            bc[st].c8 = 0;
-            bc[st].s = 0.0f;
-        }
-    }
-    __syncthreads();
+    const int64_t row = std::min<int64_t>(n0 + li, N - 1);
+    const float mu = DQ ? *w.mean : 0.0f;
+    const int64_t ksteps = ceil_div(K, 128);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool tok = li < T;
+    const uint16_t* xrow = X + std::min<int64_t>(li, T - 1) * K;
+    // passes of kGemvMaxSteps steps per wave (one pass for K <= 8192)
+    for (int64_t base = 0; base < ksteps; base += kGemvWaves * kGemvMaxSteps) {
+        uint4 pk[kGemvMaxSteps];
+        BlockConst bc[kGemvMaxSteps];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const float a = (row < N && kc0 + 128 * st + 32 * g < K) ? block_value(bc[st], w.dq, mu) : 0.0f;
-        const uint32_t words[4] = {pk[st].x, pk[st].y, pk[st].z, pk[st].w};
+        for (int i = 0; i < kGemvMaxSteps; ++i) {
+            const int64_t st = base + wave + kGemvWaves * i;
+            // clamped into the row; lanes past K are zeroed below
+            const int64_t k = std::min<int64_t>(std::min<int64_t>(st, ksteps - 1) * 128 + 32 * g, K - 32);
+            const int64_t e = row * K + k;
+            pk[i] = *reinterpret_cast<const uint4*>(w.packed + e / 2);
+            if constexpr (DQ) {
+                bc[i].c8 = w.c8[e / 64];
+                bc[i].s = w.scale[e / 64 / QL_DQ_BLOCKSIZE];
+            } else {
+                bc[i].c8 = 0;
+                bc[i].s = w.absmax[e / 64];
+            }
+        }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const uint4 av = dequant8(words[m], a, tab);
-            const uint4 bv = *reinterpret_cast<const uint4*>(sx + li * kGemvLd + 128 * st + 32 * g + 8 * m);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+        for (int i = 0; i < kGemvMaxSteps; ++i) {
+            const int64_t st = base + wave + kGemvWaves * i;
+            if (st >= ksteps) break;
+            const int64_t k = st * 128 + 32 * g;
+            const bool kin = k < K;  // K % 64 == 0: a lane's 32 codes are all in or all out
+            const Lut16 L = make_lut(kin ? block_value(bc[i], DQ ? 1 : 0, mu) : 0.0f);
+            const uint32_t words[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint4 av = dequant8_lut(words[m], L);
+                const uint4 bv =
+                    (tok && kin) ? *reinterpret_cast<const uint4*>(xrow + k + 8 * m) : make_uint4(0, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+            }
         }
     }
-    // D[n = 4 g + r][t = li]
-    if (li < T) {
+    // D[n = 4 g + rr][t = li]
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t n = n0 + 16 * wave + 4 * g + r;
-            if (n < N) part[(static_cast<int64_t>(chunk) * T + li) * N + n] = acc[r];
+    for (int rr = 0; rr < 4; ++rr) red[wave][4 * g + rr][li] = acc[rr];
+    __syncthreads();
+    if (tid < kGemvRows * 16) {
+        const int nl = tid / 16, t = tid % 16;
+        const int64_t n = n0 + nl;
+        if (n < N && t < T) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < kGemvWaves; ++ww) sum += red[ww][nl][t];
+            if (r > 0) {
+                float lora = 0.0f;
+                for (int j = 0; j < r; ++j) lora = __builtin_fmaf(U[t * r + j], bf16_to_f32(B[n * r + j]), lora);
+                sum += scale * lora;
+            }
+            Y[t * N + n] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
         }
     }
 }
 
-int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, float* part,
-                hipStream_t stream) {
-    const dim3 grid(static_cast<uint32_t>(ceil_div(N, kGemvRows)), static_cast<uint32_t>(gemv_num_chunks(K)));
+int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const float* U,
+                const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(ceil_div(N, kGemvRows)));
     timer_begin(QL_KERNEL_GEMV, stream);
-    hipLaunchKernelGGL(gemv_kernel, grid, dim3(256), 0, stream, w, X, T, N, K, part);
+    if (w.dq)
+        hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(64 * kGemvWaves), 0, stream, w, X, T, N, K, U, B, r, scale,
+                           Y);
+    else
+        hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(64 * kGemvWaves), 0, stream, w, X, T, N, K, U, B, r, scale,
+                           Y);
     timer_end(QL_KERNEL_GEMV, stream);
     return check_launch("dequant GEMV");
-}
-
-__global__ void gemv_reduce_kernel(const float* __restrict__ part, int nchunks, int64_t T, int64_t N,
-                                   const float* __restrict__ U, const uint16_t* __restrict__ B, int r, float scale,
-                                   uint16_t* __restrict__ Y) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= T * N) return;
-    const int64_t t = idx / N, n = idx % N;
-    float sum = 0.0f;
-    for (int c = 0; c < nchunks; ++c) sum += part[(static_cast<int64_t>(c) * T + t) * N + n];
-    if (r > 0) {
-        float lora = 0.0f;
-        for (int j = 0; j < r; ++j) lora = __builtin_fmaf(U[t * r + j], bf16_to_f32(B[n * r + j]), lora);
-        sum += scale * lora;
-    }
-    Y[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
-}
-
-int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, const float* U, const uint16_t* B, int r,
-                       float scale, uint16_t* Y, hipStream_t stream) {
-    hipLaunchKernelGGL(gemv_reduce_kernel, dim3(static_cast<uint32_t>(ceil_div(T * N, 256))), dim3(256), 0, stream,
-                       part, nchunks, T, N, U, B, r, scale, Y);
-    return check_launch("GEMV reduce");
 }
 
 // ===========================================================================

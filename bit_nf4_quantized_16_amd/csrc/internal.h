@@ -47,17 +47,18 @@ struct SkinnyArgs {
     int rows_bt;
     int64_t ld_bt;
 };
-int launch_skinny(const SkinnyArgs& a, hipStream_t stream);
+// part: fp32 workspace of skinny_workspace_bytes(T, kred, qrows) bytes
+size_t skinny_workspace_bytes(int64_t T, int64_t kred, int qrows);
+int launch_skinny(const SkinnyArgs& a, float* part, hipStream_t stream);
 
 // dst[i][j] = src[i][j] for j < cols, 0 for cols <= j < ldd.
 int launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ldd, hipStream_t stream);
 // dst[c][r] = src[r][c] for r < R, 0 for R <= r < ldd.
 int launch_transpose_pad(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, int64_t ldd, hipStream_t stream);
 
-int gemv_num_chunks(int64_t K);
-int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, float* part, hipStream_t stream);
-int launch_gemv_reduce(const float* part, int nchunks, int64_t T, int64_t N, const float* U, const uint16_t* B, int r,
-                       float scale, uint16_t* Y, hipStream_t stream);
+// Y[t][n] = sum_k X[t][k] W'[n][k] + scale sum_j U[t][j] B[n][j] for T <= 16.
+int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const float* U,
+                const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream);
 
 // Tile / split-K plan of the dequant GEMMs for an MA x T output with a
 // reduction of RED, and the fp32 workspace its split partials need.
