@@ -138,22 +138,17 @@ int check_linear_shape(const ql_nf4_weight* w, int64_t T, int32_t r) {
 struct FwdWs {
     uint16_t* Us = nullptr;  // bf16 [T, rp64] = bf16(s U), GEMM path
     uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
-    float* Uf = nullptr;     // fp32 [T, r], GEMV path without U_out
     float* split = nullptr;  // fp32 split-K partials of the GEMM path
-    float* sk = nullptr;     // fp32 partials of the U = X A^T pre-pass
     size_t bytes = 0;
 };
 
 constexpr int64_t kGemvMaxT = 16;
 
-FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_uout) {
+FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r) {
     Carver c(ws);
     FwdWs f;
     const int rp = rank_pad64(r);
-    if (r > 0) f.sk = c.take<float>(skinny_workspace_bytes(T, K, r) / sizeof(float));
-    if (T <= kGemvMaxT) {
-        if (r > 0 && !have_uout) f.Uf = c.take<float>(static_cast<size_t>(T) * r);
-    } else {
+    if (T > kGemvMaxT) {  // the GEMV path needs no workspace
         if (r > 0) {
             f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
             if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
@@ -167,37 +162,25 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool have_
 
 // ---- backward workspace ------------------------------------------------
 struct BwdWs {
-    uint16_t* BT = nullptr;  // bf16 [r, N] = B^T (for G = s dY B)
-    uint16_t* Gp = nullptr;  // bf16 [T, rp64] = G, dX's LoRA operand
+    uint16_t* Gp = nullptr;  // bf16 [T, rp64] = G = s dY B, dX's LoRA operand
     uint16_t* Gt = nullptr;  // bf16 [rp16, T] = G^T, dA's MFMA operand
     uint16_t* Ut = nullptr;  // bf16 [rp16, T] = U^T, dB's MFMA operand
-    float* partA = nullptr;  // fp32 [splitsA, rp16, K]
-    float* partB = nullptr;  // fp32 [splitsB, rp16, N]
+    float* gpart = nullptr;  // fp32 token-split partials of dA and dB
     float* split = nullptr;  // fp32 split-K partials of the dX GEMM
-    float* skG = nullptr;    // fp32 partials of G = s dY B
-    float* skU = nullptr;    // fp32 partials of U = X A^T (recomputed)
     size_t bytes = 0;
 };
 
-BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db,
-                bool have_u) {
+BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db) {
     Carver c(ws);
     BwdWs b;
     if (r > 0) {
-        if (want_dx || want_da) b.skG = c.take<float>(skinny_workspace_bytes(T, N, r) / sizeof(float));
-        if (want_db && !have_u) b.skU = c.take<float>(skinny_workspace_bytes(T, K, r) / sizeof(float));
         const int rp = rank_pad64(r);
         const int rp16 = lora_grad_rp(r);
-        if (want_dx || want_da) b.BT = c.take<uint16_t>(static_cast<size_t>(r) * N);
         if (want_dx) b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
-        if (want_da) {
-            b.Gt = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
-            b.partA = c.take<float>(static_cast<size_t>(lora_grad_splits(T, K)) * rp16 * K);
-        }
-        if (want_db) {
-            b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
-            b.partB = c.take<float>(static_cast<size_t>(lora_grad_splits(T, N)) * rp16 * N);
-        }
+        if (want_da) b.Gt = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
+        if (want_db) b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
+        const size_t gb = lora_grads_part_bytes(T, want_da ? K : 0, want_db ? N : 0, r);
+        if (gb) b.gpart = c.take<float>(gb / sizeof(float));
     }
     if (want_dx) {
         const size_t sb = gemm_split_bytes(K, T, N);
@@ -278,7 +261,7 @@ int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* strea
 
 size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
     if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
-    return carve_fwd(nullptr, rows, cols, T, r, false).bytes;
+    return carve_fwd(nullptr, rows, cols, T, r).bytes;
 }
 
 int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A, const uint16_t* B,
@@ -296,7 +279,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         if ((s = check_ptr(B, "B")) != QL_OK) return s;
         if (U_out != nullptr && (s = check_ptr(U_out, "U_out")) != QL_OK) return s;
     }
-    const FwdWs need = carve_fwd(nullptr, N, K, T, r, U_out != nullptr);
+    const FwdWs need = carve_fwd(nullptr, N, K, T, r);
     if (need.bytes > 0) {
         if (ws == nullptr || ws_bytes < need.bytes)
             return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
@@ -304,23 +287,31 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const FwdWs f = carve_fwd(ws, N, K, T, r, U_out != nullptr);
+    const FwdWs f = carve_fwd(ws, N, K, T, r);
     const NF4Dev wd = to_dev(w);
-    if (T <= kGemvMaxT) {
-        float* U = U_out ? U_out : f.Uf;
-        if (r > 0) {
-            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U, r, r, 0.0f, nullptr, 0, nullptr, 0, 0};
-            if ((s = launch_skinny(a, f.sk, st)) != QL_OK) return s;
-        }
-        return launch_gemv(wd, X, T, N, K, U, B, r, scale, Y, st);
-    }
+    if (T <= kGemvMaxT) return launch_gemv(wd, X, T, N, K, A, B, r, scale, Y, U_out, st);
     const int rp = rank_pad64(r);
     const uint16_t* Bsrc = B;
     int64_t ld_b = r;
     int r_b = r;
     if (r > 0) {
-        SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, U_out, r, U_out ? r : 0, scale, f.Us, rp, nullptr, 0, 0};
-        if ((s = launch_skinny(a, f.sk, st)) != QL_OK) return s;
+        // U = X A^T: fp32 for the caller, bf16(s U) padded to rp for the epilogue
+        ProjArgs a{};
+        a.proj = 1;
+        a.P = X;
+        a.ldp = K;
+        a.Q = A;
+        a.ldq = K;
+        a.rq = r;
+        a.T = T;
+        a.kred = K;
+        a.alpha_f = 1.0f;
+        a.out_f = U_out;
+        a.ld_f = r;
+        a.alpha_b = scale;
+        a.out_b = f.Us;
+        a.ld_b = rp;
+        if ((s = launch_lora_proj(a, false, st)) != QL_OK) return s;
         if (r % 8 != 0) {  // rows of B are not 16-byte aligned: pad them
             if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
             Bsrc = f.Bp;
@@ -333,7 +324,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
 
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
     if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
-    return carve_bwd(nullptr, rows, cols, T, r, true, true, true, false).bytes;
+    return carve_bwd(nullptr, rows, cols, T, r, true, true, true).bytes;
 }
 
 int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
@@ -361,7 +352,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
     const bool have_u = U_saved != nullptr;
     if (have_u && (s = check_ptr(U_saved, "U_saved")) != QL_OK) return s;
     if ((want_da || (want_db && !have_u)) && (s = check_ptr(X, "X")) != QL_OK) return s;
-    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db, have_u);
+    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db);
     if (need.bytes > 0) {
         if (ws == nullptr || ws_bytes < need.bytes)
             return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
@@ -369,36 +360,65 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db, have_u);
+    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db);
     const NF4Dev wd = to_dev(w);
     const int rp = rank_pad64(r);
     const int rp16 = lora_grad_rp(r);
-    if (r > 0 && (want_dx || want_da)) {
-        // G = s dY B: skinny GEMM over N with Q = B^T; bf16 copies for dX (row
-        // major, padded to rp64) and for dA (transposed)
-        if ((s = launch_transpose_pad(B, N, r, b.BT, N, st)) != QL_OK) return s;
-        SkinnyArgs a{dY,      N, b.BT, N, r, T, N, scale, nullptr, 0, 0, scale, want_dx ? b.Gp : nullptr,
-                     want_dx ? rp : 0, want_da ? b.Gt : nullptr, want_da ? rp16 : 0, lora_vt_ld(T)};
-        if ((s = launch_skinny(a, b.skG, st)) != QL_OK) return s;
+    const int64_t ldv = lora_vt_ld(T);
+    if (r > 0 && (want_dx || want_da || (want_db && have_u))) {
+        // G = s dY B (B read in its own layout): bf16 row-major padded to rp
+        // for the dX epilogue, bf16 transposed for dA; U^T from U_saved for dB
+        ProjArgs a{};
+        a.proj = (want_dx || want_da) ? 1 : 0;
+        a.P = dY;
+        a.ldp = N;
+        a.Q = B;
+        a.ldq = r;
+        a.rq = r;
+        a.T = T;
+        a.kred = N;
+        a.alpha_b = scale;
+        a.out_b = want_dx ? b.Gp : nullptr;
+        a.ld_b = rp;
+        a.out_bt = want_da ? b.Gt : nullptr;
+        a.rows_bt = rp16;
+        a.ld_bt = ldv;
+        if (want_db && have_u) {
+            a.Usrc = U_saved;
+            a.ru = r;
+            a.Ut = b.Ut;
+            a.rows_ut = rp16;
+            a.ld_ut = ldv;
+        }
+        if ((s = launch_lora_proj(a, true, st)) != QL_OK) return s;
+    }
+    if (r > 0 && want_db && !have_u) {  // U^T = (X A^T)^T recomputed
+        ProjArgs a{};
+        a.proj = 1;
+        a.P = X;
+        a.ldp = K;
+        a.Q = A;
+        a.ldq = K;
+        a.rq = r;
+        a.T = T;
+        a.kred = K;
+        a.alpha_b = 1.0f;
+        a.out_bt = b.Ut;
+        a.rows_bt = rp16;
+        a.ld_bt = ldv;
+        if ((s = launch_lora_proj(a, false, st)) != QL_OK) return s;
     }
     if (want_dx) {
         if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, b.split, st)) != QL_OK) return s;
     }
-    if (want_da) {
-        const int sp = lora_grad_splits(T, K);
-        if ((s = launch_lora_grad_partial(X, K, K, b.Gt, rp16, T, sp, b.partA, st)) != QL_OK) return s;
-        if ((s = launch_lora_grad_final(b.partA, sp, rp16, r, K, 1.0f, true, dA, accumulate, st)) != QL_OK) return s;
-    }
-    if (want_db) {
-        if (have_u) {
-            if ((s = launch_transpose_f32_bf16(U_saved, T, r, rp16, b.Ut, st)) != QL_OK) return s;
-        } else {
-            SkinnyArgs a{X, K, A, K, r, T, K, 1.0f, nullptr, 0, 0, 1.0f, nullptr, 0, b.Ut, rp16, lora_vt_ld(T)};
-            if ((s = launch_skinny(a, b.skU, st)) != QL_OK) return s;
-        }
-        const int sp = lora_grad_splits(T, N);
-        if ((s = launch_lora_grad_partial(dY, N, N, b.Ut, rp16, T, sp, b.partB, st)) != QL_OK) return s;
-        if ((s = launch_lora_grad_final(b.partB, sp, rp16, r, N, scale, false, dB, accumulate, st)) != QL_OK) return s;
+    if (want_da || want_db) {
+        GradArgs g{};
+        g.r = r;
+        g.T = T;
+        g.accumulate = accumulate;
+        if (want_da) g.pb[0] = GradProblem{X, K, K, b.Gt, ldv, dA, 1, 1.0f, nullptr};
+        if (want_db) g.pb[1] = GradProblem{dY, N, N, b.Ut, ldv, dB, 0, scale, nullptr};
+        if ((s = launch_lora_grads(g, b.gpart, st)) != QL_OK) return s;
     }
     return QL_OK;
 }

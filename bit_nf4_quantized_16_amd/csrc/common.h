@@ -104,13 +104,22 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
+// Orders a wave's LDS writes before its following LDS reads (and the reads
+// before later writes) when lanes read what other lanes of the same wave
+// wrote: no workgroup barrier is needed within one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Two fp32 -> two bf16 packed in a u32 (lo in the low half), round to
 // nearest even (v_cvt_pk_bf16_f32 on gfx950).
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 l = static_cast<__bf16>(lo);
-    __bf16 h = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+    const f32x2_cvt v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt));
 }
 
 // OCP FP8 E4M3FN code -> fp32 (exact). Codes 0x7F / 0xFF (NaN) never occur

@@ -84,10 +84,13 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint8_t* __re
     }
 }
 
-// bf16 output: lane u expands block u (64 codes, two 16-byte loads) with the
-// register lookup of the block's sixteen bf16 products (the same values as
-// bf16(fl32(T[c] * a'))) and writes 128 bytes; a last partial block is done
-// element by element.
+// bf16 output. Lane l of a wave expands block bw + l (64 codes, two 16-byte
+// loads) with the register lookup of the block's sixteen bf16 products (the
+// same values as bf16(fl32(T[c] * a'))) into 128 bytes. Written directly,
+// each store instruction would touch 64 lines 128 bytes apart; instead the
+// wave parks its 8 KiB in LDS (row stride 144 bytes) and stores it back so
+// that one instruction writes 1 KiB of consecutive bytes. The last wave of a
+// ragged tensor stores lane by lane, a last partial block element by element.
 template <bool DQ>
 __global__ __launch_bounds__(256) void nf4_dequantize_bf16_kernel(const uint8_t* __restrict__ packed,
                                                                   const float* __restrict__ absmax,
@@ -95,16 +98,37 @@ __global__ __launch_bounds__(256) void nf4_dequantize_bf16_kernel(const uint8_t*
                                                                   const float* __restrict__ scale,
                                                                   const float* __restrict__ mean, int64_t n,
                                                                   uint16_t* __restrict__ out) {
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t e0 = b * 64;
-    if (e0 >= n) return;
+    __shared__ uint4 stage[4][64 * 9];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t bw = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 64;  // first block of the wave
+    const int64_t b = bw + lane;
+    const int64_t nfull = n / 64;
+    if (bw * 64 >= n) return;  // wave-uniform
     const float mu = DQ ? *mean : 0.0f;
-    const float a = block_absmax<DQ>(absmax, c8, scale, mu, b);
-    if (e0 + 64 <= n) {
-        const uint4 p0 = *reinterpret_cast<const uint4*>(packed + e0 / 2);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(packed + e0 / 2 + 16);
+    if (bw + 64 <= nfull) {
+        const float a = block_absmax<DQ>(absmax, c8, scale, mu, b);
+        const uint4 p0 = *reinterpret_cast<const uint4*>(packed + b * 32);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(packed + b * 32 + 16);
         const Lut16 L = make_lut(a);
-        uint4* o = reinterpret_cast<uint4*>(out + e0);
+        uint4* sl = stage[wave] + lane * 9;
+        sl[0] = dequant8_lut(p0.x, L);
+        sl[1] = dequant8_lut(p0.y, L);
+        sl[2] = dequant8_lut(p0.z, L);
+        sl[3] = dequant8_lut(p0.w, L);
+        sl[4] = dequant8_lut(p1.x, L);
+        sl[5] = dequant8_lut(p1.y, L);
+        sl[6] = dequant8_lut(p1.z, L);
+        sl[7] = dequant8_lut(p1.w, L);
+        wave_lds_sync();
+        uint4* o = reinterpret_cast<uint4*>(out + bw * 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[64 * i + lane] = stage[wave][(8 * i + (lane >> 3)) * 9 + (lane & 7)];
+    } else if (b < nfull) {
+        const float a = block_absmax<DQ>(absmax, c8, scale, mu, b);
+        const uint4 p0 = *reinterpret_cast<const uint4*>(packed + b * 32);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(packed + b * 32 + 16);
+        const Lut16 L = make_lut(a);
+        uint4* o = reinterpret_cast<uint4*>(out + b * 64);
         o[0] = dequant8_lut(p0.x, L);
         o[1] = dequant8_lut(p0.y, L);
         o[2] = dequant8_lut(p0.z, L);
@@ -113,12 +137,12 @@ __global__ __launch_bounds__(256) void nf4_dequantize_bf16_kernel(const uint8_t*
         o[5] = dequant8_lut(p1.y, L);
         o[6] = dequant8_lut(p1.z, L);
         o[7] = dequant8_lut(p1.w, L);
-    } else {
-        for (int64_t e = e0; e < n; ++e) {
+    } else if (b * 64 < n) {
+        const float a = block_absmax<DQ>(absmax, c8, scale, mu, b);
+        for (int64_t e = b * 64; e < n; ++e) {
             const uint32_t byte = packed[e / 2];
             const uint32_t c = (e & 1) ? (byte & 0xFu) : (byte >> 4);
-            const float w = c_nf4[c] * a;
-            out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(w));
+            out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(c_nf4[c] * a));
         }
     }
 }
@@ -127,7 +151,7 @@ int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStrea
     const int64_t n = w.rows * w.cols;
     const int64_t units = ceil_div(n, 32);
     const dim3 grid(static_cast<uint32_t>(ceil_div(units, 256)));
-    const dim3 grid64(static_cast<uint32_t>(ceil_div(ceil_div(n, 64), 256)));
+    const dim3 grid64(static_cast<uint32_t>(ceil_div(ceil_div(n, 64), 256)));  // a wave per 64 blocks
     const bool dq = w.dq_blocksize != 0;
     timer_begin(QL_KERNEL_DEQUANTIZE, stream);
     if (dq && bf16_out)

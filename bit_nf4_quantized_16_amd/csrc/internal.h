@@ -25,40 +25,45 @@ int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* sca
                         hipStream_t stream);
 int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStream_t stream);
 
-// out_f[t][j] = alpha_f * sum_k P[t][k] Q[j][k]   (j < ncols_f)
-// out_b[t][j] = bf16(alpha_b * same)              (j < ld_b; zero for j >= qrows)
-// out_bt[j][t] = the same bf16 values transposed   (j < rows_bt)
-struct SkinnyArgs {
+// LoRA projection V[t][j] = sum_k P[t][k] Q[j][k] (j < rq), one launch:
+//   out_f[t][j]  = alpha_f V[t][j]                      (fp32, j < rq)
+//   out_b[t][j]  = bf16(alpha_b V[t][j]), 0 for j >= rq  (j < ld_b)
+//   out_bt[j][t] = the same bf16 values transposed       (j < rows_bt)
+// Q is A-like (q_cols false: Q[j][k] at Q + j ldq + k) or B-like (q_cols
+// true: Q[j][n] = B[n][j], B [kred, rq] row-major). Side job, done whatever
+// proj says: Ut[j][t] = bf16(Usrc[t][j]) for j < ru, 0 for ru <= j < rows_ut.
+struct ProjArgs {
+    int proj;  // 0: only the side job
     const uint16_t* P;
     int64_t ldp;
     const uint16_t* Q;
     int64_t ldq;
-    int qrows;
+    int rq;
     int64_t T;
-    int64_t kred;
+    int64_t kred;  // multiple of 8
     float alpha_f;
     float* out_f;
     int64_t ld_f;
-    int ncols_f;
     float alpha_b;
     uint16_t* out_b;
-    int64_t ld_b;
-    uint16_t* out_bt;  // optional: out_bt[j * ld_bt + t] = bf16(alpha_b * sum), j < rows_bt
+    int ld_b;
+    uint16_t* out_bt;
     int rows_bt;
     int64_t ld_bt;
+    const float* Usrc;
+    int ru;
+    uint16_t* Ut;
+    int rows_ut;
+    int64_t ld_ut;
 };
-// part: fp32 workspace of skinny_workspace_bytes(T, kred, qrows) bytes
-size_t skinny_workspace_bytes(int64_t T, int64_t kred, int qrows);
-int launch_skinny(const SkinnyArgs& a, float* part, hipStream_t stream);
+int launch_lora_proj(const ProjArgs& a, bool q_cols, hipStream_t stream);
 
 // dst[i][j] = src[i][j] for j < cols, 0 for cols <= j < ldd.
 int launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ldd, hipStream_t stream);
-// dst[c][r] = src[r][c] for r < R, 0 for R <= r < ldd.
-int launch_transpose_pad(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, int64_t ldd, hipStream_t stream);
 
 // Y[t][n] = sum_k X[t][k] W'[n][k] + scale sum_j U[t][j] B[n][j] for T <= 16.
-int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const float* U,
-                const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream);
+int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const uint16_t* A,
+                const uint16_t* B, int r, float scale, uint16_t* Y, float* U_out, hipStream_t stream);
 
 // Tile / split-K plan of the dequant GEMMs for an MA x T output with a
 // reduction of RED, and the fp32 workspace its split partials need.
@@ -78,16 +83,34 @@ int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, cons
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
                    uint16_t* dX, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream);
 
-int lora_grad_rp(int r);  // rank rounded up to 16
+int lora_grad_rp(int r);         // rank rounded up to 16
 int64_t lora_vt_ld(int64_t T);  // row stride of the transposed [rp16, T] operands
-int lora_grad_splits(int64_t T, int64_t cols);
-// part[ts][j][c] = sum_{t in split ts} Vt[j][t] * M[t][c] (Vt bf16 [rp16, T])
-int launch_lora_grad_partial(const uint16_t* M, int64_t ldm, int64_t cols, const uint16_t* Vt, int rp16, int64_t T,
-                             int splits, float* part, hipStream_t stream);
-// Vt[j][t] = bf16(U[t][j]), zero rows from r to rows
-int launch_transpose_f32_bf16(const float* U, int64_t T, int r, int rows, uint16_t* Vt, hipStream_t stream);
-// out[j][c] (layout_jc) or out[c][j] = (acc ? out : 0) + scale * sum_ts part[ts][j][c]
-int launch_lora_grad_final(const float* part, int splits, int rp, int r, int64_t cols, float scale, bool layout_jc,
-                           float* out, int accumulate, hipStream_t stream);
+
+// Adapter gradients: out = (accumulate ? out : 0) + scale * Vt M, written as
+// out[j][c] (layout_jc) or out[c][j], j < r, c < C; M bf16 [T, C] (row
+// stride ldm), Vt bf16 [rp16, ldv]. A problem with out == NULL is skipped.
+struct GradProblem {
+    const uint16_t* M;
+    int64_t ldm;
+    int64_t C;
+    const uint16_t* Vt;
+    int64_t ldv;
+    float* out;
+    int layout_jc;
+    float scale;
+    float* part;  // set by the launcher
+};
+struct GradArgs {
+    GradProblem pb[2];
+    int nblk0;  // set by the launcher
+    int r;
+    int64_t T;
+    int64_t t_per;  // set by the launcher
+    int accumulate;
+};
+// fp32 workspace for token-split partials (0 when one split suffices);
+// C0, C1: columns of the problems that will run (0 for a skipped one)
+size_t lora_grads_part_bytes(int64_t T, int64_t C0, int64_t C1, int r);
+int launch_lora_grads(GradArgs a, float* part, hipStream_t stream);
 
 }  // namespace qlnf4

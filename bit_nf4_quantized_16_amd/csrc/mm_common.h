@@ -100,10 +100,12 @@ __device__ __forceinline__ uint32_t lut_bytes(const uint32_t (&t)[4], uint32_t s
 __device__ __forceinline__ uint4 dequant8_lut(uint32_t w, const Lut16& L) {
     const uint32_t se = (w >> 4) & 0x07070707u;  // even elements, low 3 bits of the code
     const uint32_t so = w & 0x07070707u;         // odd elements
-    const uint32_t be = w & 0x80808080u;         // bit 3 of the even codes, at bit 7 of each byte
-    const uint32_t bo = (w << 4) & 0x80808080u;  // bit 3 of the odd codes
-    const uint32_t me = (be << 1) - (be >> 7);   // 0xFF per byte where set
-    const uint32_t mo = (bo << 1) - (bo >> 7);
+    // 0xFF per byte where bit 3 of the code is set. Bit 3 of the even code is
+    // bit 7 of its byte (bit 7 of the odd one after << 4); v_perm selectors
+    // 8..11 replicate bit 7 of bytes 1, 3 (second source) and 5, 7 (first
+    // source), so the first source is the word shifted up one byte.
+    const uint32_t me = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+    const uint32_t mo = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);
     const uint32_t le = lut_bytes(L.lo, se, me), he = lut_bytes(L.hi, se, me);
     const uint32_t lo = lut_bytes(L.lo, so, mo), ho = lut_bytes(L.hi, so, mo);
     const uint32_t xa = __builtin_amdgcn_perm(he, le, 0x05010400u);  // e0 | e2 << 16

@@ -173,7 +173,8 @@ int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* strea
  *          when that size is 0)
  *
  * r == 0 (A and B may then be NULL) runs the base matmul alone. T <= 16 takes
- * the dequant-GEMV kernels, larger T the dequant-in-LDS MFMA GEMM.
+ * the single dequant-GEMV kernel (LoRA branch included, workspace size 0),
+ * larger T the dequant-in-LDS MFMA GEMM.
  * K must be a multiple of 64. Y must not alias any input.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE (T < 0, K % 64 != 0, r < 0 or
  * r > QL_MAX_RANK), QL_ERR_UNSUPPORTED, QL_ERR_ALIGN, QL_ERR_WORKSPACE,

@@ -69,6 +69,26 @@ def test_ragged_shapes_and_ranks(qn, N, K, T, r):
     _run(qn, case)
 
 
+# decode path: every rank-tile variant of the fused GEMV (1, 2, 3->4, 7->8 and
+# 8 tiles of 16), a half last K step (K % 128 == 64), N below one 16-row tile,
+# several passes over K (K = 4160: 33 steps of 128) and the base alone
+@pytest.mark.parametrize("N,K,T,r", [(200, 320, 3, 5), (136, 64, 1, 24), (264, 192, 16, 40), (520, 1088, 7, 100),
+                                     (8, 128, 2, 128), (96, 4160, 16, 16), (48, 4160, 5, 64), (72, 256, 1, 0)])
+def test_gemv_ranks_and_ragged_k(qn, N, K, T, r):
+    W = workloads.normal_weight(N, K, 0.02, seed=N + 3 * K)
+    case = workloads.lora_case("gemv_N%dK%dT%dr%d" % (N, K, T, r), W, T, r, 2.0 * max(r, 1), 1 / K, 0.05,
+                               seed=N * 5 + T)
+    if r == 0:
+        w = qn.quantize_weight(W.cuda())
+        Y, U = qn.qlora_linear_fwd(w, case.X.cuda())
+        assert U is None
+        ref = oracle_weight(W.numpy())
+        H = bf16_to_np(case.X).astype(np.float64) @ ref["wd"].T
+        assert normwise_rel_err(bf16_to_np(Y), H) <= TOL
+    else:
+        _run(qn, case)
+
+
 def test_without_double_quant(qn):
     case = workloads.tiny_256()
     _run(qn, case, dq=False)
