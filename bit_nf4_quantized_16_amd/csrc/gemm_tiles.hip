@@ -69,6 +69,27 @@ __device__ __forceinline__ v4i16 ld_tr16(const uint16_t* p) {
 // 64-bank LDS) get different chunk positions.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
+// Padding (bf16 elements) of the dX weight-tile rows, which are read
+// column-wise with transposing LDS loads: with 32, the four rows a 16-lane
+// group reads fall in different banks of the 64-bank LDS.
+#ifndef QL_GEMM_DX_PAD
+#define QL_GEMM_DX_PAD 32
+#endif
+
+// End of a pipeline stage: this wave's LDS writes are complete and its
+// direct-to-LDS token loads have landed, then the workgroup barrier. The
+// token loads of the stage were issued before at least N other vector loads
+// (the codes prefetched for a later stage), which stay in flight: vmcnt(N)
+// with lgkmcnt(0). A __syncthreads (or any LDS fence, which cannot tell the
+// direct-to-LDS loads from the code loads) would drain them all. The memory
+// clobber keeps the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("s_barrier" ::: "memory");
+}
+
 template <int TA, int TT, int WA, int WT, bool DX>
 struct TileShape {
     static constexpr int NW = WA * WT, NTHR = 64 * NW;      // waves, threads
@@ -78,7 +99,7 @@ struct TileShape {
     static constexpr int CPT = TA * kStep / NTHR;            // codes per thread per step
     static constexpr int CC = CPT / 32;                      // 16-B code chunks per thread
     static constexpr int ROWS_A = DX ? kStep : TA;           // weight-tile rows (reduction rows for dX)
-    static constexpr int LDA = DX ? TA + 8 : kStep + 8;      // weight-tile LDS row (bf16, padded)
+    static constexpr int LDA = DX ? TA + QL_GEMM_DX_PAD : kStep + 8;  // weight-tile LDS row (bf16, padded)
     static constexpr int TPR = DX ? TA / CPT : kStep / CPT;  // threads per weight-tile row
     static_assert(CPT == 32 || CPT == 64, "a thread expands one block or half of one");
     static_assert(DMA >= 1 && TT % (8 * NW) == 0, "token tile split");
@@ -156,8 +177,8 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
             const int64_t n = min(m0 + wrow, p.N - 1);
             e = n * p.K + r0 + wcol;
         }
-#pragma unroll
-        for (int cc = 0; cc < CC; ++cc) cs.c[cc] = ld16(p.w.packed + e / 2 + 16 * cc);
+        // block constant first, the CC code chunks last (the stage barrier
+        // lets the last CC loads of a stage stay in flight)
         const int64_t b = e / 64;
         if constexpr (DQ) {
             cs.bc.c8 = p.w.c8[b];
@@ -166,6 +187,8 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
             cs.bc.c8 = 0;
             cs.bc.s = p.w.absmax[b];
         }
+#pragma unroll
+        for (int cc = 0; cc < CC; ++cc) cs.c[cc] = ld16(p.w.packed + e / 2 + 16 * cc);
     };
 
     // ---- expand one step's codes into a weight stage -----------------------
@@ -237,6 +260,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     __syncthreads();
     for (int s = sb; s < msteps; s += 2) {
         dma(min(s + 1, msteps - 1), sX1);
+        __builtin_amdgcn_sched_barrier(0);  // the token loads stay ahead of the code loads
         gcodes(min(s + 2, msteps - 1), cs0);
         if (expand_first) {
             expand(s + 1, cs1, sA1);
@@ -245,9 +269,10 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
             compute(sA0, sX0);
             expand(s + 1, cs1, sA1);
         }
-        __syncthreads();
+        stage_barrier<CC>();
         if (s + 1 >= msteps) break;
         dma(min(s + 2, msteps - 1), sX0);
+        __builtin_amdgcn_sched_barrier(0);
         gcodes(min(s + 3, msteps - 1), cs1);
         if (expand_first) {
             expand(s + 2, cs0, sA0);
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
             compute(sA1, sX1);
             expand(s + 2, cs0, sA0);
         }
-        __syncthreads();
+        stage_barrier<CC>();
     }
     }  // sb < se
 

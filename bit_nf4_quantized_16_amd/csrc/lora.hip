@@ -29,10 +29,11 @@ typedef short v8i16_l __attribute__((ext_vector_type(8)));
 // ds_read_b64_tr_b16, each returning four rows of the lane's column.
 __device__ __forceinline__ bf16x8_t lds_col8(const uint16_t* tile, int ld, int r0, int c0, int li) {
     const uint16_t* base = tile + (r0 + (li >> 2)) * ld + c0 + 4 * (li & 3);
-    const v4i16_l lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16_l*)(reinterpret_cast<uintptr_t>(base)));
-    const v4i16_l hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16_l*)(reinterpret_cast<uintptr_t>(base + 4 * ld)));
+    // address-space casts (not integer casts) keep the pointer's provenance,
+    // so the compiler can tell these reads from direct-to-LDS loads elsewhere
+    const v4i16_l lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_l*)(base));
+    const v4i16_l hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_l*)(base + 4 * ld));
     const v8i16_l v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -183,6 +184,205 @@ __global__ __launch_bounds__(512) void lora_proj_kernel(ProjArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same projection with the operands staged in LDS by direct-to-LDS loads
+// (global_load_lds_dwordx4): every load instruction then covers whole
+// 128-byte lines (8 rows x 128 bytes of P or of A, or 1 KiB of consecutive
+// rows of B), where register loads in MFMA operand order touch 32 half lines
+// each. A wave runs its 64-wide reduction steps w, w + NW, ... through a ring
+// of three LDS slots: while it multiplies one step, the next two are in
+// flight. P and A tiles keep 16-byte chunk c of row r at c ^ swz(r), so the
+// 16 lanes reading one chunk column hit every bank twice at most; B tiles are
+// read column-wise with transposing LDS loads.
+// Used for every A-like Q, and for B-like Q when rq % 4 == 0.
+// ---------------------------------------------------------------------------
+#define QL_LDS_AS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+
+// s_waitcnt vmcnt(N), leaving the LDS and export counters alone. LDS writes
+// of direct-to-LDS loads are complete once the issuing wave's vmcnt has
+// dropped past them; the compiler does not insert this wait by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int RT>
+struct ProjDma {
+    static constexpr int NW = RT <= 2 ? 8 : (RT == 4 ? 4 : 2);  // waves: three slots per wave fit in LDS
+    static constexpr int PS = 16 * 64;                           // P slot: 16 tokens x 64 k
+    static constexpr int QS = 16 * RT * 64;                      // Q slot: 16 RT rows x 64 k, or 64 rows of B
+};
+
+template <int RT, bool QCOLS>
+__global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(ProjArgs p) {
+    using D = ProjDma<RT>;
+    constexpr int NW = D::NW;
+    __shared__ __attribute__((aligned(16))) uint16_t sP0[NW][D::PS];
+    __shared__ __attribute__((aligned(16))) uint16_t sP1[NW][D::PS];
+    __shared__ __attribute__((aligned(16))) uint16_t sP2[NW][D::PS];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ0[NW][D::QS];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ1[NW][D::QS];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ2[NW][D::QS];
+    __shared__ float red[NW][16][16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, g = lane >> 4;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+
+    if (p.proj) {
+        const int64_t nst = ceil_div(p.kred, 64);
+        const int64_t my = nst > wave ? ceil_div(nst - wave, NW) : 0;  // this wave's steps
+        const int64_t qlast = p.kred * p.rq - 8;
+
+        auto issue = [&](int64_t s, uint16_t* sp, uint16_t* sq) {
+            const int64_t k0 = (wave + NW * s) * 64;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = 8 * i + (lane >> 3);
+                const int c = (lane & 7) ^ swz8(row);
+                const int64_t t = std::min<int64_t>(t0 + row, p.T - 1);
+                const int64_t col = std::min<int64_t>(k0 + 8 * c, p.kred - 8);
+                __builtin_amdgcn_global_load_lds(p.P + t * p.ldp + col, (QL_LDS_AS void*)(sp + 512 * i), 16, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 2 * RT; ++i) {
+                if constexpr (!QCOLS) {
+                    const int row = 8 * i + (lane >> 3);
+                    const int c = (lane & 7) ^ swz8(row);
+                    const int64_t j = std::min(row, p.rq - 1);
+                    const int64_t col = std::min<int64_t>(k0 + 8 * c, p.kred - 8);
+                    __builtin_amdgcn_global_load_lds(p.Q + j * p.ldq + col, (QL_LDS_AS void*)(sq + 512 * i), 16, 0,
+                                                     0);
+                } else {  // rows k0 .. k0+63 of B are one run of 64 rq values
+                    const int64_t e = std::min<int64_t>(k0 * p.rq + 512 * i + 8 * lane, qlast);
+                    __builtin_amdgcn_global_load_lds(p.Q + e, (QL_LDS_AS void*)(sq + 512 * i), 16, 0, 0);
+                }
+            }
+        };
+
+        f32x4 acc[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](int64_t s, const uint16_t* sp, const uint16_t* sq) {
+            const int64_t k0 = (wave + NW * s) * 64;
+            const bool partial = k0 + 64 > p.kred;  // wave-uniform
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 4 * h + g;
+                uint4 pv = *reinterpret_cast<const uint4*>(sp + li * 64 + 8 * (c ^ swz8(li)));
+                if (partial && k0 + 8 * c >= p.kred) pv = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    bf16x8_t qo;
+                    if constexpr (!QCOLS) {
+                        const int row = 16 * t + li;
+                        qo = as_bf16x8(*reinterpret_cast<const uint4*>(sq + row * 64 + 8 * (c ^ swz8(row))));
+                    } else {
+                        qo = lds_col8(sq, p.rq, 32 * h + 8 * g, 16 * t, li);
+                    }
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qo, as_bf16x8(pv), acc[t], 0, 0, 0);
+                }
+            }
+        };
+
+        // wait for the loads of step s; those of the (at most two) later steps
+        // already issued may stay in flight
+        constexpr int DPS = 2 + 2 * RT;  // load instructions per step
+        auto wait_step = [&](int64_t s) {
+            if (s + 2 < my)
+                wait_vmcnt<2 * DPS>();
+            else if (s + 1 < my)
+                wait_vmcnt<DPS>();
+            else
+                wait_vmcnt<0>();
+        };
+        if (0 < my) issue(0, sP0[wave], sQ0[wave]);
+        if (1 < my) issue(1, sP1[wave], sQ1[wave]);
+        if (2 < my) issue(2, sP2[wave], sQ2[wave]);
+        for (int64_t s = 0; s < my; s += 3) {
+            wait_step(s);
+            compute(s, sP0[wave], sQ0[wave]);
+            if (s + 3 < my) {
+                wave_lds_sync();  // slot 0 has been read
+                issue(s + 3, sP0[wave], sQ0[wave]);
+            }
+            if (s + 1 < my) {
+                wait_step(s + 1);
+                compute(s + 1, sP1[wave], sQ1[wave]);
+                if (s + 4 < my) {
+                    wave_lds_sync();
+                    issue(s + 4, sP1[wave], sQ1[wave]);
+                }
+            }
+            if (s + 2 < my) {
+                wait_step(s + 2);
+                compute(s + 2, sP2[wave], sQ2[wave]);
+                if (s + 5 < my) {
+                    wave_lds_sync();
+                    issue(s + 5, sP2[wave], sQ2[wave]);
+                }
+            }
+        }
+
+        // D[j = 4 g + rr][token li] of each rank tile; fixed-order sum of the waves
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (rt > 0) __syncthreads();
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) red[wave][4 * g + rr][li] = acc[rt][rr];
+            __syncthreads();
+            for (int e = tid; e < 256; e += 64 * NW) {
+                const int jl = e >> 4, tl = e & 15;
+                const int64_t t = t0 + tl;
+                if (t >= p.T) continue;
+                float v = 0.0f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) v += red[ww][jl][tl];
+                const int j = 16 * rt + jl;
+                if (p.out_f != nullptr && j < p.rq) p.out_f[t * p.ld_f + j] = p.alpha_f * v;
+                const uint16_t hb = to_bf16_bits(j < p.rq ? p.alpha_b * v : 0.0f);
+                if (p.out_b != nullptr && j < p.ld_b) p.out_b[t * p.ld_b + j] = hb;
+                if (p.out_bt != nullptr && j < p.rows_bt) p.out_bt[j * p.ld_bt + t] = hb;
+            }
+        }
+        if (p.out_b != nullptr) {  // zero columns past the rank tiles
+            for (int e = tid; e < 16 * (p.ld_b - 16 * RT); e += 64 * NW) {
+                const int64_t tt = t0 + (e & 15);
+                if (tt < p.T) p.out_b[tt * p.ld_b + 16 * RT + (e >> 4)] = 0;
+            }
+        }
+    }
+    if (p.Ut != nullptr) {
+        for (int e = tid; e < 16 * p.rows_ut; e += 64 * NW) {
+            const int j = e >> 4;
+            const int64_t tt = t0 + (e & 15);
+            if (tt < p.T) p.Ut[j * p.ld_ut + tt] = to_bf16_bits(j < p.ru ? p.Usrc[tt * p.ru + j] : 0.0f);
+        }
+    }
+}
+
+template <bool QCOLS>
+static void launch_proj_dma_rt(int rt, const ProjArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(ceil_div(a.T, 16)));
+    switch (rt) {
+        case 1:
+            hipLaunchKernelGGL((lora_proj_dma_kernel<1, QCOLS>), grid, dim3(64 * ProjDma<1>::NW), 0, stream, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((lora_proj_dma_kernel<2, QCOLS>), grid, dim3(64 * ProjDma<2>::NW), 0, stream, a);
+            break;
+        case 4:
+            hipLaunchKernelGGL((lora_proj_dma_kernel<4, QCOLS>), grid, dim3(64 * ProjDma<4>::NW), 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((lora_proj_dma_kernel<8, QCOLS>), grid, dim3(64 * ProjDma<8>::NW), 0, stream, a);
+            break;
+    }
+}
+
 template <bool QCOLS>
 static void launch_proj_rt(int rt, const ProjArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>(ceil_div(a.T, 16))), block(64 * kProjWaves);
@@ -201,10 +401,12 @@ int launch_lora_proj(const ProjArgs& a, bool q_cols, hipStream_t stream) {
     const int rt = tiles <= 2 ? tiles : (tiles <= 4 ? 4 : 8);
     if (a.out_b != nullptr && a.ld_b < a.rq)
         return set_error(QL_ERR_SHAPE, "LoRA projection: bf16 output narrower than the rank");
-    if (q_cols)
-        launch_proj_rt<true>(rt, a, stream);
+    if (!q_cols)
+        launch_proj_dma_rt<false>(rt, a, stream);
+    else if (a.rq % 4 == 0)
+        launch_proj_dma_rt<true>(rt, a, stream);
     else
-        launch_proj_rt<false>(rt, a, stream);
+        launch_proj_rt<true>(rt, a, stream);
     return check_launch("LoRA projection");
 }
 
