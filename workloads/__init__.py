@@ -113,3 +113,28 @@ LLAMA7B_LAYER = [
 ]
 
 LLAMA65B_SHAPES = [("sq", 8192, 8192), ("up", 22016, 8192), ("down", 8192, 22016)]
+
+
+def llama7b_layer_linear(which, T=4096, seed=3):
+    """One linear of the 32-layer 7B-shaped stack at T = 4096 tokens, LoRA
+    r = 64, alpha = 16 on all linears. The stack's weight distribution is not
+    stated: attention shapes take the 4096x4096 recipe (N(0, 0.02), 0.1 %
+    outliers x20), MLP shapes the 0.02 Student-t(5) recipe."""
+    shapes = {name: (n, k, i) for i, (name, n, k) in enumerate(LLAMA7B_LAYER)}
+    n, k, off = shapes[which]
+    s = seed * 10 + off
+    if which in ("gate", "up", "down"):
+        W = student_t_weight(n, k, 5, 0.02, s)
+    else:
+        W = normal_weight(n, k, 0.02, s, outlier_frac=1e-3, outlier_scale=20.0)
+    return lora_case("llama7b_%s_%dx%d" % (which, n, k), W, T, 64, 16.0, 1.0 / k, 0.01, s)
+
+
+def llama65b_linear(which, T=4096, seed=4):
+    """65B-shaped linears 8192x8192, 22016x8192, 8192x22016: W ~ N(0, 0.015);
+    x bf16 [4096, K]; LoRA r = 64, alpha = 16."""
+    shapes = {name: (n, k, i) for i, (name, n, k) in enumerate(LLAMA65B_SHAPES)}
+    n, k, off = shapes[which]
+    s = seed * 10 + off
+    W = normal_weight(n, k, 0.015, s)
+    return lora_case("llama65b_%s_%dx%d" % (which, n, k), W, T, 64, 16.0, 1.0 / k, 0.01, s)
