@@ -177,6 +177,28 @@ __device__ __forceinline__ float max8(float v) {
     return v;
 }
 
+// The same maxima on non-negative floats by their bit patterns (integer max
+// orders non-negative floats like float max and needs no NaN canonicalising,
+// so each step is one v_max_u32 with a DPP source).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t umax_(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umax16(uint32_t v) {
+    v = umax_(v, dpp_u<0x128>(v));
+    v = umax_(v, dpp_u<0x124>(v));
+    v = umax_(v, dpp_u<0x4E>(v));
+    v = umax_(v, dpp_u<0xB1>(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t umax8(uint32_t v) {
+    v = umax_(v, dpp_u<0x141>(v));
+    v = umax_(v, dpp_u<0x4E>(v));
+    v = umax_(v, dpp_u<0xB1>(v));
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
     return v;

@@ -415,7 +415,7 @@ int launch_lora_proj(const ProjArgs& a, bool q_cols, hipStream_t stream) {
 //   out[j][c] (dA) or out[c][j] (dB) = scale * sum_t Vt[j][t] M[t][c]
 // with M = X, Vt = G^T for dA and M = dY, Vt = U^T, scale = s for dB. One
 // grid holds both problems: workgroups [0, nblk0) take 64-column blocks of
-// the first, the rest those of the second. A workgroup's four waves take
+// the first, the rest those of the second. A workgroup's eight waves take
 // 32-token chunks in turn; each wave stages its chunk of M in a private LDS
 // tile and reads it back column-wise with transposing LDS loads (8
 // consecutive tokens of one column per lane, the MFMA B operand); the A
@@ -428,6 +428,7 @@ int64_t lora_vt_ld(int64_t T) { return ceil_div(T, 8) * 8; }
 
 constexpr int kGradCols = 64;  // columns of M per workgroup
 constexpr int kGradRows = 32;  // token rows per MFMA step
+constexpr int kGradWaves = 8;  // waves per workgroup, taking chunks in turn
 constexpr int kGradLd = kGradCols + 8;
 
 int lora_grad_splits(int64_t T, int64_t cols_total) {
@@ -435,16 +436,16 @@ int lora_grad_splits(int64_t T, int64_t cols_total) {
     if (T <= 2048) return 1;
     const int64_t col_blocks = ceil_div(cols_total, kGradCols);
     int64_t s = ceil_div(512, col_blocks);
-    const int64_t max_s = ceil_div(T, 4 * kGradRows);
+    const int64_t max_s = ceil_div(T, kGradWaves * kGradRows);
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
     return static_cast<int>(s);
 }
 
 template <int RT>
-__global__ __launch_bounds__(256) void lora_grads_kernel(GradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sm[4][kGradRows * kGradLd];
-    __shared__ float red[4][16][kGradCols];
+__global__ __launch_bounds__(64 * kGradWaves) void lora_grads_kernel(GradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sm[kGradWaves][kGradRows * kGradLd];
+    __shared__ float red[kGradWaves][16][kGradCols];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const bool second = static_cast<int>(blockIdx.x) >= a.nblk0;
@@ -474,9 +475,9 @@ __global__ __launch_bounds__(256) void lora_grads_kernel(GradArgs a) {
     uint4 cur[4];
     int64_t t = tb + kGradRows * wave;
     if (t < te) load_chunk(t, cur);
-    for (; t < te; t += 4 * kGradRows) {
+    for (; t < te; t += kGradWaves * kGradRows) {
         uint4 nxt[4];
-        const int64_t tn = t + 4 * kGradRows;
+        const int64_t tn = t + kGradWaves * kGradRows;
         if (tn < te) load_chunk(tn, nxt);
         wave_lds_sync();  // the previous chunk's reads are done
 #pragma unroll
@@ -513,12 +514,14 @@ __global__ __launch_bounds__(256) void lora_grads_kernel(GradArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) red[wave][4 * g + r][16 * cb + li] = acc[rt][cb][r];
         __syncthreads();
-        for (int e = tid; e < 16 * kGradCols; e += 256) {
+        for (int e = tid; e < 16 * kGradCols; e += 64 * kGradWaves) {
             const int jl = e / kGradCols, cl = e % kGradCols;
             const int j = 16 * rt + jl;
             const int64_t c = c0 + cl;
             if (c >= C) continue;
-            const float v = ((red[0][jl][cl] + red[1][jl][cl]) + red[2][jl][cl]) + red[3][jl][cl];
+            float v = red[0][jl][cl];
+#pragma unroll
+            for (int ww = 1; ww < kGradWaves; ++ww) v += red[ww][jl][cl];
             if (direct) {
                 if (j < a.r) {
                     const int64_t idx = pb.layout_jc ? j * C + c : c * a.r + j;
@@ -574,7 +577,7 @@ int launch_lora_grads(GradArgs a, float* part, hipStream_t stream) {
     const int64_t c0 = a.pb[0].out ? a.pb[0].C : 0, c1 = a.pb[1].out ? a.pb[1].C : 0;
     if (c1 == 0) a.pb[1].C = 0;
     const int splits = lora_grad_splits(a.T, c0 + c1);
-    a.t_per = ceil_div(ceil_div(a.T, splits), 4 * kGradRows) * 4 * kGradRows;
+    a.t_per = ceil_div(ceil_div(a.T, splits), kGradWaves * kGradRows) * kGradWaves * kGradRows;
     a.nblk0 = static_cast<int>(ceil_div(c0, kGradCols));
     if (splits > 1) {
         if (part == nullptr) return set_error(QL_ERR_WORKSPACE, "LoRA gradient: workspace missing");
@@ -586,7 +589,7 @@ int launch_lora_grads(GradArgs a, float* part, hipStream_t stream) {
     switch (rp16 / 16) {
 #define QL_GRAD_CASE(R_)                                                                   \
     case R_:                                                                               \
-        hipLaunchKernelGGL(lora_grads_kernel<R_>, grid, dim3(256), 0, stream, a);          \
+        hipLaunchKernelGGL(lora_grads_kernel<R_>, grid, dim3(64 * kGradWaves), 0, stream, a); \
         break;
         QL_GRAD_CASE(1)
         QL_GRAD_CASE(2)

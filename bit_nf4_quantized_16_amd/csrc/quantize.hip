@@ -23,10 +23,13 @@ __constant__ LutEntry c_lut[kLutBuckets] = {
 };
 
 // Code of a normalised value x (|x| <= 1 up to rounding) from the bucket
-// lookup held in LDS.
+// lookup held in LDS. b = floor(16 x + 16) is taken as one fused
+// multiply-add (16 x is exact, so it rounds like 16 x + 16) and
+// v_cvt_u32_f32, which clamps negative values (the x = -1 - ulp case) and
+// NaN to 0; x never exceeds 1 + 2^-23, so b <= 32.
 __device__ __forceinline__ uint32_t nf4_code(float x, const LutEntry* lut) {
-    int b = static_cast<int>(x * 16.0f + 16.0f);
-    b = b < 0 ? 0 : (b > kLutBuckets - 1 ? kLutBuckets - 1 : b);
+    uint32_t b;
+    asm("v_cvt_u32_f32 %0, %1" : "=v"(b) : "v"(__builtin_fmaf(x, 16.0f, 16.0f)));
     LutEntry e = lut[b];
     return e.base + (x > e.thr ? 1u : 0u);
 }
@@ -35,9 +38,15 @@ __device__ __forceinline__ uint32_t nf4_code(float x, const LutEntry* lut) {
 // Main quantize kernel. The input is cut into 1 KiB segments; within a
 // segment lane l holds the 16 bytes at offset 16 l (4 fp32 or 8 bf16 values),
 // so each load instruction of a wave is one contiguous 1 KiB. A 64-element
-// block is then 16 lanes (fp32) or 8 lanes (bf16), reduced with DPP.
-// Each wave takes kSegsPerWave consecutive segments and issues all their
-// loads before any compute.
+// block is then 16 lanes (fp32) or 8 lanes (bf16), reduced with DPP on the
+// bit patterns. Each wave takes kSegsPerWave = 4 consecutive segments and
+// issues all their loads before any compute.
+// The correctly rounded reciprocal fl32(1 / absmax) costs a dozen VALU
+// instructions; instead of one per segment, lane l computes it for segment
+// l % 4 of its own block row and the quad broadcasts it (DPP quad_perm), so
+// a wave does one division for its four segments. The same selection gives
+// each of the first four lanes of a block row one segment's absmax to store,
+// so the wave writes its 16 (or 32) constants in one instruction.
 // ---------------------------------------------------------------------------
 constexpr int kQuantThreads = 256;
 constexpr int kSegsPerWave = 4;
@@ -49,7 +58,9 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t
                                                                    float* __restrict__ absmax) {
     constexpr int kPerLane = BF16 ? 8 : 4;           // elements per lane per segment
     constexpr int kLanesPerBlock = 64 / kPerLane;    // 8 or 16
+    constexpr int kBlocksPerSeg = 64 / kLanesPerBlock;  // 8 or 4
     constexpr int kSegElems = 64 * kPerLane;         // 512 or 256
+    static_assert(kSegsPerWave == 4, "one quad of lanes per block row serves four segments");
 
     __shared__ LutEntry lut[kLutBuckets];
     if (threadIdx.x < kLutBuckets) lut[threadIdx.x] = c_lut[threadIdx.x];
@@ -59,53 +70,78 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t
     const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6);
     const int64_t seg0 = wave * kSegsPerWave;
     if (seg0 >= nseg) return;
+    const int nsegs = static_cast<int>(nseg - seg0 < kSegsPerWave ? nseg - seg0 : kSegsPerWave);  // wave-uniform
 
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 v[kSegsPerWave];
+    const u32x4* src = reinterpret_cast<const u32x4*>(W + seg0 * kSegBytes) + lane;
+    if (nsegs == kSegsPerWave) {
 #pragma unroll
-    for (int s = 0; s < kSegsPerWave; ++s) {
-        if (seg0 + s < nseg)
-            v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (seg0 + s) * kSegBytes) + lane);
+        for (int s = 0; s < kSegsPerWave; ++s) v[s] = __builtin_nontemporal_load(src + s * (kSegBytes / 16));
+    } else {
+        // a short last wave re-reads its last segment (in bounds, results dropped)
+#pragma unroll
+        for (int s = 0; s < kSegsPerWave; ++s)
+            v[s] = __builtin_nontemporal_load(src + (s < nsegs ? s : nsegs - 1) * (kSegBytes / 16));
     }
 
+    float e[kSegsPerWave][kPerLane];
+    uint32_t mb[kSegsPerWave];  // block absmax, as bits
 #pragma unroll
     for (int s = 0; s < kSegsPerWave; ++s) {
-        if (seg0 + s >= nseg) break;
-        float e[kPerLane];
         if (BF16) {
             const uint32_t w4[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                e[2 * i] = __uint_as_float(w4[i] << 16);
-                e[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+                e[s][2 * i] = __uint_as_float(w4[i] << 16);
+                e[s][2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
             }
         } else {
-            e[0] = __uint_as_float(v[s].x);
-            e[1] = __uint_as_float(v[s].y);
-            e[2] = __uint_as_float(v[s].z);
-            e[3] = __uint_as_float(v[s].w);
+            e[s][0] = __uint_as_float(v[s].x);
+            e[s][1] = __uint_as_float(v[s].y);
+            e[s][2] = __uint_as_float(v[s].z);
+            e[s][3] = __uint_as_float(v[s].w);
         }
         float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) m = fmaxf(m, fabsf(e[i]));
-        m = BF16 ? max8(m) : max16(m);
-        const float inv = m > 0.0f ? 1.0f / m : 0.0f;
+        for (int i = 0; i < kPerLane; ++i) m = fmaxf(m, fabsf(e[s][i]));
+        mb[s] = BF16 ? umax8(__float_as_uint(m)) : umax16(__float_as_uint(m));
+    }
+
+    // one reciprocal per lane: segment lane % 4 of this lane's block row
+    const int sel = lane & 3;
+    const uint32_t mine = sel == 0 ? mb[0] : (sel == 1 ? mb[1] : (sel == 2 ? mb[2] : mb[3]));
+    const float mf = __uint_as_float(mine);
+    const float minv = mf > 0.0f ? 1.0f / mf : 0.0f;
+    float inv[kSegsPerWave];
+    inv[0] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(minv), 0x00, 0xF, 0xF, false));  // quad lane 0
+    inv[1] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(minv), 0x55, 0xF, 0xF, false));  // quad lane 1
+    inv[2] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(minv), 0xAA, 0xF, 0xF, false));  // quad lane 2
+    inv[3] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(minv), 0xFF, 0xF, 0xF, false));  // quad lane 3
+
+    uint8_t* pk = packed + (seg0 * kSegElems + static_cast<int64_t>(lane) * kPerLane) / 2;
+#pragma unroll
+    for (int s = 0; s < kSegsPerWave; ++s) {
+        if (s >= nsegs) break;
         uint32_t word = 0;
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
-            uint32_t c = nf4_code(e[i] * inv, lut);
+            const uint32_t c = nf4_code(e[s][i] * inv[s], lut);
             // element 2j goes to the high nibble of byte j
             const int byte = i >> 1;
             const int shift = byte * 8 + ((i & 1) ? 0 : 4);
             word |= c << shift;
         }
-        const int64_t elem0 = (seg0 + s) * kSegElems + static_cast<int64_t>(lane) * kPerLane;
         if (BF16)
-            *reinterpret_cast<uint32_t*>(packed + elem0 / 2) = word;
+            *reinterpret_cast<uint32_t*>(pk + s * (kSegElems / 2)) = word;
         else
-            *reinterpret_cast<uint16_t*>(packed + elem0 / 2) = static_cast<uint16_t>(word);
-        if ((lane % kLanesPerBlock) == 0) absmax[elem0 / 64] = m;
+            *reinterpret_cast<uint16_t*>(pk + s * (kSegElems / 2)) = static_cast<uint16_t>(word);
     }
+    // absmax of block (segment sel, row lane / kLanesPerBlock), by the first
+    // four lanes of each block row
+    const int row = lane / kLanesPerBlock;
+    if ((lane % kLanesPerBlock) < 4 && sel < nsegs)
+        absmax[seg0 * kBlocksPerSeg + sel * kBlocksPerSeg + row] = mf;
 }
 
 // Tail: the elements after the last whole segment (fewer than 512), one
@@ -169,17 +205,14 @@ constexpr int kTreeThreads = 256;
 constexpr int kTreePerThread = 16;
 constexpr int kTreeChunk = kTreeThreads * kTreePerThread;  // 4096
 
-// One level of the contiguous pairwise fp64 tree: workgroup g sums the
-// aligned chunk [4096 g, 4096 g + 4096) (zero beyond n) in tree order: pairs
-// inside each thread's 16 values, then xor-butterfly across lanes (lane t
-// and t^d hold the same sum, so the butterfly is the tree), then the four
-// wave sums as (w0 + w1) + (w2 + w3). With a single workgroup the root is
-// the tree sum of everything and the mean is written.
+// Sum of the aligned chunk [4096 c, 4096 c + 4096) of `in` (zero beyond n)
+// in the order of the contiguous pairwise fp64 tree: pairs inside each
+// thread's 16 values, then xor-butterfly across lanes (lane t and t^d hold
+// the same sum, so the butterfly is the tree), then the four wave sums as
+// (w0 + w1) + (w2 + w3). Called by all 256 threads; every thread gets the sum.
 template <bool F32_IN>
-__global__ __launch_bounds__(kTreeThreads) void dq_tree_level(const void* __restrict__ in, int64_t n,
-                                                              double* __restrict__ out, float* __restrict__ mean,
-                                                              int64_t n_total) {
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTreeChunk + threadIdx.x * kTreePerThread;
+__device__ double tree_chunk_sum(const void* __restrict__ in, int64_t n, int64_t c) {
+    const int64_t base = c * kTreeChunk + threadIdx.x * kTreePerThread;
     double v[kTreePerThread];
 #pragma unroll
     for (int i = 0; i < kTreePerThread; ++i) {
@@ -198,22 +231,44 @@ __global__ __launch_bounds__(kTreeThreads) void dq_tree_level(const void* __rest
     __shared__ double ws[kTreeThreads / 64];
     if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
     __syncthreads();
+    const double t = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    __syncthreads();  // ws may be reused by the caller
+    return t;
+}
+
+// One level of the tree: workgroup g writes the sum of chunk g. With a
+// single workgroup the root is the tree sum of everything and the mean is
+// written.
+template <bool F32_IN>
+__global__ __launch_bounds__(kTreeThreads) void dq_tree_level(const void* __restrict__ in, int64_t n,
+                                                              double* __restrict__ out, float* __restrict__ mean,
+                                                              int64_t n_total) {
+    const double t = tree_chunk_sum<F32_IN>(in, n, blockIdx.x);
     if (threadIdx.x == 0) {
-        const double t = (ws[0] + ws[1]) + (ws[2] + ws[3]);
         out[blockIdx.x] = t;
         if (mean != nullptr) *mean = static_cast<float>(t / static_cast<double>(n_total));
     }
 }
 
 // Symmetric E4M3FN code of (a - mean) per group of 256 constants; one wave
-// per group, four groups per workgroup.
+// per group, four groups per workgroup. With `partials` (at most 4096 chunk
+// sums of the tree), every workgroup first adds them up itself, in the tree's
+// order, instead of a separate launch doing it; workgroup 0 stores the mean.
 __global__ __launch_bounds__(256) void dq_encode(const float* __restrict__ absmax, int64_t n1,
-                                                 const float* __restrict__ mean_p, uint8_t* __restrict__ c8,
-                                                 float* __restrict__ scale) {
+                                                 const float* __restrict__ mean_p, const double* __restrict__ partials,
+                                                 int64_t npart, float* __restrict__ mean_out,
+                                                 uint8_t* __restrict__ c8, float* __restrict__ scale) {
+    float mu;
+    if (partials != nullptr) {
+        const double t = tree_chunk_sum<false>(partials, npart, 0);
+        mu = static_cast<float>(t / static_cast<double>(n1));
+        if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
+    } else {
+        mu = *mean_p;
+    }
     const int lane = threadIdx.x & 63;
     const int64_t g = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (g * QL_DQ_BLOCKSIZE >= n1) return;
-    const float mu = *mean_p;
     const int64_t i0 = g * QL_DQ_BLOCKSIZE + lane * 4;
     float d[4];
     bool valid[4];
@@ -258,10 +313,13 @@ size_t dq_workspace_bytes(int64_t n1) {
 
 int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* scale, float* mean, double* ws,
                         hipStream_t stream) {
+    // tree levels until at most one chunk (4096) of partial sums is left;
+    // the encoding kernel adds that last chunk itself (one launch fewer)
     int64_t count = n1;
     const void* in = absmax;
     bool f32 = true;
     double* out = ws;
+    const double* last = nullptr;  // partials the encoder reduces, or none (mean already stored)
     while (true) {
         const int64_t grid = ceil_div(count, kTreeChunk);
         float* mean_out = (grid == 1) ? mean : nullptr;
@@ -272,6 +330,11 @@ int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* sca
             hipLaunchKernelGGL(dq_tree_level<false>, dim3(static_cast<uint32_t>(grid)), dim3(kTreeThreads), 0,
                                stream, in, count, out, mean_out, n1);
         if (grid == 1) break;
+        if (grid <= kTreeChunk) {
+            last = out;
+            count = grid;
+            break;
+        }
         in = out;
         f32 = false;
         count = grid;
@@ -280,7 +343,7 @@ int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* sca
     const int64_t groups = ceil_div(n1, QL_DQ_BLOCKSIZE);
     timer_begin(QL_KERNEL_DQ_ENCODE, stream);
     hipLaunchKernelGGL(dq_encode, dim3(static_cast<uint32_t>(ceil_div(groups, 4))), dim3(256), 0, stream, absmax, n1,
-                       mean, c8, scale);
+                       mean, last, last ? count : 0, mean, c8, scale);
     timer_end(QL_KERNEL_DQ_ENCODE, stream);
     return check_launch("nf4_double_quant");
 }
