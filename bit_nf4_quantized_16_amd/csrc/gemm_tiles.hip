@@ -324,27 +324,64 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         __syncthreads();
     }
 
-    // Epilogue: D[m][t] -> out[t][m] in bf16; acc element r of sub-tile (a, b)
-    // sits at m = 32a + 8(r/4) + 4(lane/32) + r%4, t = 32b + lane%32.
+    // Epilogue: D[m][t] -> out[t][m]; acc element r of sub-tile (a, b) sits at
+    // m = 32a + 8(r/4) + 4(lane/32) + r%4, t = 32b + lane%32 of the wave tile.
+    if (p.splits > 1) {
+        // fp32 partial tile of this split (staging these through LDS like the
+        // bf16 tile below measured no faster)
+#pragma unroll
+        for (int a = 0; a < SA; ++a)
+#pragma unroll
+            for (int b = 0; b < ST; ++b)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int64_t m = m0 + wa * MW + a * 32 + 8 * qq + 4 * (lane >> 5);
+                    const int64_t t = t0 + wt * TW + b * 32 + (lane & 31);
+                    if (t < p.T && m < MA) {
+                        const float4 v = make_float4(acc[a][b][4 * qq], acc[a][b][4 * qq + 1], acc[a][b][4 * qq + 2],
+                                                     acc[a][b][4 * qq + 3]);
+                        *reinterpret_cast<float4*>(p.part + (static_cast<int64_t>(split) * p.T + t) * MA + m) = v;
+                    }
+                }
+        return;
+    }
+    // bf16 tile through the (now idle) LDS stages, transposed to [t][m], so
+    // that every global store writes whole 16-byte chunks of output rows
+    // (lanes 8 bytes each in 32 different rows would scatter the writes).
+    // Rows of TA bf16, a quarter of the TT rows per stage array, the 16-byte
+    // chunk c of row r stored at c ^ (r % CPR).
+    constexpr int RPA = TT / 4, CPR = TA / 8;
+    static_assert(RPA * TA * 2 <= TT * kStep * 2 && RPA * TA * 2 <= S::ROWS_A * LDA * 2, "output staging fits");
+    auto out_row = [&](int t) -> char* {
+        const int g = t / RPA;
+        uint16_t* const base = g == 0 ? sA0 : g == 1 ? sA1 : g == 2 ? sX0 : sX1;
+        return reinterpret_cast<char*>(base) + (t % RPA) * (TA * 2);
+    };
+    __syncthreads();  // every wave is done reading the stages
 #pragma unroll
     for (int a = 0; a < SA; ++a)
 #pragma unroll
         for (int b = 0; b < ST; ++b)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                const int64_t m = m0 + wa * MW + a * 32 + 8 * qq + 4 * (lane >> 5);
-                const int64_t t = t0 + wt * TW + b * 32 + (lane & 31);
-                if (t < p.T && m < MA && p.splits > 1) {
-                    float4 v = make_float4(acc[a][b][4 * qq], acc[a][b][4 * qq + 1], acc[a][b][4 * qq + 2],
-                                           acc[a][b][4 * qq + 3]);
-                    *reinterpret_cast<float4*>(p.part + (static_cast<int64_t>(split) * p.T + t) * MA + m) = v;
-                } else if (t < p.T && m < MA) {
-                    uint2 v;
-                    v.x = pack_bf16x2(acc[a][b][4 * qq], acc[a][b][4 * qq + 1]);
-                    v.y = pack_bf16x2(acc[a][b][4 * qq + 2], acc[a][b][4 * qq + 3]);
-                    *reinterpret_cast<uint2*>(p.out + t * MA + m) = v;
-                }
+                const int m = wa * MW + a * 32 + 8 * qq + 4 * (lane >> 5);
+                const int t = wt * TW + b * 32 + (lane & 31);
+                uint2 v;
+                v.x = pack_bf16x2(acc[a][b][4 * qq], acc[a][b][4 * qq + 1]);
+                v.y = pack_bf16x2(acc[a][b][4 * qq + 2], acc[a][b][4 * qq + 3]);
+                const int c = (m / 8) ^ (t % RPA % CPR);
+                *reinterpret_cast<uint2*>(out_row(t) + c * 16 + (m % 8) * 2) = v;
             }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TT * CPR / NTHR; ++i) {
+        const int q = i * NTHR + tid;
+        const int t = q / CPR, c = q % CPR;
+        const int64_t gt = t0 + t, gm = m0 + 8 * c;
+        if (gt >= p.T || gm >= MA) continue;  // MA is a multiple of 8: a chunk is whole or outside
+        const uint4 v = *reinterpret_cast<const uint4*>(out_row(t) + (c ^ (t % RPA % CPR)) * 16);
+        *reinterpret_cast<uint4*>(p.out + gt * MA + gm) = v;
+    }
 }
 
 namespace {
