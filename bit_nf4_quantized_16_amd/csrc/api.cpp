@@ -3,6 +3,7 @@
 // timers. No C++ exception crosses this file's extern "C" functions.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -138,6 +139,7 @@ int check_linear_shape(const ql_nf4_weight* w, int64_t T, int32_t r) {
 struct FwdWs {
     uint16_t* Us = nullptr;  // bf16 [T, rp64] = bf16(s U), GEMM path
     uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
+    void* proj = nullptr;    // split partials of the U projection
     float* split = nullptr;  // fp32 split-K partials of the GEMM path
     size_t bytes = 0;
 };
@@ -152,6 +154,8 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r) {
         if (r > 0) {
             f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
             if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
+            const size_t pb = lora_proj_ws_bytes(T, r, K, false);
+            if (pb) f.proj = c.take<char>(pb);
         }
         const size_t sb = gemm_split_bytes(N, T, K);
         if (sb) f.split = c.take<float>(sb / sizeof(float));
@@ -166,6 +170,7 @@ struct BwdWs {
     uint16_t* Gt = nullptr;  // bf16 [rp16, T] = G^T, dA's MFMA operand
     uint16_t* Ut = nullptr;  // bf16 [rp16, T] = U^T, dB's MFMA operand
     float* gpart = nullptr;  // fp32 token-split partials of dA and dB
+    void* proj = nullptr;    // split partials of the G (and U) projections, used in turn
     float* split = nullptr;  // fp32 split-K partials of the dX GEMM
     size_t bytes = 0;
 };
@@ -181,6 +186,8 @@ BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_
         if (want_db) b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
         const size_t gb = lora_grads_part_bytes(T, want_da ? K : 0, want_db ? N : 0, r);
         if (gb) b.gpart = c.take<float>(gb / sizeof(float));
+        const size_t pb = std::max(lora_proj_ws_bytes(T, r, N, true), lora_proj_ws_bytes(T, r, K, false));
+        if (pb) b.proj = c.take<char>(pb);
     }
     if (want_dx) {
         const size_t sb = gemm_split_bytes(K, T, N);
@@ -311,7 +318,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         a.alpha_b = scale;
         a.out_b = f.Us;
         a.ld_b = rp;
-        if ((s = launch_lora_proj(a, false, st)) != QL_OK) return s;
+        if ((s = launch_lora_proj(a, false, f.proj, st)) != QL_OK) return s;
         if (r % 8 != 0) {  // rows of B are not 16-byte aligned: pad them
             if ((s = launch_pad_copy(B, N, r, f.Bp, rp, st)) != QL_OK) return s;
             Bsrc = f.Bp;
@@ -390,7 +397,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
             a.rows_ut = rp16;
             a.ld_ut = ldv;
         }
-        if ((s = launch_lora_proj(a, true, st)) != QL_OK) return s;
+        if ((s = launch_lora_proj(a, true, b.proj, st)) != QL_OK) return s;
     }
     if (r > 0 && want_db && !have_u) {  // U^T = (X A^T)^T recomputed
         ProjArgs a{};
@@ -406,7 +413,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         a.out_bt = b.Ut;
         a.rows_bt = rp16;
         a.ld_bt = ldv;
-        if ((s = launch_lora_proj(a, false, st)) != QL_OK) return s;
+        if ((s = launch_lora_proj(a, false, b.proj, st)) != QL_OK) return s;
     }
     if (want_dx) {
         if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, b.split, st)) != QL_OK) return s;

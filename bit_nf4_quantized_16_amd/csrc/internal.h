@@ -55,8 +55,16 @@ struct ProjArgs {
     uint16_t* Ut;
     int rows_ut;
     int64_t ld_ut;
+    // set by the launcher: fp32 partials and per-token-block counters when
+    // the reduction is split over several workgroups, and the launch token
+    float* part;
+    uint64_t* cnt;
+    uint64_t token;
 };
-int launch_lora_proj(const ProjArgs& a, bool q_cols, hipStream_t stream);
+// Workspace of a projection over T tokens, rank rq, reduction kred (0 when
+// its reduction is not split); ws must hold that many bytes, 16-B aligned.
+size_t lora_proj_ws_bytes(int64_t T, int rq, int64_t kred, bool q_cols);
+int launch_lora_proj(const ProjArgs& a, bool q_cols, void* ws, hipStream_t stream);
 
 // dst[i][j] = src[i][j] for j < cols, 0 for cols <= j < ldd.
 int launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ldd, hipStream_t stream);

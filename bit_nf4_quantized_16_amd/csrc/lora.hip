@@ -14,6 +14,8 @@
 // epilogues, bf16 G^T and U^T for the gradient kernel), and the gradient
 // kernel computes dA and dB in one grid.
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 
 #include "common.h"
 #include "internal.h"
@@ -231,14 +233,18 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, g = lane >> 4;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int split = blockIdx.y, nsplit = gridDim.y;
+    __shared__ int s_last;
 
     if (p.proj) {
+        // this split's 64-wide steps [sbeg, send); wave w takes sbeg + w, sbeg + w + NW, ...
         const int64_t nst = ceil_div(p.kred, 64);
-        const int64_t my = nst > wave ? ceil_div(nst - wave, NW) : 0;  // this wave's steps
+        const int64_t sbeg = nst * split / nsplit, send = nst * (split + 1) / nsplit;
+        const int64_t my = send - sbeg > wave ? ceil_div(send - sbeg - wave, NW) : 0;  // this wave's steps
         const int64_t qlast = p.kred * p.rq - 8;
 
         auto issue = [&](int64_t s, uint16_t* sp, uint16_t* sq) {
-            const int64_t k0 = (wave + NW * s) * 64;
+            const int64_t k0 = (sbeg + wave + NW * s) * 64;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int row = 8 * i + (lane >> 3);
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto compute = [&](int64_t s, const uint16_t* sp, const uint16_t* sq) {
-            const int64_t k0 = (wave + NW * s) * 64;
+            const int64_t k0 = (sbeg + wave + NW * s) * 64;
             const bool partial = k0 + 64 > p.kred;  // wave-uniform
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -327,6 +333,18 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
             }
         }
 
+        // every layout the consumers read, from the final value v of
+        // (rank j, token t)
+        auto emit = [&](int j, int64_t t, float v) {
+            if (p.out_f != nullptr && j < p.rq) p.out_f[t * p.ld_f + j] = p.alpha_f * v;
+            const uint16_t hb = to_bf16_bits(j < p.rq ? p.alpha_b * v : 0.0f);
+            if (p.out_b != nullptr && j < p.ld_b) p.out_b[t * p.ld_b + j] = hb;
+            if (p.out_bt != nullptr && j < p.rows_bt) p.out_bt[j * p.ld_bt + t] = hb;
+        };
+        // with splits, this split's partial of rank tile rt, element
+        // e = 16 jl + tl, goes to part[((blockIdx.x nsplit + split) RT + rt) 256 + e]
+        float* const mypart = p.part + ((static_cast<int64_t>(blockIdx.x) * nsplit + split) * RT) * 256;
+
         // D[j = 4 g + rr][token li] of each rank tile; fixed-order sum of the waves
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -336,26 +354,59 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
             __syncthreads();
             for (int e = tid; e < 256; e += 64 * NW) {
                 const int jl = e >> 4, tl = e & 15;
-                const int64_t t = t0 + tl;
-                if (t >= p.T) continue;
                 float v = 0.0f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) v += red[ww][jl][tl];
-                const int j = 16 * rt + jl;
-                if (p.out_f != nullptr && j < p.rq) p.out_f[t * p.ld_f + j] = p.alpha_f * v;
-                const uint16_t hb = to_bf16_bits(j < p.rq ? p.alpha_b * v : 0.0f);
-                if (p.out_b != nullptr && j < p.ld_b) p.out_b[t * p.ld_b + j] = hb;
-                if (p.out_bt != nullptr && j < p.rows_bt) p.out_bt[j * p.ld_bt + t] = hb;
+                if (nsplit > 1) {
+                    // device-scope store: read back by another workgroup,
+                    // possibly on another XCD
+                    __hip_atomic_store(mypart + rt * 256 + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    continue;
+                }
+                const int64_t t = t0 + tl;
+                if (t < p.T) emit(16 * rt + jl, t, v);
             }
         }
-        if (p.out_b != nullptr) {  // zero columns past the rank tiles
+        if (nsplit > 1) {
+            // The last split of this token block to arrive (a per-block
+            // counter tagged with the launch token; a counter carrying another
+            // token counts as zero) adds the partials in split order, so the
+            // result does not depend on the arrival order. The wait orders
+            // the partial stores before the count.
+            __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+            __syncthreads();
+            if (tid == 0) {
+                uint64_t* c = p.cnt + blockIdx.x;
+                uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                uint64_t nv;
+                do {
+                    nv = ((old >> 8) == p.token) ? old + 1 : ((p.token << 8) | 1u);
+                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT));
+                s_last = static_cast<int>(nv & 0xFFu) == nsplit;
+            }
+            __syncthreads();
+            if (s_last) {
+                const float* const blockpart = p.part + static_cast<int64_t>(blockIdx.x) * nsplit * RT * 256;
+                for (int e = tid; e < RT * 256; e += 64 * NW) {
+                    float v = 0.0f;
+                    for (int sp = 0; sp < nsplit; ++sp)
+                        v += __hip_atomic_load(blockpart + sp * RT * 256 + e, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    const int rt = e >> 8, jl = (e >> 4) & 15, tl = e & 15;
+                    const int64_t t = t0 + tl;
+                    if (t < p.T) emit(16 * rt + jl, t, v);
+                }
+            }
+        }
+        if (p.out_b != nullptr && split == 0) {  // zero columns past the rank tiles
             for (int e = tid; e < 16 * (p.ld_b - 16 * RT); e += 64 * NW) {
                 const int64_t tt = t0 + (e & 15);
                 if (tt < p.T) p.out_b[tt * p.ld_b + 16 * RT + (e >> 4)] = 0;
             }
         }
     }
-    if (p.Ut != nullptr) {
+    if (p.Ut != nullptr && split == 0) {
         for (int e = tid; e < 16 * p.rows_ut; e += 64 * NW) {
             const int j = e >> 4;
             const int64_t tt = t0 + (e & 15);
@@ -364,9 +415,64 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
     }
 }
 
+namespace {
+
+int cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cached = n;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
+// A fresh 56-bit token per launch, so that split counters left in a reused
+// workspace by earlier launches count as zero.
+uint64_t next_token() {
+    static std::atomic<uint64_t> ctr{
+        (static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) * 0x9E3779B97F4A7C15ull) >>
+        8};
+    return ctr.fetch_add(1) & ((1ull << 56) - 1);
+}
+
+int proj_rt(int rq) {
+    const int tiles = (rq + 15) / 16;
+    return tiles <= 2 ? tiles : (tiles <= 4 ? 4 : 8);
+}
+
+int proj_waves(int rt) { return rt == 1 ? ProjDma<1>::NW : rt == 2 ? ProjDma<2>::NW : rt == 4 ? ProjDma<4>::NW : ProjDma<8>::NW; }
+
+// Workgroups per 16-token block: enough blocks to cover the CUs, each
+// split keeping at least five steps per wave (with fewer, splitting
+// measured slower than not: the partial-sum hand-off costs a few memory
+// round trips); at most 8, and 1 for the register-path kernel.
+int proj_splits(int64_t T, int rq, int64_t kred, bool q_cols) {
+    if (q_cols && rq % 4 != 0) return 1;
+    const int64_t nblk = ceil_div(T, 16);
+    const int64_t nst = ceil_div(kred, 64);
+    int64_t s = cu_count() / nblk;
+    s = std::min<int64_t>(s, nst / (5 * proj_waves(proj_rt(rq))));
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 8)));
+}
+
+}  // namespace
+
+size_t lora_proj_ws_bytes(int64_t T, int rq, int64_t kred, bool q_cols) {
+    if (T <= 0 || rq < 1) return 0;
+    const int s = proj_splits(T, rq, kred, q_cols);
+    if (s == 1) return 0;
+    const int64_t nblk = ceil_div(T, 16);
+    const size_t part = static_cast<size_t>(nblk) * s * proj_rt(rq) * 256 * sizeof(float);
+    return (part + 255) / 256 * 256 + static_cast<size_t>(nblk) * sizeof(uint64_t);
+}
+
 template <bool QCOLS>
-static void launch_proj_dma_rt(int rt, const ProjArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<uint32_t>(ceil_div(a.T, 16)));
+static void launch_proj_dma_rt(int rt, const ProjArgs& a, int splits, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(ceil_div(a.T, 16)), static_cast<uint32_t>(splits));
     switch (rt) {
         case 1:
             hipLaunchKernelGGL((lora_proj_dma_kernel<1, QCOLS>), grid, dim3(64 * ProjDma<1>::NW), 0, stream, a);
@@ -394,17 +500,28 @@ static void launch_proj_rt(int rt, const ProjArgs& a, hipStream_t stream) {
     }
 }
 
-int launch_lora_proj(const ProjArgs& a, bool q_cols, hipStream_t stream) {
+int launch_lora_proj(const ProjArgs& args, bool q_cols, void* ws, hipStream_t stream) {
+    ProjArgs a = args;
     if (a.rq < 1 || a.rq > QL_MAX_RANK) return set_error(QL_ERR_SHAPE, "LoRA projection: rank %d out of range", a.rq);
     if (a.T <= 0) return QL_OK;
-    const int tiles = (a.rq + 15) / 16;
-    const int rt = tiles <= 2 ? tiles : (tiles <= 4 ? 4 : 8);
+    const int rt = proj_rt(a.rq);
     if (a.out_b != nullptr && a.ld_b < a.rq)
         return set_error(QL_ERR_SHAPE, "LoRA projection: bf16 output narrower than the rank");
+    const int splits = a.proj ? proj_splits(a.T, a.rq, a.kred, q_cols) : 1;
+    a.part = nullptr;
+    a.cnt = nullptr;
+    a.token = next_token();
+    if (splits > 1) {
+        if (ws == nullptr) return set_error(QL_ERR_WORKSPACE, "LoRA projection: split workspace missing");
+        const int64_t nblk = ceil_div(a.T, 16);
+        const size_t part = static_cast<size_t>(nblk) * splits * rt * 256 * sizeof(float);
+        a.part = static_cast<float*>(ws);
+        a.cnt = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + (part + 255) / 256 * 256);
+    }
     if (!q_cols)
-        launch_proj_dma_rt<false>(rt, a, stream);
+        launch_proj_dma_rt<false>(rt, a, splits, stream);
     else if (a.rq % 4 == 0)
-        launch_proj_dma_rt<true>(rt, a, stream);
+        launch_proj_dma_rt<true>(rt, a, splits, stream);
     else
         launch_proj_rt<true>(rt, a, stream);
     return check_launch("LoRA projection");

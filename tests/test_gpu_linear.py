@@ -153,6 +153,25 @@ def test_bitwise_deterministic(qn):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("r", [16, 40, 128])
+def test_split_projections_deterministic(qn, r):
+    """At few tokens the LoRA projections split their reduction over several
+    workgroups (the last to arrive adds the partials in order): parity with
+    the oracle, and three calls in a row (reusing the workspace and its
+    stale counters) give the same bits."""
+    W = workloads.normal_weight(5120, 5120, 0.02, seed=23 + r)
+    case = workloads.lora_case("splitproj_r%d" % r, W, 256, r, 2.0 * r, 1 / 5120, 0.05, seed=23)
+    _, (w, X, dY, A, B, Y, dX, dA, dB) = _run(qn, case)
+    for _ in range(2):
+        Y2, U2 = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+        dX2, dA2, dB2 = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, U=U2)
+        dX3, dA3, dB3 = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale)  # U recomputed
+        torch.cuda.synchronize()
+        for a, b in ((Y2, Y), (dX2, dX), (dA2, dA), (dB2, dB), (dX3, dX), (dA3, dA)):
+            assert torch.equal(a, b)
+        assert normwise_rel_err(f32_to_np(dB3), f32_to_np(dB)) < 1e-6
+
+
 def test_gradient_accumulation(qn):
     W = workloads.normal_weight(256, 256, 0.02, seed=20)
     case = workloads.lora_case("acc", W, 64, 8, 16.0, 1 / 256, 0.05, seed=20)
