@@ -126,10 +126,11 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wa = wave / WT, wt = wave % WT;
-    // With eight waves, the two waves that share a SIMD (w and w+4) run the
-    // two halves of a step in opposite order, so one expands codes (VALU)
-    // while the other feeds the matrix core.
-    const bool expand_first = (NW == 8) && ((wave >> 2) & 1);
+    // dX: with eight waves, the two waves that share a SIMD (w and w+4) run
+    // the two halves of a step in opposite order, so one expands codes (VALU)
+    // while the other feeds the matrix core. The forward instead interleaves
+    // each wave's own work instruction by instruction (interleave_step below).
+    const bool expand_first = DX && (NW == 8) && ((wave >> 2) & 1);
 
     // Workgroups are handed to the eight XCDs round robin; give each XCD a
     // contiguous range of tiles, token-major, so one XCD's L2 serves the same
@@ -248,6 +249,22 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         }
     };
 
+    // Forward step schedule: groups of one MFMA, one LDS operand read and six
+    // VALU instructions (the expansion of the next step), so the three pipes
+    // overlap within every wave; measured 3-5 % faster than the compiler's
+    // order with the ping-pong above. (The dX kernel, whose A operands take
+    // two transposing reads each, measured no better with it.)
+    auto interleave_step = [&]() {
+        if constexpr (!DX) {
+#pragma unroll
+            for (int ig = 0; ig < SA * ST * (kStep / 16); ++ig) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+            }
+        }
+    };
+
     // Pipeline (two steps per iteration, stages named statically):
     //   step s:   token loads for s+1 -> the other stage; codes for s+2 -> the
     //             free register set; MFMAs on stage s; expand step s+1.
@@ -262,6 +279,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         dma(min(s + 1, msteps - 1), sX1);
         __builtin_amdgcn_sched_barrier(0);  // the token loads stay ahead of the code loads
         gcodes(min(s + 2, msteps - 1), cs0);
+        interleave_step();
         if (expand_first) {
             expand(s + 1, cs1, sA1);
             compute(sA0, sX0);
@@ -274,6 +292,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         dma(min(s + 2, msteps - 1), sX0);
         __builtin_amdgcn_sched_barrier(0);
         gcodes(min(s + 3, msteps - 1), cs1);
+        interleave_step();
         if (expand_first) {
             expand(s + 2, cs0, sA0);
             compute(sA1, sX1);
