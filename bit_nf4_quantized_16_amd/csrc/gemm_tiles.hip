@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     // dX: with eight waves, the two waves that share a SIMD (w and w+4) run
     // the two halves of a step in opposite order, so one expands codes (VALU)
     // while the other feeds the matrix core. The forward instead interleaves
-    // each wave's own work instruction by instruction (interleave_step below).
+    // each wave's own work (compute_expand below).
     const bool expand_first = DX && (NW == 8) && ((wave >> 2) & 1);
 
     // Workgroups are handed to the eight XCDs round robin; give each XCD a
@@ -249,19 +249,52 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         }
     };
 
-    // Forward step schedule: groups of one MFMA, one LDS operand read and six
-    // VALU instructions (the expansion of the next step), so the three pipes
-    // overlap within every wave; measured 3-5 % faster than the compiler's
-    // order with the ping-pong above. (The dX kernel, whose A operands take
-    // two transposing reads each, measured no better with it.)
+    // Forward step: the MFMAs on one stage fused with the expansion of the
+    // next step's codes into the other, a quarter of the expansion after each
+    // 16-wide slice of the reduction, and scheduling groups that issue the
+    // next slice's operand reads between this slice's MFMAs (six reads ahead)
+    // with five VALU instructions after each MFMA. The three pipes then
+    // overlap within every wave; measured 8-10 % faster than the two-wave
+    // ping-pong of separate compute and expand phases, which the dX kernel
+    // keeps (its A operands take two transposing reads each, and the fused
+    // form measured slower there).
+    auto compute_expand = [&](const uint16_t* sA, const uint16_t* sX, const Codes<CC>& cs, uint16_t* sAo) {
+        const Lut16 L = make_lut(block_value(cs.bc, DQ ? 1 : 0, mu));
+        uint16_t* dst = sAo + wrow * LDA + wcol;
+        constexpr int NQ = CC * 4, PER = NQ / (kStep / 16);  // 8-code words per slice
+        static_assert(NQ % (kStep / 16) == 0, "expansion split over the slices");
+#pragma unroll
+        for (int ks = 0; ks < kStep / 16; ++ks) {
+            bf16x8_t av[SA], bv[ST];
+#pragma unroll
+            for (int a = 0; a < SA; ++a) av[a] = load_a(sA, a, ks);
+#pragma unroll
+            for (int b = 0; b < ST; ++b) bv[b] = load_b(sX, b, ks);
+#pragma unroll
+            for (int a = 0; a < SA; ++a)
+#pragma unroll
+                for (int b = 0; b < ST; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+#pragma unroll
+            for (int j = ks * PER; j < (ks + 1) * PER; ++j) {
+                const int cc = j / 4, q = j % 4;
+                const uint32_t w = q == 0 ? cs.c[cc].x : q == 1 ? cs.c[cc].y : q == 2 ? cs.c[cc].z : cs.c[cc].w;
+                st16(dst + 32 * cc + 8 * q, dequant8_lut(w, L));
+            }
+        }
+    };
     auto interleave_step = [&]() {
         if constexpr (!DX) {
+            __builtin_amdgcn_sched_group_barrier(0x100, SA + ST, 0);  // LDS reads: operands of slice 0
 #pragma unroll
-            for (int ig = 0; ig < SA * ST * (kStep / 16); ++ig) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-            }
+            for (int ks = 0; ks < kStep / 16; ++ks)
+#pragma unroll
+                for (int i = 0; i < SA * ST; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    if (ks + 1 < kStep / 16 && i < SA + ST)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an operand of slice ks + 1
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // VALU
+                }
         }
     };
 
@@ -280,7 +313,9 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         __builtin_amdgcn_sched_barrier(0);  // the token loads stay ahead of the code loads
         gcodes(min(s + 2, msteps - 1), cs0);
         interleave_step();
-        if (expand_first) {
+        if constexpr (!DX) {
+            compute_expand(sA0, sX0, cs1, sA1);
+        } else if (expand_first) {
             expand(s + 1, cs1, sA1);
             compute(sA0, sX0);
         } else {
@@ -293,7 +328,9 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         __builtin_amdgcn_sched_barrier(0);
         gcodes(min(s + 3, msteps - 1), cs1);
         interleave_step();
-        if (expand_first) {
+        if constexpr (!DX) {
+            compute_expand(sA1, sX1, cs0, sA0);
+        } else if (expand_first) {
             expand(s + 2, cs0, sA0);
             compute(sA1, sX1);
         } else {
