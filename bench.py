@@ -130,23 +130,24 @@ KERNELS = {
 }
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_fwd_llama7b_mlp.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_llama7b_mlp.json")
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when there is none or the
-    kernel's sources have changed since the counters were taken."""
+    """HBM bytes per launch of `kernel` ("gemm_fwd" or "gemm_dx") from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is
+    none or the GEMM sources have changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
-        if d.get("kernel") != kernel:
+        entry = d["kernels"].get(kernel)
+        if entry is None:
             return None
         h = hashlib.sha256()
         for src in d["source_files"]:
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
-        return d["bytes_per_launch"] if h.hexdigest() == d["source_sha256"] else None
+        return entry["bytes_per_launch"] if h.hexdigest() == d["source_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
 

@@ -30,6 +30,9 @@
  *     asynchronous on it; buffers must stay alive until the work completes.
  *     Calls are re-entrant; calls that share output or workspace buffers on
  *     different streams race.
+ *   - Workspace buffers need no initialisation and may hold anything between
+ *     calls (the arrival counters kept in them are tagged with a token that
+ *     is new for every launch).
  *   - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
  *   - All arguments are validated before anything is launched; on an error
  *     nothing is written. No C++ exception crosses this interface.
