@@ -76,6 +76,14 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 #define QL_GEMM_DX_PAD 32
 #endif
 
+// dX weight tile: the 16-byte chunk c of row r is stored at chunk c ^ (r & 3).
+// The expansion writes eight 64-byte row pieces per 16 lanes, which without
+// it fall on four bank groups (4-way conflicts); with it two-way, while the
+// transposing reads (whose rows r and r + 4 share the swizzle) stay
+// conflict-free. (Measured time-neutral: the conflicts were not what bounds
+// the dX kernel.)
+__device__ __forceinline__ int dx_col(int r, int c) { return (((c >> 3) ^ (r & 3)) << 3) | (c & 7); }
+
 // End of a pipeline stage: this wave's LDS writes are complete and its
 // direct-to-LDS token loads have landed, then the workgroup barrier. The
 // token loads of the stage were issued before at least N other vector loads
@@ -197,12 +205,15 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         float a = block_value(cs.bc, DQ ? 1 : 0, mu);
         if constexpr (DX) a = (static_cast<int64_t>(step) * kStep + wrow < p.N) ? a : 0.0f;
         const Lut16 L = make_lut(a);
-        uint16_t* dst = sA + wrow * LDA + wcol;
+        uint16_t* dst = sA + wrow * LDA;
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
             const uint32_t words[4] = {cs.c[cc].x, cs.c[cc].y, cs.c[cc].z, cs.c[cc].w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) st16(dst + 32 * cc + 8 * q, dequant8_lut(words[q], L));
+            for (int q = 0; q < 4; ++q) {
+                const int c = wcol + 32 * cc + 8 * q;
+                st16(dst + (DX ? dx_col(wrow, c) : c), dequant8_lut(words[q], L));
+            }
         }
     };
 
@@ -220,8 +231,8 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         } else {
             // rows (reduction) 16 ks + 8 (lane/32) + 0..7 of column (k out) lane%32
             const int grp = lane >> 4, j = lane & 15;
-            const uint16_t* base =
-                sA + (ks * 16 + 8 * (grp >> 1) + (j >> 2)) * LDA + wa * MW + a * 32 + 16 * (grp & 1) + 4 * (j & 3);
+            const int r = ks * 16 + 8 * (grp >> 1) + (j >> 2);  // and r + 4, same swizzle
+            const uint16_t* base = sA + r * LDA + dx_col(r, wa * MW + a * 32 + 16 * (grp & 1) + 4 * (j & 3));
             const v4i16 lo = ld_tr16(base);
             const v4i16 hi = ld_tr16(base + 4 * LDA);
             const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                 const int64_t j = j0 + row;
                 const int64_t k = m0 + col;
                 const uint4 v = (j < p.r_la && k < p.K) ? ld16(p.la + j * p.ld_la + k) : make_uint4(0, 0, 0, 0);
-                st16(sA0 + row * LDA + col, v);
+                st16(sA0 + row * LDA + dx_col(row, col), v);
             }
         }
         __syncthreads();
