@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-stage cold-cache measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the step: the wider measurement set (32-layer 7B stack, 65B linears, "
+                         "a GEMV pass over the stack, residency, torch.matmul context), one JSON line")
     return ap.parse_args()
 
 
@@ -299,6 +302,188 @@ def cpu_baseline(inp, ideal_s):
     }
 
 
+
+# ---------------------------------------------------------------------------
+# --suite: the wider measurement set. Weights are generated on the device
+# (seeded torch generator); nothing here is compared with the oracle (the
+# tests do that at these shapes on sampled outputs).
+# ---------------------------------------------------------------------------
+LLAMA7B_LAYER = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+                 ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)]
+LLAMA65B = [("sq", 8192, 8192), ("up", 22016, 8192), ("down", 8192, 22016)]
+
+
+def bwd_flops(N, K, T, r):
+    return 2 * T * N * K + 2 * T * N * r + 2 * T * r * K + 2 * r * T * K + 2 * N * T * r
+
+
+def clock_info():
+    import subprocess
+    out = {}
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c"], ["rocm-smi", "--showclocks"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            lines = [ln.strip() for ln in r.stdout.splitlines() if "clk" in ln.lower() or "CLK" in ln]
+            out[cmd[0]] = lines[:12]
+        except (OSError, subprocess.SubprocessError):
+            out[cmd[0]] = None
+    return out
+
+
+def run_suite(torch, qn):
+    res = {}
+    prop = torch.cuda.get_device_properties(0)
+    res["device"] = {"name": prop.name, "compute_units": prop.multi_processor_count,
+                     "memory_GiB": round(prop.total_memory / 2 ** 30, 1), "clocks": clock_info()}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=5, warm=1):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    g = torch.Generator(device="cuda")
+
+    def dev_randn(shape, std, seed, dtype=torch.float32):
+        g.manual_seed(seed)
+        return (torch.randn(shape, device="cuda", generator=g) * std).to(dtype)
+
+    # (1) the 32-layer 7B-shaped stack quantized end to end (fp32 in, DQ).
+    # Times are the library's HIP-event kernel timers summed over the launches
+    # (quantize, double-quant levels): GPU time, without the host's launch gaps.
+    print("suite: quantizing the 7B stack", file=sys.stderr, flush=True)
+    tq, td = qn.KernelTimer(1), qn.KernelTimer(2)
+    stack, nweights = [], 0
+    tq.arm()
+    td.arm()
+    for layer in range(32):
+        for i, (name, n, k) in enumerate(LLAMA7B_LAYER):
+            W = dev_randn((n, k), 0.02, 1000 * layer + i)
+            w = qn.quantize_weight(W)
+            nweights += n * k
+            stack.append((name, n, k, w))
+            del W
+    torch.cuda.synchronize()
+    nq, msq = tq.read()
+    nd, msd = td.read()
+    tq.disarm()
+    td.disarm()
+    qsec = (msq + msd) / 1e3
+    qbytes = (BPW_QUANT_F32 + BPW_DQ) * nweights
+    res["c4_stack_quantize"] = {"weights": nweights, "quantize_ms": round(msq, 3), "double_quant_ms": round(msd, 3),
+                                "launches": nq + nd, "GB/s": round(qbytes / qsec / 1e9, 1),
+                                "frac": round(qbytes / qsec / PEAK_HBM, 4),
+                                "quantize_alone_GB/s": round(BPW_QUANT_F32 * nweights / (msq / 1e3) / 1e9, 1)}
+    packed_bytes = sum(w.packed.numel() + w.c8.numel() + 4 * w.dq_scale.numel() for _, _, _, w in stack)
+    res["c4_stack_resident_GB"] = round(packed_bytes / 1e9, 3)
+
+    # (2) one decode GEMV pass over all 224 linears, r = 16, T in {1, 16}:
+    # the sum of the GEMV kernel times, and the wall time of the pass
+    print("suite: GEMV pass", file=sys.stderr, flush=True)
+    lora = {}
+    for _, n, k in LLAMA7B_LAYER:
+        if (n, k) not in lora:
+            lora[(n, k)] = (dev_randn((16, k), 1.0 / k, n + k, torch.bfloat16),
+                            dev_randn((n, 16), 0.01, n + 2 * k, torch.bfloat16))
+    for T in (1, 16):
+        Xs = {k: dev_randn((T, k), 1.0, k + T, torch.bfloat16) for k in (4096, 11008)}
+        outs = [torch.empty(T, n, dtype=torch.bfloat16, device="cuda") for _, n, _, _ in stack]
+
+        def gemv_pass():
+            for (_, n, k, w), Y in zip(stack, outs):
+                A, B = lora[(n, k)]
+                qn.qlora_linear_fwd(w, Xs[k], A, B, 2.0, save_u=False, out=Y)
+
+        wall = timed(gemv_pass, reps=3)
+        tg = qn.KernelTimer(4)
+        tg.arm()
+        gemv_pass()
+        torch.cuda.synchronize()
+        ng, msg = tg.read()
+        tg.disarm()
+        sec = msg / 1e3
+        nbytes = sum(gemv_bytes(n, k, T, 16) for _, n, k, _ in stack)
+        res["c4_gemv_pass_T%d" % T] = {"calls": ng, "kernel_ms": round(msg, 3), "wall_ms": round(wall * 1e3, 3),
+                                       "GB": round(nbytes / 1e9, 3), "GB/s": round(nbytes / sec / 1e9, 1),
+                                       "frac": round(nbytes / sec / PEAK_HBM, 4),
+                                       "kernel_us_per_call": round(msg * 1e3 / max(ng, 1), 2)}
+        del outs
+
+    def gemm_rows(shapes, T, r, alpha, std, seed0, weights=None):
+        rows, tf_f, tf_b, t_f, t_b = {}, 0.0, 0.0, 0.0, 0.0
+        for i, (name, n, k) in enumerate(shapes):
+            w = weights[i] if weights is not None else qn.quantize_weight(dev_randn((n, k), std, seed0 + i))
+            X = dev_randn((T, k), 1.0, seed0 + 100 + i, torch.bfloat16)
+            dY = dev_randn((T, n), 1.0, seed0 + 200 + i, torch.bfloat16)
+            A = dev_randn((r, k), 1.0 / k, seed0 + 300 + i, torch.bfloat16)
+            B = dev_randn((n, r), 0.01, seed0 + 400 + i, torch.bfloat16)
+            s = alpha / r
+            sf = timed(lambda: qn.qlora_linear_fwd(w, X, A, B, s))
+            _, U = qn.qlora_linear_fwd(w, X, A, B, s)
+            sb = timed(lambda: qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U))
+            ff, fb = fwd_flops(n, k, T, r), bwd_flops(n, k, T, r)
+            rows[name] = {"shape": [n, k], "fwd_us": round(sf * 1e6, 1), "fwd_TFLOP/s": round(ff / sf / 1e12, 1),
+                          "fwd_frac": round(ff / sf / PEAK_BF16, 4), "bwd_us": round(sb * 1e6, 1),
+                          "bwd_TFLOP/s": round(fb / sb / 1e12, 1), "bwd_frac": round(fb / sb / PEAK_BF16, 4)}
+            tf_f += ff
+            tf_b += fb
+            t_f += sf
+            t_b += sb
+            del X, dY, A, B, U
+        rows["aggregate"] = {"fwd_ms": round(t_f * 1e3, 3), "fwd_TFLOP/s": round(tf_f / t_f / 1e12, 1),
+                             "fwd_frac": round(tf_f / t_f / PEAK_BF16, 4), "bwd_ms": round(t_b * 1e3, 3),
+                             "bwd_TFLOP/s": round(tf_b / t_b / 1e12, 1), "bwd_frac": round(tf_b / t_b / PEAK_BF16, 4)}
+        return rows
+
+    # (3) GEMMs of one 7B layer at T = 4096, r = 64, alpha = 16 (layer 0 of the
+    # stack); the stack's 32 layers take 32x that time
+    print("suite: 7B layer GEMMs", file=sys.stderr, flush=True)
+    layer0 = [w for _, _, _, w in stack[:7]]
+    rows = gemm_rows(LLAMA7B_LAYER, 4096, 64, 16.0, 0.02, 7000, weights=layer0)
+    agg = rows["aggregate"]
+    agg["stack_fwd_bwd_ms_x32"] = round(32 * (agg["fwd_ms"] + agg["bwd_ms"]), 1)
+    res["c4_layer_T4096_r64"] = rows
+    del stack, layer0
+    torch.cuda.empty_cache()
+
+    # (4) the 65B-shaped linears at T = 4096, r = 64
+    print("suite: 65B linears", file=sys.stderr, flush=True)
+    res["c5_T4096_r64"] = gemm_rows(LLAMA65B, 4096, 64, 16.0, 0.015, 8000)
+    torch.cuda.empty_cache()
+
+    # (5) residency: 80 layers of 65B-shaped packed weights + constants
+    per_layer = 4 * 8192 * 8192 + 2 * 22016 * 8192 + 8192 * 22016
+    nbytes = per_layer * 80 * (0.5 + 1 / 64 + 4 / (64 * 256))
+    buf = torch.empty(int(nbytes), dtype=torch.uint8, device="cuda")
+    free, total = torch.cuda.mem_get_info()
+    res["c5_80_layer_residency"] = {"packed_GB": round(nbytes / 1e9, 2), "allocated": True,
+                                    "free_after_GB": round(free / 1e9, 1), "total_GB": round(total / 1e9, 1)}
+    del buf
+    torch.cuda.empty_cache()
+
+    # (6) context: the fused NF4 GEMM against torch.matmul (hipBLASLt) on the
+    # dequantized bf16 weight, 7B gate shape, T = 1024
+    n, k, T = 11008, 4096, 1024
+    w = qn.quantize_weight(dev_randn((n, k), 0.02, 9000))
+    Wd = qn.nf4_dequantize(w)
+    X = dev_randn((T, k), 1.0, 9001, torch.bfloat16)
+    s_nf4 = timed(lambda: qn.qlora_linear_fwd(w, X, save_u=False), reps=11)
+    s_mm = timed(lambda: torch.matmul(X, Wd.t()), reps=11)
+    fl = 2 * T * n * k
+    res["context_vs_torch_matmul_11008x4096_T1024"] = {
+        "nf4_fused_us": round(s_nf4 * 1e6, 1), "nf4_fused_TFLOP/s": round(fl / s_nf4 / 1e12, 1),
+        "torch_matmul_bf16_us": round(s_mm * 1e6, 1), "torch_matmul_TFLOP/s": round(fl / s_mm / 1e12, 1),
+        "nf4_over_bf16_time": round(s_nf4 / s_mm, 3)}
+    return res
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -311,6 +496,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     torch.cuda.set_device(0)
+    if args.suite:
+        print(json.dumps({"suite": run_suite(torch, qn)}), flush=True)
+        return
     print("bench: generating inputs", file=sys.stderr, flush=True)
     inp = Inputs(torch, workloads)
     torch.cuda.synchronize()
