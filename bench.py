@@ -217,6 +217,9 @@ def measure_rows(torch, qn, inp, flush):
     rows["gemm_dx_T1024_11008x4096"] = _mfma_row(dx_flops(N, K, T, r) - 2 * T * N * r, sec)
     sec = timed(7, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_dx=False))
     rows["lora_grad_T1024_11008x4096"] = _hbm_row(lora_grad_bytes(N, K, T, r), sec)  # dA and dB, one launch
+    # adapter merge of the same weight: codes and constants in, bf16 out, A and B read once
+    sec = timed(8, lambda: qn.qlora_merge(w, m["A"], m["B"], m["s"]))
+    rows["merge_r%d_11008x4096" % r] = _hbm_row(BPW_DEQUANT * N * K + 2 * r * (N + K), sec)
     # dispatch floor: the same HIP-event timing around a kernel that does
     # nothing measurable (a one-element fill), cold cache as above
     tiny = torch.empty(1, device="cuda")

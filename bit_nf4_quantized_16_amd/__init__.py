@@ -22,6 +22,7 @@ __all__ = [
     "nf4_quantize",
     "nf4_double_quant",
     "nf4_dequantize",
+    "qlora_merge",
     "qlora_linear_fwd",
     "qlora_linear_bwd",
     "quantize_weight",
@@ -155,6 +156,16 @@ def nf4_dequantize(w, dtype=torch.bfloat16, out=None):
         out = torch.empty(w.rows, w.cols, dtype=dtype, device=w.packed.device)
     d = w.descriptor()
     _check(lib.nf4_dequantize(ctypes.byref(d), _ptr(out), od, _stream()))
+    return out
+
+
+def qlora_merge(w, A=None, B=None, scale=1.0, out=None):
+    """bf16 [rows, cols] = dequant(W) + scale * B @ A (one rounding to bf16)."""
+    r = 0 if A is None else A.shape[0]
+    if out is None:
+        out = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.packed.device)
+    d = w.descriptor()
+    _check(lib.qlora_merge(ctypes.byref(d), _ptr(_bits(A)), _ptr(_bits(B)), r, float(scale), _ptr(out), _stream()))
     return out
 
 

@@ -28,6 +28,7 @@ QL_KERNEL_GEMV = 4
 QL_KERNEL_GEMM_FWD = 5
 QL_KERNEL_GEMM_DX = 6
 QL_KERNEL_LORA_GRAD = 7
+QL_KERNEL_MERGE = 8
 
 
 class QlNf4Weight(ctypes.Structure):
@@ -61,6 +62,7 @@ SIGNATURES = {
     "nf4_double_quant_workspace": (_SZ, [_I64]),
     "nf4_double_quant": (_I, [_P, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nf4_dequantize": (_I, [_WP, _P, _I, _P]),
+    "qlora_merge": (_I, [_WP, _P, _P, _I32, _F, _P, _P]),
     "qlora_linear_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),

@@ -266,6 +266,20 @@ int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* strea
     return launch_dequantize(*w, out, out_dtype == QL_BF16, static_cast<hipStream_t>(stream));
 }
 
+int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale, uint16_t* out,
+                void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if ((s = check_weight(w)) != QL_OK) return s;
+    if ((s = check_linear_shape(w, 0, r)) != QL_OK) return s;
+    if ((s = check_ptr(out, "out")) != QL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (r == 0) return launch_dequantize(*w, out, true, st);
+    if ((s = check_ptr(A, "A")) != QL_OK) return s;
+    if ((s = check_ptr(B, "B")) != QL_OK) return s;
+    return launch_merge(to_dev(w), w->rows, w->cols, A, B, r, scale, out, st);
+}
+
 size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
     if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
     return carve_fwd(nullptr, rows, cols, T, r).bytes;

@@ -25,6 +25,12 @@ int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* sca
                         hipStream_t stream);
 int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStream_t stream);
 
+// Adapter merge: out[n][k] = bf16(fl32(w'[n][k] + scale sum_j B[n][j] A[j][k]))
+// for 1 <= r <= QL_MAX_RANK, K % 64 == 0. Dynamic LDS merge_lds_bytes(r).
+size_t merge_lds_bytes(int r);
+int launch_merge(const NF4Dev& w, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int r, float scale,
+                 uint16_t* out, hipStream_t stream);
+
 // LoRA projection V[t][j] = sum_k P[t][k] Q[j][k] (j < rq), one launch:
 //   out_f[t][j]  = alpha_f V[t][j]                      (fp32, j < rq)
 //   out_b[t][j]  = bf16(alpha_b V[t][j]), 0 for j >= rq  (j < ld_b)

@@ -23,34 +23,6 @@
 
 namespace qlnf4 {
 
-typedef short v4i16_l __attribute__((ext_vector_type(4)));
-typedef short v8i16_l __attribute__((ext_vector_type(8)));
-
-// Rows r0 .. r0+7 of column c0 + li of a row-major bf16 LDS tile (row stride
-// ld elements) as one MFMA operand of lane li of a 16-lane group: two
-// ds_read_b64_tr_b16, each returning four rows of the lane's column.
-__device__ __forceinline__ bf16x8_t lds_col8(const uint16_t* tile, int ld, int r0, int c0, int li) {
-    const uint16_t* base = tile + (r0 + (li >> 2)) * ld + c0 + 4 * (li & 3);
-    // address-space casts (not integer casts) keep the pointer's provenance,
-    // so the compiler can tell these reads from direct-to-LDS loads elsewhere
-    const v4i16_l lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_l*)(base));
-    const v4i16_l hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_l*)(base + 4 * ld));
-    const v8i16_l v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// rowp[c .. c+8), zero for columns >= n (rows of n bf16 values).
-__device__ __forceinline__ uint4 load_cols8(const uint16_t* rowp, int c, int n) {
-    if ((n & 7) == 0) return c < n ? *reinterpret_cast<const uint4*>(rowp + c) : make_uint4(0, 0, 0, 0);
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (c + e < n) ? rowp[c + e] : 0u;
-    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-}
-
-__device__ __forceinline__ uint16_t to_bf16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
-
 // ===========================================================================
 // Projection: V[t][j] = sum_k P[t][k] Q[j][k], j < rq <= 128.
 // Q is either rows of the reduction (A [r, K]: Q[j][k] = A[j][k]) or its

@@ -165,6 +165,27 @@ int nf4_double_quant(const float* absmax, int64_t n1, int32_t dq_blocksize, uint
 int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* stream);
 
 /*
+ * qlora_merge — fold the trained adapter into a 16-bit copy of the base
+ * weight ([codex] §3.6: after training the product of the two adapter
+ * matrices is added to the base weight, so inference needs no adapter branch;
+ * [aivaro] §7 step 5: adapters merged with the 4-bit model for inference;
+ * [tqpw] "Introduction": the adapter weights are 16-bit, so the merged weight
+ * is a 16-bit one). The quantized weight is left unchanged.
+ *
+ *   A    [r, K] bf16 row-major      B  [N, r] bf16 row-major
+ *   out  [N, K] bf16 row-major (caller-owned, 16-B aligned):
+ *        out[n][k] = bf16(fl32(w'[n][k] + scale * D[n][k])),  D = B A
+ *   w' = fl32(NF4[code] * a') as in nf4_dequantize; D is accumulated in fp32
+ *   (order unspecified); the sum takes one fused multiply-add in fp32 and
+ *   bf16 rounding is to nearest even. With r == 0, A and B are not read and
+ *   out is exactly nf4_dequantize's bf16 output.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (K % 64 != 0, N % 8 != 0, r < 0 or
+ * r > QL_MAX_RANK), QL_ERR_UNSUPPORTED, QL_ERR_ALIGN, QL_ERR_HIP.
+ */
+int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                uint16_t* out, void* stream);
+
+/*
  * qlora_linear_fwd — forward of the frozen-base LoRA linear layer ([apxml]:
  * h = dequant(W_NF4) x + B A x; [aivaro] §2: B in R^{d x r}, A in R^{r x k};
  * the scale s = alpha / r is the LoRA scaling factor).
@@ -231,7 +252,8 @@ const char* qlora_last_error(void);
 #define QL_KERNEL_GEMM_FWD 5
 #define QL_KERNEL_GEMM_DX 6
 #define QL_KERNEL_LORA_GRAD 7
-#define QL_KERNEL_COUNT 8
+#define QL_KERNEL_MERGE 8
+#define QL_KERNEL_COUNT 9
 int qlora_timer_arm(int kernel_id);
 int qlora_timer_read(int kernel_id, int64_t* launches, double* total_ms);
 int qlora_timer_disarm(int kernel_id);

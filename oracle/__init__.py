@@ -12,13 +12,13 @@ Sources (web pages on QLoRA; cited by title and section):
   * aivaro.ru "Как работает QLoRA (Quantized LoRA) для training?", §2, §5, §7
   * apxml.com "量化 LoRA (QLoRA) 与 4 位训练" (the h = dequant(W_NF4)x + BAx
     equation and the four configuration knobs)
-  * ai-reference-codex "QLoRA 与 PEFT 全家", §3.1-§3.3
+  * ai-reference-codex "QLoRA 与 PEFT 全家", §3.1-§3.3 and §3.6 (merge)
 
 Precision: the quantization steps take their integer decisions (codes) in
 fp32, as the kernels do; sums that set a bit-exact value (the mean of the
 absmax constants) are fp64; the forward and backward matmuls are fp64.
 
-Readings the pages leave open (each is listed in the design doc): the outermost
+Readings the pages leave open: the outermost
 quantile probability of the NF4 construction, the tie rule at a code
 midpoint (lower index), the nibble order (first element in the high
 nibble), the 8-bit format of the second-level constants (OCP E4M3FN, round to
@@ -50,4 +50,4 @@ from .nf4 import (  # noqa: F401
     dequantize,
     dq_bits_per_param,
 )
-from .linear import lora_forward, lora_backward  # noqa: F401
+from .linear import lora_forward, lora_backward, lora_merge  # noqa: F401

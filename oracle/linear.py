@@ -17,6 +17,8 @@ equations omit it). aivaro.ru §7: gradients flow through the dequantized
 
 import numpy as np
 
+from .nf4 import f32_to_bf16_bits
+
 
 def _f64(a):
     return np.asarray(a, dtype=np.float64)
@@ -47,3 +49,18 @@ def lora_backward(X, dY, Wd, A, B, scale):
     dA = G.T @ X
     dB = s * (dY.T @ U)
     return dX, dA, dB, G, U
+
+
+def lora_merge(Wd, A, B, scale):
+    """Merged 16-bit weight after training (ai-reference-codex "QLoRA 与 PEFT
+    全家", §3.6: the adapter product is added back into the base weight, so
+    inference needs no adapter branch; aivaro.ru §7, step 5; tqpw.cn notes,
+    "Introduction": the adapters are 16-bit and cannot be folded into the
+    4-bit weight, so the merged weight is 16-bit).
+
+    Wd is the dequantized base w' as fp32 values [N, K] (before its bf16
+    rounding), A [r, K], B [N, r]. Returns bf16 bit patterns of
+    bf16(fl32(w' + s B A)), the product and the sum taken in fp64."""
+    Wd, A, B = _f64(Wd), _f64(A), _f64(B)
+    merged = Wd + float(scale) * (B @ A)
+    return f32_to_bf16_bits(merged.astype(np.float32))

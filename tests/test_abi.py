@@ -163,6 +163,22 @@ def test_linear_bwd_rejects(lib):
     assert call(dX=None, dA=None, dB=None) == L.QL_OK  # nothing requested
 
 
+def test_merge_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    def call(w=None, A=P2, B=P3, r=8, out=P):
+        return lib.qlora_merge(w if w is not None else _weight(L), A, B, r, 0.5, out, None)
+
+    assert call(w=_weight(L, cols=96)) == L.QL_ERR_SHAPE  # K % 64
+    assert call(w=_weight(L, rows=100)) == L.QL_ERR_SHAPE  # N % 8
+    assert call(r=129) == L.QL_ERR_SHAPE
+    assert call(r=-1) == L.QL_ERR_SHAPE
+    assert call(A=None) == L.QL_ERR_NULL
+    assert call(B=MIS) == L.QL_ERR_ALIGN
+    assert call(out=None) == L.QL_ERR_NULL
+    assert call(w=_weight(L, c8=None)) == L.QL_ERR_NULL
+
+
 def test_timer_ids(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 

@@ -126,3 +126,65 @@ def test_quantized_all_zero_weight_gives_zero_base():
     assert np.all(ar == 0)
     wd = oracle.dequantize(packed, ar, w.size, out="f32")
     assert np.all(wd == 0)
+
+
+# ---- adapter merge ---------------------------------------------------------
+
+
+def _bf16_bits_torch(v):
+    """Independent bf16 rounding (torch's fp32 -> bf16 cast, nearest even)."""
+    t = torch.tensor(np.asarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_merge_matches_brute_force_loops():
+    _, W, A, B, _ = _case(N=5, K=7, r=3, seed=7)
+    W = W.astype(np.float32)
+    s = 1.5
+    got = oracle.lora_merge(W, A, B, s)
+    N, K = W.shape
+    want = np.empty((N, K), dtype=np.float32)
+    for n in range(N):
+        for k in range(K):
+            d = 0.0
+            for j in range(B.shape[1]):
+                d += B[n, j] * A[j, k]
+            want[n, k] = np.float32(float(W[n, k]) + s * d)
+    assert np.array_equal(got, _bf16_bits_torch(want))
+
+
+def test_merge_rank_one_zero_base_is_scaled_outer_product():
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal(9)
+    b = rng.standard_normal(4)
+    s = 0.25
+    got = oracle.lora_merge(np.zeros((4, 9), dtype=np.float32), a[None, :], b[:, None], s)
+    assert np.array_equal(got, _bf16_bits_torch(s * np.multiply.outer(b, a)))
+
+
+def test_merge_without_adapter_is_the_bf16_dequant():
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((8, 128)) * 0.05).astype(np.float32)
+    packed, a = oracle.quantize(w)
+    c8, S, mu = oracle.double_quant(a)
+    ar = oracle.dequant_absmax(c8, S, mu)
+    wd = oracle.dequantize(packed, ar, w.size, out="f32").reshape(8, 128)
+    bits = oracle.dequantize(packed, ar, w.size, out="bf16").reshape(8, 128)
+    A = rng.standard_normal((4, 128))
+    assert np.array_equal(oracle.lora_merge(wd, A, np.zeros((8, 4)), 2.0), bits)
+    assert np.array_equal(oracle.lora_merge(wd, np.zeros((4, 128)), rng.standard_normal((8, 4)), 2.0), bits)
+
+
+def test_merged_weight_reproduces_the_adapter_branch():
+    # the point of merging: X M^T equals X W'^T + s (X A^T) B^T up to the one
+    # bf16 rounding of M (relative 2^-9 per element)
+    X, W, A, B, _ = _case(T=6, N=11, K=24, r=4, seed=10)
+    s = 3.0
+    M = oracle.bf16_bits_to_f32(oracle.lora_merge(W.astype(np.float32), A, B, s)).astype(np.float64)
+    H, _ = oracle.lora_forward(X, W.astype(np.float32), A, B, s)
+    exact = W.astype(np.float32).astype(np.float64) + s * (B @ A)
+    bound = np.abs(X) @ (np.abs(exact) * 2.0 ** -8).T + 1e-12
+    assert np.all(np.abs(X @ M.T - H) <= bound)
+    # a dropped scale would be far outside the bound
+    M1 = oracle.bf16_bits_to_f32(oracle.lora_merge(W.astype(np.float32), A, B, 1.0)).astype(np.float64)
+    assert not np.all(np.abs(X @ M1.T - H) <= bound)
