@@ -165,11 +165,16 @@ def nf4_codes(w, absmax, blocksize=BLOCKSIZE, table=NF4_PRINTED):
 
     Readings: the normalisation is x = fl32(w * fl32(1/absmax)); a tie
     between two nearest values goes to the lower code; a block whose absmax
-    is 0 gets code 7 (the value 0) throughout.
+    is 0 gets code 7 (the value 0) throughout. "Nearest, ties to the lower
+    code" is decided exactly as "code = number of midpoints below x": the
+    midpoint of two neighbouring fp32 table values is exact in fp64, and so
+    is the comparison with the fp32 x (a distance argmin in fp64 cannot
+    resolve an x within 1e-17 of a midpoint at zero, as the uniform grid has).
     """
     w = np.asarray(w, dtype=np.float32).ravel()
     absmax = np.asarray(absmax, dtype=np.float32)
     t64 = np.asarray(table, dtype=np.float32).astype(np.float64)
+    mids = (t64[:-1] + t64[1:]) * 0.5  # ascending, exact
     codes = np.empty(w.size, dtype=np.uint8)
     for s in range(0, w.size, _CHUNK):
         ww = w[s : s + _CHUNK]
@@ -178,8 +183,8 @@ def nf4_codes(w, absmax, blocksize=BLOCKSIZE, table=NF4_PRINTED):
             inv = np.float32(1.0) / a
             x = ww * inv
         x = np.where(a == 0, np.float32(0.0), x).astype(np.float32)
-        dist = np.abs(x.astype(np.float64)[:, None] - t64[None, :])
-        codes[s : s + ww.size] = np.argmin(dist, axis=1)  # first minimum: lower code on a tie
+        # number of midpoints strictly below x (x on a midpoint: the lower code)
+        codes[s : s + ww.size] = np.searchsorted(mids, x.astype(np.float64), side="left")
     return codes
 
 
