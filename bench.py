@@ -220,6 +220,9 @@ def measure_rows(torch, qn, inp, flush):
     # adapter merge of the same weight: codes and constants in, bf16 out, A and B read once
     sec = timed(8, lambda: qn.qlora_merge(w, m["A"], m["B"], m["s"]))
     rows["merge_r%d_11008x4096" % r] = _hbm_row(BPW_DEQUANT * N * K + 2 * r * (N + K), sec)
+    # quantization-error measurement on the uniform grid, fp32 weight read once
+    sec = timed(9, lambda: qn.q4_quant_error(m["W"], "uniform"))
+    rows["quant_error_uniform_f32_11008x4096"] = _hbm_row(4 * N * K, sec)
     # dispatch floor: the same HIP-event timing around a kernel that does
     # nothing measurable (a one-element fill), cold cache as above
     tiny = torch.empty(1, device="cuda")
@@ -485,6 +488,68 @@ def run_suite(torch, qn):
         "nf4_fused_us": round(s_nf4 * 1e6, 1), "nf4_fused_TFLOP/s": round(fl / s_nf4 / 1e12, 1),
         "torch_matmul_bf16_us": round(s_mm * 1e6, 1), "torch_matmul_TFLOP/s": round(fl / s_mm / 1e12, 1),
         "nf4_over_bf16_time": round(s_nf4 / s_mm, 3)}
+    del w, Wd, X
+    torch.cuda.empty_cache()
+
+    # (7) NF4 against the uniform 4-bit grid: quantization error (sum of
+    # squares relative to sum w^2, max |w - w'|) of 11008 x 4096 weights with
+    # normal, Student-t (3 degrees of freedom) and outlier entries, and the
+    # error kernel's throughput (cold cache, library timer)
+    print("suite: NF4 vs uniform 4-bit error", file=sys.stderr, flush=True)
+    import workloads
+
+    flush = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
+    dists = {
+        "normal_sd0.02": lambda: workloads.normal_weight(n, k, 0.02, seed=1),
+        "student_t3_scale0.02": lambda: workloads.student_t_weight(n, k, 3.0, 0.02, seed=2),
+        "normal_sd0.02_outliers_1e-3_x20": lambda: workloads.normal_weight(n, k, 0.02, seed=3, outlier_frac=1e-3,
+                                                                          outlier_scale=20.0),
+    }
+    qe = {}
+    for name, make in dists.items():
+        W = make().cuda()
+        row = {}
+        for grid in ("nf4", "uniform"):
+            tmr = qn.KernelTimer(9)
+            qn.q4_quant_error(W, grid)
+            torch.cuda.synchronize()
+            tmr.arm()
+            for _ in range(5):
+                flush.fill_(1)
+                st = qn.q4_quant_error(W, grid)
+            cnt, ms = tmr.read()
+            tmr.disarm()
+            sse, ssw, mx = st.cpu().tolist()
+            sec = ms / cnt / 1e3
+            row[grid] = {"rel_mse": sse / ssw, "max_abs_err": mx, "kernel_us": round(sec * 1e6, 2),
+                         "GB/s": round(4 * n * k / sec / 1e9, 1)}
+        row["uniform_over_nf4_mse"] = round(row["uniform"]["rel_mse"] / row["nf4"]["rel_mse"], 4)
+        qe[name] = row
+        del W
+    res["q4_error_nf4_vs_uniform_11008x4096_f32"] = qe
+
+    # (8) adapter merge of a 7B MLP weight at ranks 16, 64 and 128 (cold cache)
+    print("suite: adapter merge", file=sys.stderr, flush=True)
+    w = qn.quantize_weight(dev_randn((n, k), 0.02, 9100))
+    out = torch.empty(n, k, dtype=torch.bfloat16, device="cuda")
+    mg = {}
+    for r in (16, 64, 128):
+        A = dev_randn((r, k), 1.0 / k, 9101 + r, torch.bfloat16)
+        B = dev_randn((n, r), 0.01, 9201 + r, torch.bfloat16)
+        tmr = qn.KernelTimer(8)
+        qn.qlora_merge(w, A, B, 2.0, out=out)
+        torch.cuda.synchronize()
+        tmr.arm()
+        for _ in range(5):
+            flush.fill_(1)
+            qn.qlora_merge(w, A, B, 2.0, out=out)
+        cnt, ms = tmr.read()
+        tmr.disarm()
+        sec = ms / cnt / 1e3
+        nbytes = BPW_DEQUANT * n * k + 2 * r * (n + k)
+        mg["r%d" % r] = {"us": round(sec * 1e6, 2), "GB/s": round(nbytes / sec / 1e9, 1),
+                         "frac": round(nbytes / sec / PEAK_HBM, 4)}
+    res["merge_11008x4096"] = mg
     return res
 
 def main():

@@ -23,6 +23,7 @@ __all__ = [
     "nf4_double_quant",
     "nf4_dequantize",
     "qlora_merge",
+    "q4_quant_error",
     "qlora_linear_fwd",
     "qlora_linear_bwd",
     "quantize_weight",
@@ -167,6 +168,21 @@ def qlora_merge(w, A=None, B=None, scale=1.0, out=None):
     d = w.descriptor()
     _check(lib.qlora_merge(ctypes.byref(d), _ptr(_bits(A)), _ptr(_bits(B)), r, float(scale), _ptr(out), _stream()))
     return out
+
+
+def q4_quant_error(W, grid="nf4", stats=None):
+    """Blockwise-absmax 4-bit quantization error of W (fp32 or bf16, 2-D) on
+    the NF4 or the uniform grid: fp64 device tensor [sum (w-w')^2, sum w^2,
+    max |w-w'|]."""
+    dt = {torch.float32: _lib.QL_F32, torch.bfloat16: _lib.QL_BF16}[W.dtype]
+    g = {"nf4": _lib.QL_GRID_NF4, "uniform": _lib.QL_GRID_UNIFORM}[grid]
+    assert W.is_contiguous()
+    rows, cols = (W.shape[0], W.numel() // W.shape[0]) if W.dim() >= 1 and W.shape[0] > 0 else (0, 0)
+    if stats is None:
+        stats = torch.empty(3, dtype=torch.float64, device=W.device)
+    ws, wsb = _workspace(lib.q4_quant_error_workspace(rows, cols, dt), W.device)
+    _check(lib.q4_quant_error(_ptr(W), dt, rows, cols, BLOCKSIZE, g, _ptr(stats), _ptr(ws), wsb, _stream()))
+    return stats
 
 
 def qlora_linear_fwd(w, X, A=None, B=None, scale=1.0, save_u=True, out=None):

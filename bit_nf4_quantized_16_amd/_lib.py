@@ -29,6 +29,9 @@ QL_KERNEL_GEMM_FWD = 5
 QL_KERNEL_GEMM_DX = 6
 QL_KERNEL_LORA_GRAD = 7
 QL_KERNEL_MERGE = 8
+QL_KERNEL_QERROR = 9
+QL_GRID_NF4 = 0
+QL_GRID_UNIFORM = 1
 
 
 class QlNf4Weight(ctypes.Structure):
@@ -63,6 +66,8 @@ SIGNATURES = {
     "nf4_double_quant": (_I, [_P, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nf4_dequantize": (_I, [_WP, _P, _I, _P]),
     "qlora_merge": (_I, [_WP, _P, _P, _I32, _F, _P, _P]),
+    "q4_quant_error_workspace": (_SZ, [_I64, _I64, _I]),
+    "q4_quant_error": (_I, [_P, _I, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),

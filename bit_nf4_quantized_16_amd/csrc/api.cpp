@@ -266,6 +266,32 @@ int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* strea
     return launch_dequantize(*w, out, out_dtype == QL_BF16, static_cast<hipStream_t>(stream));
 }
 
+size_t q4_quant_error_workspace(int64_t rows, int64_t cols, int w_dtype) {
+    if (rows <= 0 || cols <= 0 || (w_dtype != QL_F32 && w_dtype != QL_BF16)) return 0;
+    return q4_error_ws_bytes(w_dtype == QL_BF16, rows * cols);
+}
+
+int q4_quant_error(const void* W, int w_dtype, int64_t rows, int64_t cols, int32_t blocksize, int32_t grid,
+                   double* stats, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows <= 0 || cols <= 0)
+        return set_error(QL_ERR_SHAPE, "shape %lld x %lld", (long long)rows, (long long)cols);
+    if (blocksize != QL_NF4_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "blocksize %d (only 64 is offered)", blocksize);
+    if (w_dtype != QL_F32 && w_dtype != QL_BF16) return set_error(QL_ERR_UNSUPPORTED, "input dtype %d", w_dtype);
+    if (grid != QL_GRID_NF4 && grid != QL_GRID_UNIFORM) return set_error(QL_ERR_UNSUPPORTED, "grid %d", grid);
+    int s;
+    if ((s = check_ptr(W, "W")) != QL_OK) return s;
+    if ((s = check_ptr(stats, "stats")) != QL_OK) return s;
+    const size_t need = q4_error_ws_bytes(w_dtype == QL_BF16, rows * cols);
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes, need);
+        if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    return launch_q4_error(W, w_dtype == QL_BF16, rows * cols, grid, stats, ws, static_cast<hipStream_t>(stream));
+}
+
 int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, int32_t r, float scale, uint16_t* out,
                 void* stream) {
     g_last_error[0] = '\0';

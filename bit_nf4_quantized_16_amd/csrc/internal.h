@@ -27,6 +27,10 @@ int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStrea
 
 // Adapter merge: out[n][k] = bf16(fl32(w'[n][k] + scale sum_j B[n][j] A[j][k]))
 // for 1 <= r <= QL_MAX_RANK, K % 64 == 0. Dynamic LDS merge_lds_bytes(r).
+// Quantization error on a 4-bit grid (QL_GRID_*): fp64 partials in ws.
+size_t q4_error_ws_bytes(bool bf16, int64_t n);
+int launch_q4_error(const void* W, bool bf16, int64_t n, int grid, double* stats, void* ws, hipStream_t stream);
+
 size_t merge_lds_bytes(int r);
 int launch_merge(const NF4Dev& w, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int r, float scale,
                  uint16_t* out, hipStream_t stream);

@@ -165,6 +165,33 @@ int nf4_double_quant(const float* absmax, int64_t n1, int32_t dq_blocksize, uint
 int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* stream);
 
 /*
+ * q4_quant_error — error of blockwise-absmax 4-bit quantization of a weight
+ * on one of two sixteen-value grids, measured in one pass ([codex] §3.2: the
+ * naive grid spaces sixteen values equally, NF4 by the normal density, and
+ * NF4 distorts less; §5: its edge shrinks for non-normal weights; the page
+ * gives no figures).
+ *
+ *   W      [rows, cols] row-major, fp32 (w_dtype QL_F32) or bf16 (QL_BF16)
+ *   grid   QL_GRID_NF4 (the NF4 table) or QL_GRID_UNIFORM (fl32(-1 + 2i/15),
+ *          i = 0..15)
+ *   stats  device, 3 fp64: sum (w - w')^2, sum w^2, max |w - w'|
+ *   ws     workspace of q4_quant_error_workspace(rows, cols, w_dtype) bytes,
+ *          16-B aligned (may be NULL when that is 0)
+ *
+ * Per block of 64 consecutive elements (a shorter last block): a = max |w|,
+ * x = fl32(w * fl32(1/a)), c = the nearest grid value with ties to the lower
+ * code (for NF4 the code nf4_quantize writes), w' = fl32(T[c] * a). The sums
+ * are fp64 in an order fixed by the size, so equal inputs give equal bits.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (rows or cols <= 0), QL_ERR_UNSUPPORTED
+ * (blocksize != 64, dtype, grid), QL_ERR_ALIGN, QL_ERR_WORKSPACE, QL_ERR_HIP.
+ */
+#define QL_GRID_NF4 0
+#define QL_GRID_UNIFORM 1
+size_t q4_quant_error_workspace(int64_t rows, int64_t cols, int w_dtype);
+int q4_quant_error(const void* W, int w_dtype, int64_t rows, int64_t cols, int32_t blocksize, int32_t grid,
+                   double* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qlora_merge — fold the trained adapter into a 16-bit copy of the base
  * weight ([codex] §3.6: after training the product of the two adapter
  * matrices is added to the base weight, so inference needs no adapter branch;
@@ -253,7 +280,8 @@ const char* qlora_last_error(void);
 #define QL_KERNEL_GEMM_DX 6
 #define QL_KERNEL_LORA_GRAD 7
 #define QL_KERNEL_MERGE 8
-#define QL_KERNEL_COUNT 9
+#define QL_KERNEL_QERROR 9
+#define QL_KERNEL_COUNT 10
 int qlora_timer_arm(int kernel_id);
 int qlora_timer_read(int kernel_id, int64_t* launches, double* total_ms);
 int qlora_timer_disarm(int kernel_id);

@@ -179,6 +179,25 @@ def test_merge_rejects(lib):
     assert call(w=_weight(L, c8=None)) == L.QL_ERR_NULL
 
 
+def test_quant_error_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    need = lib.q4_quant_error_workspace(64, 4096, L.QL_F32)
+    assert need > 0 and lib.q4_quant_error_workspace(0, 4, L.QL_F32) == 0
+
+    def call(W=P, dt=L.QL_F32, rows=64, cols=4096, bs=64, grid=L.QL_GRID_UNIFORM, stats=P2, ws=P3, wsb=need):
+        return lib.q4_quant_error(W, dt, rows, cols, bs, grid, stats, ws, wsb, None)
+
+    assert call(rows=0) == L.QL_ERR_SHAPE
+    assert call(bs=32) == L.QL_ERR_UNSUPPORTED
+    assert call(dt=9) == L.QL_ERR_UNSUPPORTED
+    assert call(grid=2) == L.QL_ERR_UNSUPPORTED
+    assert call(W=None) == L.QL_ERR_NULL
+    assert call(stats=MIS) == L.QL_ERR_ALIGN
+    assert call(wsb=need - 1) == L.QL_ERR_WORKSPACE
+    assert call(ws=None) == L.QL_ERR_WORKSPACE
+
+
 def test_timer_ids(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 
