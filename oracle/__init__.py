@@ -12,8 +12,9 @@ Sources (web pages on QLoRA; cited by title and section):
   * aivaro.ru "Как работает QLoRA (Quantized LoRA) для training?", §2, §5, §7
   * apxml.com "量化 LoRA (QLoRA) 与 4 位训练" (the h = dequant(W_NF4)x + BAx
     equation and the four configuration knobs)
-  * ai-reference-codex "QLoRA 与 PEFT 全家", §3.1-§3.3, §3.6 (merge), §3.2 and
-    §5 (the uniform 4-bit grid, for the quantization-error comparison)
+  * ai-reference-codex "QLoRA 与 PEFT 全家", §3.1-§3.3, §3.4 (dropout), §3.6
+    (merge), §3.2 and §5 (the uniform 4-bit grid, for the quantization-error
+    comparison)
 
 Precision: the quantization steps take their integer decisions (codes) in
 fp32, as the kernels do; sums that set a bit-exact value (the mean of the
@@ -51,5 +52,5 @@ from .nf4 import (  # noqa: F401
     dequantize,
     dq_bits_per_param,
 )
-from .linear import lora_forward, lora_backward, lora_merge  # noqa: F401
+from .linear import lora_forward, lora_backward, lora_merge, lora_forward_dropout, lora_backward_dropout  # noqa: F401
 from .q4error import UNIFORM4, GRIDS, quantize_dequantize, quant_error  # noqa: F401

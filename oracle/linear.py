@@ -64,3 +64,42 @@ def lora_merge(Wd, A, B, scale):
     Wd, A, B = _f64(Wd), _f64(A), _f64(B)
     merged = Wd + float(scale) * (B @ A)
     return f32_to_bf16_bits(merged.astype(np.float32))
+
+
+def lora_forward_dropout(X, Wd, A, B, scale, keep, p):
+    """Forward with dropout on the adapter input (ai-reference-codex "QLoRA 与
+    PEFT 全家", §3.4: dropout, 0.05-0.1 on the adapters for small data;
+    aivaro.ru §11: lora_dropout = 0.05). Reading: inverted dropout of the
+    adapter branch's input only, the keep mask ``keep`` [T, K] (0/1) given:
+
+        U = X_d A^T / (1 - p),  X_d = X * keep
+        H = X W'^T + s U B^T
+
+    Returns (H, U) in fp64."""
+    X, Wd, A, B, keep = _f64(X), _f64(Wd), _f64(A), _f64(B), _f64(keep)
+    c = 1.0 / (1.0 - float(p))
+    U = c * ((X * keep) @ A.T)
+    H = X @ Wd.T + float(scale) * (U @ B.T)
+    return H, U
+
+
+def lora_backward_dropout(X, dY, Wd, A, B, scale, keep, p):
+    """Backward of :func:`lora_forward_dropout` (fp64): the dropout's
+    derivative passes the kept entries scaled by 1/(1 - p).
+
+        G  = s dY B
+        dX = dY W' + (G A) * keep / (1 - p)
+        dA = G^T X_d / (1 - p)
+        dB = s dY^T U
+
+    Returns (dX, dA, dB, G, U)."""
+    X, dY, Wd, A, B, keep = _f64(X), _f64(dY), _f64(Wd), _f64(A), _f64(B), _f64(keep)
+    s = float(scale)
+    c = 1.0 / (1.0 - float(p))
+    Xd = X * keep
+    U = c * (Xd @ A.T)
+    G = s * (dY @ B)
+    dX = dY @ Wd + c * ((G @ A) * keep)
+    dA = c * (G.T @ Xd)
+    dB = s * (dY.T @ U)
+    return dX, dA, dB, G, U

@@ -188,3 +188,68 @@ def test_merged_weight_reproduces_the_adapter_branch():
     # a dropped scale would be far outside the bound
     M1 = oracle.bf16_bits_to_f32(oracle.lora_merge(W.astype(np.float32), A, B, 1.0)).astype(np.float64)
     assert not np.all(np.abs(X @ M1.T - H) <= bound)
+
+
+# ---- dropout on the adapter input --------------------------------------------
+
+
+def test_dropout_with_everything_kept_and_p0_is_the_plain_layer():
+    X, W, A, B, dY = _case(T=4, N=6, K=16, r=3, seed=11)
+    keep = np.ones_like(X)
+    H0, U0 = oracle.lora_forward(X, W, A, B, 1.5)
+    H1, U1 = oracle.lora_forward_dropout(X, W, A, B, 1.5, keep, 0.0)
+    assert np.array_equal(H0, H1) and np.array_equal(U0, U1)
+    for a, b in zip(oracle.lora_backward(X, dY, W, A, B, 1.5), oracle.lora_backward_dropout(X, dY, W, A, B, 1.5, keep, 0.0)):
+        assert np.array_equal(a, b)
+
+
+def test_dropout_backward_matches_autograd_fp64():
+    X, W, A, B, dY = _case(T=5, N=7, K=24, r=3, seed=12)
+    rng = np.random.default_rng(13)
+    keep = (rng.random(X.shape) >= 0.3).astype(np.float64)
+    p, s = 0.3, 2.0
+    tX = torch.tensor(X, dtype=torch.float64, requires_grad=True)
+    tA = torch.tensor(A, dtype=torch.float64, requires_grad=True)
+    tB = torch.tensor(B, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64)
+    tk = torch.tensor(keep)
+    H = tX @ tW.T + s * (((tX * tk) / (1 - p)) @ tA.T) @ tB.T
+    H.backward(torch.tensor(dY, dtype=torch.float64))
+    Href, _ = oracle.lora_forward_dropout(X, W, A, B, s, keep, p)
+    dX, dA, dB, _, _ = oracle.lora_backward_dropout(X, dY, W, A, B, s, keep, p)
+    assert np.allclose(Href, H.detach().numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dX, tX.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dA, tA.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dB, tB.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_dropout_forward_matches_brute_force_loops():
+    X, W, A, B, _ = _case(T=2, N=3, K=8, r=2, seed=14)
+    keep = np.array([[1, 0, 1, 1, 0, 1, 1, 1], [0, 0, 1, 0, 1, 1, 0, 1]], dtype=np.float64)
+    p, s = 0.25, 3.0
+    H, U = oracle.lora_forward_dropout(X, W, A, B, s, keep, p)
+    for t in range(2):
+        for j in range(2):
+            u = sum(X[t, k] * keep[t, k] * A[j, k] for k in range(8)) / (1 - p)
+            assert abs(u - U[t, j]) < 1e-12
+        for n in range(3):
+            h = sum(X[t, k] * W[n, k] for k in range(8)) + s * sum(U[t, j] * B[n, j] for j in range(2))
+            assert abs(h - H[t, n]) < 1e-12
+
+
+def test_dropout_with_nothing_kept_leaves_only_the_base():
+    X, W, A, B, dY = _case(T=3, N=5, K=8, r=2, seed=15)
+    keep = np.zeros_like(X)
+    H, U = oracle.lora_forward_dropout(X, W, A, B, 2.0, keep, 0.5)
+    assert np.all(U == 0) and np.array_equal(H, X @ W.T)
+    dX, dA, dB, _, _ = oracle.lora_backward_dropout(X, dY, W, A, B, 2.0, keep, 0.5)
+    assert np.all(dA == 0) and np.all(dB == 0) and np.array_equal(dX, dY @ W)
+
+
+def test_keep_bit_packing_layout():
+    import workloads
+
+    keep = torch.zeros(2, 16, dtype=torch.bool)
+    keep[0, 0] = keep[0, 9] = keep[1, 7] = keep[1, 15] = True
+    bits = workloads.pack_keep_bits(keep)
+    assert bits.tolist() == [[1, 2], [128, 128]]

@@ -43,6 +43,22 @@ def student_t_weight(rows, cols, df, scale, seed):
     return (z / torch.sqrt(v / df) * scale).to(torch.float32)
 
 
+def keep_mask(rows, cols, p, seed):
+    """bool [rows, cols]: each entry kept (True) with probability 1 - p (the
+    dropout draws, made here and passed to both sides as an input)."""
+    g = _gen(seed)
+    return torch.rand(rows, cols, generator=g) >= p
+
+
+def pack_keep_bits(keep):
+    """bool [T, K] (K a multiple of 8) -> uint8 [T, K / 8], element 8i + j of a
+    row in bit j (least significant first) of byte i: the layout the library
+    takes the keep mask in."""
+    k = keep.to(torch.uint8).reshape(keep.shape[0], -1, 8)
+    weights = torch.tensor([1, 2, 4, 8, 16, 32, 64, 128], dtype=torch.int32)
+    return (k.to(torch.int32) * weights).sum(dim=2).to(torch.uint8).contiguous()
+
+
 def bf16_normal(shape, std, seed):
     """bf16 tensor ~ N(0, std) (drawn in fp32, rounded by torch's cast)."""
     g = _gen(seed)
