@@ -220,6 +220,17 @@ def measure_rows(torch, qn, inp, flush):
     # adapter merge of the same weight: codes and constants in, bf16 out, A and B read once
     sec = timed(8, lambda: qn.qlora_merge(w, m["A"], m["B"], m["s"]))
     rows["merge_r%d_11008x4096" % r] = _hbm_row(BPW_DEQUANT * N * K + 2 * r * (N + K), sec)
+    # dropout (p = 0.05) on the adapter input of the same layer: the masking
+    # pass (X and the keep bits in, X * keep out) and the masked adapter term
+    # of dX (dX, G, the bits in, dX out; A is L2-resident)
+    import workloads
+
+    bits = workloads.pack_keep_bits(workloads.keep_mask(T, K, 0.05, 31)).cuda()
+    sec = timed(10, lambda: qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"], keep=bits, p=0.05))
+    rows["dropout_keep_apply_T1024_K4096"] = _hbm_row(T * K * (2 + 2 + 1 / 8), sec)
+    sec = timed(11, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_da=False,
+                                               need_db=False, keep=bits, p=0.05))
+    rows["dropout_dx_term_T1024_K4096"] = _hbm_row(T * K * (2 + 2 + 1 / 8) + 2 * T * 64 + 2 * r * K, sec)
     # quantization-error measurement on the uniform grid, fp32 weight read once
     sec = timed(9, lambda: qn.q4_quant_error(m["W"], "uniform"))
     rows["quant_error_uniform_f32_11008x4096"] = _hbm_row(4 * N * K, sec)
@@ -550,6 +561,24 @@ def run_suite(torch, qn):
         mg["r%d" % r] = {"us": round(sec * 1e6, 2), "GB/s": round(nbytes / sec / 1e9, 1),
                          "frac": round(nbytes / sec / PEAK_HBM, 4)}
     res["merge_11008x4096"] = mg
+
+    # (9) dropout (p = 0.05, r = 16) on the 7B gate projection at T = 1024:
+    # forward and backward time with and without it (warm)
+    print("suite: dropout", file=sys.stderr, flush=True)
+    T, r = 1024, 16
+    X = dev_randn((T, k), 1.0, 9301, torch.bfloat16)
+    dY = dev_randn((T, n), 1.0, 9302, torch.bfloat16)
+    A = dev_randn((r, k), 1.0 / k, 9303, torch.bfloat16)
+    B = dev_randn((n, r), 0.01, 9304, torch.bfloat16)
+    bits = workloads.pack_keep_bits(workloads.keep_mask(T, k, 0.05, 9305)).cuda()
+    _, U = qn.qlora_linear_fwd(w, X, A, B, 2.0)
+    _, Ud = qn.qlora_linear_fwd(w, X, A, B, 2.0, keep=bits, p=0.05)
+    res["dropout_11008x4096_T1024_r16_p0.05"] = {
+        "fwd_us": round(timed(lambda: qn.qlora_linear_fwd(w, X, A, B, 2.0), reps=11) * 1e6, 1),
+        "fwd_dropout_us": round(timed(lambda: qn.qlora_linear_fwd(w, X, A, B, 2.0, keep=bits, p=0.05), reps=11) * 1e6, 1),
+        "bwd_us": round(timed(lambda: qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U), reps=11) * 1e6, 1),
+        "bwd_dropout_us": round(timed(lambda: qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=Ud, keep=bits, p=0.05),
+                                      reps=11) * 1e6, 1)}
     return res
 
 def main():

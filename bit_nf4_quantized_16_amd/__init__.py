@@ -185,25 +185,42 @@ def q4_quant_error(W, grid="nf4", stats=None):
     return stats
 
 
-def qlora_linear_fwd(w, X, A=None, B=None, scale=1.0, save_u=True, out=None):
-    """Y = X W'^T + scale (X A^T) B^T. Returns (Y bf16 [T, N], U fp32 [T, r] or None)."""
+def _keep(keep, T, K):
+    assert keep.dtype == torch.uint8 and keep.is_contiguous() and keep.numel() == T * (K // 8), \
+        "keep: bit-packed uint8 [T, K/8]"
+    return keep
+
+
+def qlora_linear_fwd(w, X, A=None, B=None, scale=1.0, save_u=True, out=None, keep=None, p=0.0):
+    """Y = X W'^T + scale (X A^T) B^T. Returns (Y bf16 [T, N], U fp32 [T, r] or None).
+    With ``keep`` (bit-packed uint8 [T, K/8]) and ``p``: dropout on the
+    adapter input, U = (X * keep) A^T / (1 - p)."""
     T = X.shape[0]
     r = 0 if A is None else A.shape[0]
     dev = X.device
     Y = out if out is not None else torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
     U = torch.empty(T, r, dtype=torch.float32, device=dev) if (save_u and r > 0) else None
-    ws, wsb = _workspace(lib.qlora_linear_fwd_workspace(w.rows, w.cols, max(T, 1), r), dev)
     d = w.descriptor()
-    _check(
-        lib.qlora_linear_fwd(ctypes.byref(d), _ptr(_bits(X)), T, _ptr(_bits(A)), _ptr(_bits(B)), r, float(scale),
-                             _ptr(Y), _ptr(U), _ptr(ws), wsb, _stream())
-    )
+    if keep is None:
+        ws, wsb = _workspace(lib.qlora_linear_fwd_workspace(w.rows, w.cols, max(T, 1), r), dev)
+        _check(
+            lib.qlora_linear_fwd(ctypes.byref(d), _ptr(_bits(X)), T, _ptr(_bits(A)), _ptr(_bits(B)), r, float(scale),
+                                 _ptr(Y), _ptr(U), _ptr(ws), wsb, _stream())
+        )
+    else:
+        ws, wsb = _workspace(lib.qlora_linear_fwd_dropout_workspace(w.rows, w.cols, max(T, 1), r), dev)
+        _check(
+            lib.qlora_linear_fwd_dropout(ctypes.byref(d), _ptr(_bits(X)), T, _ptr(_bits(A)), _ptr(_bits(B)), r,
+                                         float(scale), _ptr(_keep(keep, T, w.cols)), float(p), _ptr(Y), _ptr(U),
+                                         _ptr(ws), wsb, _stream())
+        )
     return Y, U
 
 
 def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, need_da=True, need_db=True, dA=None,
-                     dB=None, accumulate=False):
-    """Returns (dX bf16 [T, K] or None, dA fp32 [r, K] or None, dB fp32 [N, r] or None)."""
+                     dB=None, accumulate=False, keep=None, p=0.0):
+    """Returns (dX bf16 [T, K] or None, dA fp32 [r, K] or None, dB fp32 [N, r] or None).
+    ``keep`` / ``p``: the forward's dropout mask and probability."""
     T = dY.shape[0]
     r = 0 if A is None else A.shape[0]
     dev = dY.device
@@ -216,13 +233,22 @@ def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, 
         dA = None
     if not need_db:
         dB = None
-    ws, wsb = _workspace(lib.qlora_linear_bwd_workspace(w.rows, w.cols, max(T, 1), r), dev)
     d = w.descriptor()
-    _check(
-        lib.qlora_linear_bwd(ctypes.byref(d), _ptr(_bits(X)), _ptr(_bits(dY)), T, _ptr(_bits(A)), _ptr(_bits(B)), r,
-                             float(scale), _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), 1 if accumulate else 0, _ptr(ws),
-                             wsb, _stream())
-    )
+    if keep is None:
+        ws, wsb = _workspace(lib.qlora_linear_bwd_workspace(w.rows, w.cols, max(T, 1), r), dev)
+        _check(
+            lib.qlora_linear_bwd(ctypes.byref(d), _ptr(_bits(X)), _ptr(_bits(dY)), T, _ptr(_bits(A)), _ptr(_bits(B)),
+                                 r, float(scale), _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), 1 if accumulate else 0,
+                                 _ptr(ws), wsb, _stream())
+        )
+    else:
+        ws, wsb = _workspace(lib.qlora_linear_bwd_dropout_workspace(w.rows, w.cols, max(T, 1), r), dev)
+        _check(
+            lib.qlora_linear_bwd_dropout(ctypes.byref(d), _ptr(_bits(X)), _ptr(_bits(dY)), T, _ptr(_bits(A)),
+                                         _ptr(_bits(B)), r, float(scale), _ptr(_keep(keep, T, w.cols)), float(p),
+                                         _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), 1 if accumulate else 0, _ptr(ws), wsb,
+                                         _stream())
+        )
     return dX, dA, dB
 
 
@@ -231,19 +257,21 @@ class QLoRALinearFunction(torch.autograd.Function):
     (no gradient), A and B receive fp32 gradients cast to their dtype."""
 
     @staticmethod
-    def forward(ctx, X, A, B, w, scale):
-        Y, U = qlora_linear_fwd(w, X.contiguous(), A.contiguous(), B.contiguous(), scale, save_u=True)
+    def forward(ctx, X, A, B, w, scale, keep=None, p=0.0):
+        Y, U = qlora_linear_fwd(w, X.contiguous(), A.contiguous(), B.contiguous(), scale, save_u=True, keep=keep, p=p)
         ctx.save_for_backward(X, A, B, U)
         ctx.w = w
         ctx.scale = scale
+        ctx.keep = keep
+        ctx.p = p
         return Y
 
     @staticmethod
     def backward(ctx, dY):
         X, A, B, U = ctx.saved_tensors
         dX, dA, dB = qlora_linear_bwd(ctx.w, X, dY.contiguous().to(torch.bfloat16), A, B, ctx.scale, U=U,
-                                      need_dx=ctx.needs_input_grad[0])
-        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None
+                                      need_dx=ctx.needs_input_grad[0], keep=ctx.keep, p=ctx.p)
+        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None, None
 
 
 class KernelTimer:

@@ -30,6 +30,8 @@ QL_KERNEL_GEMM_DX = 6
 QL_KERNEL_LORA_GRAD = 7
 QL_KERNEL_MERGE = 8
 QL_KERNEL_QERROR = 9
+QL_KERNEL_KEEP_APPLY = 10
+QL_KERNEL_DX_KEEP = 11
 QL_GRID_NF4 = 0
 QL_GRID_UNIFORM = 1
 
@@ -70,8 +72,12 @@ SIGNATURES = {
     "q4_quant_error": (_I, [_P, _I, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_fwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
+    "qlora_linear_fwd_dropout": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_bwd": (_I, [_WP, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
+    "qlora_linear_bwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
+    "qlora_linear_bwd_dropout": (_I, [_WP, _P, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
     "qlora_status_string": (ctypes.c_char_p, [_I]),
     "qlora_last_error": (ctypes.c_char_p, []),
     "qlora_timer_arm": (_I, [_I]),

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora_nf4.so")
 
-SOURCES = ["quantize.hip", "dequant.hip", "gemv.hip", "lora.hip", "gemm_tiles.hip", "merge.hip", "qerror.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "dequant.hip", "gemv.hip", "lora.hip", "gemm_tiles.hip", "merge.hip", "qerror.hip", "dropout.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -137,6 +137,7 @@ int check_linear_shape(const ql_nf4_weight* w, int64_t T, int32_t r) {
 
 // ---- forward workspace -------------------------------------------------
 struct FwdWs {
+    uint16_t* Xd = nullptr;  // bf16 [T, K] = X * keep (dropout only)
     uint16_t* Us = nullptr;  // bf16 [T, rp64] = bf16(s U), GEMM path
     uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
     void* proj = nullptr;    // split partials of the U projection
@@ -146,12 +147,15 @@ struct FwdWs {
 
 constexpr int64_t kGemvMaxT = 16;
 
-FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r) {
+// Dropout (a keep mask) always takes the GEMM path: the GEMV feeds the base
+// and the adapter the same x operands.
+FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool drop = false) {
     Carver c(ws);
     FwdWs f;
     const int rp = rank_pad64(r);
-    if (T > kGemvMaxT) {  // the GEMV path needs no workspace
+    if (T > kGemvMaxT || drop) {  // the GEMV path needs no workspace
         if (r > 0) {
+            if (drop) f.Xd = c.take<uint16_t>(static_cast<size_t>(T) * K);
             f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
             if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
             const size_t pb = lora_proj_ws_bytes(T, r, K, false);
@@ -166,6 +170,7 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r) {
 
 // ---- backward workspace ------------------------------------------------
 struct BwdWs {
+    uint16_t* Xd = nullptr;  // bf16 [T, K] = X * keep (dropout, for dA or a recomputed U)
     uint16_t* Gp = nullptr;  // bf16 [T, rp64] = G = s dY B, dX's LoRA operand
     uint16_t* Gt = nullptr;  // bf16 [rp16, T] = G^T, dA's MFMA operand
     uint16_t* Ut = nullptr;  // bf16 [rp16, T] = U^T, dB's MFMA operand
@@ -175,10 +180,12 @@ struct BwdWs {
     size_t bytes = 0;
 };
 
-BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db) {
+BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_dx, bool want_da, bool want_db,
+                bool drop = false) {
     Carver c(ws);
     BwdWs b;
     if (r > 0) {
+        if (drop && (want_da || want_db)) b.Xd = c.take<uint16_t>(static_cast<size_t>(T) * K);
         const int rp = rank_pad64(r);
         const int rp16 = lora_grad_rp(r);
         if (want_dx) b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
@@ -311,12 +318,31 @@ size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t
     return carve_fwd(nullptr, rows, cols, T, r).bytes;
 }
 
-int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A, const uint16_t* B,
-                     int32_t r, float scale, uint16_t* Y, float* U_out, void* ws, size_t ws_bytes, void* stream) {
+size_t qlora_linear_fwd_dropout_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    return carve_fwd(nullptr, rows, cols, T, r, true).bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_dropout(const uint8_t* keep, float p) {
+    int s;
+    if ((s = check_ptr(keep, "keep")) != QL_OK) return s;
+    if (!(p >= 0.0f && p < 1.0f)) return set_error(QL_ERR_UNSUPPORTED, "dropout p = %g (0 <= p < 1)", (double)p);
+    return QL_OK;
+}
+
+int linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A, const uint16_t* B, int32_t r,
+               float scale, const uint8_t* keep, float p, uint16_t* Y, float* U_out, void* ws, size_t ws_bytes,
+               void* stream) {
     g_last_error[0] = '\0';
     int s;
     if ((s = check_weight(w)) != QL_OK) return s;
     if ((s = check_linear_shape(w, T, r)) != QL_OK) return s;
+    const bool drop = keep != nullptr;
+    if (drop && (s = check_dropout(keep, p)) != QL_OK) return s;
     if (T == 0) return QL_OK;
     const int64_t N = w->rows, K = w->cols;
     if ((s = check_ptr(X, "X")) != QL_OK) return s;
@@ -326,7 +352,7 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         if ((s = check_ptr(B, "B")) != QL_OK) return s;
         if (U_out != nullptr && (s = check_ptr(U_out, "U_out")) != QL_OK) return s;
     }
-    const FwdWs need = carve_fwd(nullptr, N, K, T, r);
+    const FwdWs need = carve_fwd(nullptr, N, K, T, r, drop);
     if (need.bytes > 0) {
         if (ws == nullptr || ws_bytes < need.bytes)
             return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
@@ -334,28 +360,31 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
         if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const FwdWs f = carve_fwd(ws, N, K, T, r);
+    const FwdWs f = carve_fwd(ws, N, K, T, r, drop);
     const NF4Dev wd = to_dev(w);
-    if (T <= kGemvMaxT) return launch_gemv(wd, X, T, N, K, A, B, r, scale, Y, U_out, st);
+    if (T <= kGemvMaxT && !drop) return launch_gemv(wd, X, T, N, K, A, B, r, scale, Y, U_out, st);
     const int rp = rank_pad64(r);
     const uint16_t* Bsrc = B;
     int64_t ld_b = r;
     int r_b = r;
     if (r > 0) {
-        // U = X A^T: fp32 for the caller, bf16(s U) padded to rp for the epilogue
+        // U = X A^T (with dropout: c (X * keep) A^T, c = 1 / (1 - p)): fp32
+        // for the caller, bf16(s U) padded to rp for the epilogue
+        const float c = drop ? 1.0f / (1.0f - p) : 1.0f;
+        if (drop && (s = launch_keep_apply(X, keep, T, K, f.Xd, st)) != QL_OK) return s;
         ProjArgs a{};
         a.proj = 1;
-        a.P = X;
+        a.P = drop ? f.Xd : X;
         a.ldp = K;
         a.Q = A;
         a.ldq = K;
         a.rq = r;
         a.T = T;
         a.kred = K;
-        a.alpha_f = 1.0f;
+        a.alpha_f = c;
         a.out_f = U_out;
         a.ld_f = r;
-        a.alpha_b = scale;
+        a.alpha_b = scale * c;
         a.out_b = f.Us;
         a.ld_b = rp;
         if ((s = launch_lora_proj(a, false, f.proj, st)) != QL_OK) return s;
@@ -369,18 +398,16 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
     return launch_gemm_fwd(wd, X, f.Us, Bsrc, ld_b, r_b, rp, Y, T, N, K, f.split, st);
 }
 
-size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
-    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
-    return carve_bwd(nullptr, rows, cols, T, r, true, true, true).bytes;
-}
-
-int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
-                     const uint16_t* B, int32_t r, float scale, const float* U_saved, uint16_t* dX, float* dA,
-                     float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+int linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
+               const uint16_t* B, int32_t r, float scale, const uint8_t* keep, float p, const float* U_saved,
+               uint16_t* dX, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
     g_last_error[0] = '\0';
     int s;
     if ((s = check_weight(w)) != QL_OK) return s;
     if ((s = check_linear_shape(w, T, r)) != QL_OK) return s;
+    const bool drop = keep != nullptr;
+    if (drop && (s = check_dropout(keep, p)) != QL_OK) return s;
+    const float c = drop ? 1.0f / (1.0f - p) : 1.0f;
     if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_UNSUPPORTED, "accumulate = %d", accumulate);
     if (r == 0 && (dA != nullptr || dB != nullptr))
         return set_error(QL_ERR_SHAPE, "dA / dB requested with rank 0");
@@ -399,7 +426,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
     const bool have_u = U_saved != nullptr;
     if (have_u && (s = check_ptr(U_saved, "U_saved")) != QL_OK) return s;
     if ((want_da || (want_db && !have_u)) && (s = check_ptr(X, "X")) != QL_OK) return s;
-    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db);
+    const BwdWs need = carve_bwd(nullptr, N, K, T, r, want_dx, want_da, want_db, drop);
     if (need.bytes > 0) {
         if (ws == nullptr || ws_bytes < need.bytes)
             return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
@@ -407,7 +434,7 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db);
+    const BwdWs b = carve_bwd(ws, N, K, T, r, want_dx, want_da, want_db, drop);
     const NF4Dev wd = to_dev(w);
     const int rp = rank_pad64(r);
     const int rp16 = lora_grad_rp(r);
@@ -439,35 +466,89 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
         }
         if ((s = launch_lora_proj(a, true, b.proj, st)) != QL_OK) return s;
     }
-    if (r > 0 && want_db && !have_u) {  // U^T = (X A^T)^T recomputed
+    // dropout: the adapter input X * keep, for dA and a recomputed U
+    const bool need_xd = drop && r > 0 && (want_da || (want_db && !have_u));
+    if (need_xd && (s = launch_keep_apply(X, keep, T, K, b.Xd, st)) != QL_OK) return s;
+    const uint16_t* Xa = need_xd ? b.Xd : X;
+    if (r > 0 && want_db && !have_u) {  // U^T = (X A^T)^T recomputed (c (X * keep) A^T with dropout)
         ProjArgs a{};
         a.proj = 1;
-        a.P = X;
+        a.P = Xa;
         a.ldp = K;
         a.Q = A;
         a.ldq = K;
         a.rq = r;
         a.T = T;
         a.kred = K;
-        a.alpha_b = 1.0f;
+        a.alpha_b = c;
         a.out_bt = b.Ut;
         a.rows_bt = rp16;
         a.ld_bt = ldv;
         if ((s = launch_lora_proj(a, false, b.proj, st)) != QL_OK) return s;
     }
     if (want_dx) {
-        if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, rp, dX, T, N, K, b.split, st)) != QL_OK) return s;
+        // with dropout the adapter term is masked per element: the GEMM takes
+        // only dY W', a second kernel adds c (G A) * keep
+        if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, drop ? 0 : rp, dX, T, N, K, b.split, st)) != QL_OK) return s;
+        if (drop && r > 0 && (s = launch_lora_dx_keep(b.Gp, rp, A, r, keep, c, T, K, dX, st)) != QL_OK) return s;
     }
     if (want_da || want_db) {
         GradArgs g{};
         g.r = r;
         g.T = T;
         g.accumulate = accumulate;
-        if (want_da) g.pb[0] = GradProblem{X, K, K, b.Gt, ldv, dA, 1, 1.0f, nullptr};
+        if (want_da) g.pb[0] = GradProblem{Xa, K, K, b.Gt, ldv, dA, 1, c, nullptr};
         if (want_db) g.pb[1] = GradProblem{dY, N, N, b.Ut, ldv, dB, 0, scale, nullptr};
         if ((s = launch_lora_grads(g, b.gpart, st)) != QL_OK) return s;
     }
     return QL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A, const uint16_t* B,
+                     int32_t r, float scale, uint16_t* Y, float* U_out, void* ws, size_t ws_bytes, void* stream) {
+    return linear_fwd(w, X, T, A, B, r, scale, nullptr, 0.0f, Y, U_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float scale, const uint8_t* keep, float p, uint16_t* Y,
+                             float* U_out, void* ws, size_t ws_bytes, void* stream) {
+    if (keep == nullptr) {
+        g_last_error[0] = '\0';
+        return set_error(QL_ERR_NULL, "keep is NULL");
+    }
+    return linear_fwd(w, X, T, A, B, r, scale, keep, p, Y, U_out, ws, ws_bytes, stream);
+}
+
+size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    return carve_bwd(nullptr, rows, cols, T, r, true, true, true).bytes;
+}
+
+size_t qlora_linear_bwd_dropout_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    return carve_bwd(nullptr, rows, cols, T, r, true, true, true, true).bytes;
+}
+
+int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float scale, const float* U_saved, uint16_t* dX, float* dA,
+                     float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+    return linear_bwd(w, X, dY, T, A, B, r, scale, nullptr, 0.0f, U_saved, dX, dA, dB, accumulate, ws, ws_bytes,
+                      stream);
+}
+
+int qlora_linear_bwd_dropout(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float scale, const uint8_t* keep,
+                             float p, const float* U_saved, uint16_t* dX, float* dA, float* dB, int accumulate,
+                             void* ws, size_t ws_bytes, void* stream) {
+    if (keep == nullptr) {
+        g_last_error[0] = '\0';
+        return set_error(QL_ERR_NULL, "keep is NULL");
+    }
+    return linear_bwd(w, X, dY, T, A, B, r, scale, keep, p, U_saved, dX, dA, dB, accumulate, ws, ws_bytes, stream);
 }
 
 const char* qlora_status_string(int status) {

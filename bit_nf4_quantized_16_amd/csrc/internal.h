@@ -27,6 +27,13 @@ int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStrea
 
 // Adapter merge: out[n][k] = bf16(fl32(w'[n][k] + scale sum_j B[n][j] A[j][k]))
 // for 1 <= r <= QL_MAX_RANK, K % 64 == 0. Dynamic LDS merge_lds_bytes(r).
+// LoRA dropout with a bit-packed keep mask [T, K/8] (element 8i + j in bit
+// j of byte i): X_d = X * keep; dX[t][k] += fl32(c sum_j G[t][j] A[j][k]) for
+// kept (t, k) (G bf16 with row stride ldg, A [r, K]).
+int launch_keep_apply(const uint16_t* X, const uint8_t* keep, int64_t T, int64_t K, uint16_t* Xd, hipStream_t stream);
+int launch_lora_dx_keep(const uint16_t* G, int64_t ldg, const uint16_t* A, int r, const uint8_t* keep, float c,
+                        int64_t T, int64_t K, uint16_t* dX, hipStream_t stream);
+
 // Quantization error on a 4-bit grid (QL_GRID_*): fp64 partials in ws.
 size_t q4_error_ws_bytes(bool bf16, int64_t n);
 int launch_q4_error(const void* W, bool bf16, int64_t n, int grid, double* stats, void* ws, hipStream_t stream);

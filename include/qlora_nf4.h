@@ -237,6 +237,27 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_dropout — the forward with dropout on the adapter input
+ * ([codex] §3.4: dropout on the adapters, 0.05-0.1 for small data; [aivaro]
+ * §11: lora_dropout = 0.05). Inverted dropout of the adapter branch only, the
+ * random draws passed in as a keep mask:
+ *
+ *   keep   device, bit-packed [T, K/8] u8: element (t, 8i + j) in bit j of
+ *          byte t K/8 + i, 1 = kept; 16-B aligned
+ *   p      the dropout probability, 0 <= p < 1; c = fl32(1 / (1 - p))
+ *   U_out  c (X * keep) A^T (fp32), the U the backward needs
+ *   Y      X W'^T + s U B^T (the base sees X unmasked)
+ *
+ * Other arguments, layouts and errors as qlora_linear_fwd (QL_ERR_NULL for a
+ * NULL keep, QL_ERR_UNSUPPORTED for p outside [0, 1)); the workspace is
+ * qlora_linear_fwd_dropout_workspace(...) bytes. Every T takes the GEMM path.
+ */
+size_t qlora_linear_fwd_dropout_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
+int qlora_linear_fwd_dropout(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float scale, const uint8_t* keep, float p,
+                             uint16_t* Y, float* U_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qlora_linear_bwd — backward of the layer ([aivaro] §7: gradients flow
  * through the 4-bit weight, dequantized on the fly, and only the adapters
  * are updated).
@@ -258,6 +279,25 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
                      const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                      const float* U_saved, uint16_t* dX, float* dA, float* dB, int accumulate,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd_dropout — the backward of qlora_linear_fwd_dropout with
+ * the same keep mask and p ([codex] §3.4):
+ *
+ *   dX = dY W' + c (G A) * keep,  dA = c G^T (X * keep),  dB = s dY^T U
+ *
+ * with G = s dY B and U = c (X * keep) A^T (U_saved from the forward, or
+ * recomputed from X and keep when NULL). dX is dY W' rounded to bf16, then
+ * the kept entries get fl32(c (G A)) added and are rounded again. Other
+ * arguments, layouts and errors as qlora_linear_bwd (QL_ERR_NULL for a NULL
+ * keep, QL_ERR_UNSUPPORTED for p outside [0, 1)); the workspace is
+ * qlora_linear_bwd_dropout_workspace(...) bytes.
+ */
+size_t qlora_linear_bwd_dropout_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
+int qlora_linear_bwd_dropout(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float scale, const uint8_t* keep,
+                             float p, const float* U_saved, uint16_t* dX, float* dA, float* dB, int accumulate,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* ---- diagnostics ------------------------------------------------------- */
 /* Static text for a status code. */
@@ -281,7 +321,9 @@ const char* qlora_last_error(void);
 #define QL_KERNEL_LORA_GRAD 7
 #define QL_KERNEL_MERGE 8
 #define QL_KERNEL_QERROR 9
-#define QL_KERNEL_COUNT 10
+#define QL_KERNEL_KEEP_APPLY 10
+#define QL_KERNEL_DX_KEEP 11
+#define QL_KERNEL_COUNT 12
 int qlora_timer_arm(int kernel_id);
 int qlora_timer_read(int kernel_id, int64_t* launches, double* total_ms);
 int qlora_timer_disarm(int kernel_id);

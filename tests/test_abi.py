@@ -198,6 +198,32 @@ def test_quant_error_rejects(lib):
     assert call(ws=None) == L.QL_ERR_WORKSPACE
 
 
+def test_dropout_entries_reject(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    need = lib.qlora_linear_fwd_dropout_workspace(256, 256, 64, 8)
+    assert need > lib.qlora_linear_fwd_workspace(256, 256, 64, 8)  # X * keep is staged
+
+    def fwd(keep=P, p=0.1, wsb=need, T=64):
+        return lib.qlora_linear_fwd_dropout(_weight(L), P, T, P2, P3, 8, 2.0, keep, p, P, None, P, wsb, None)
+
+    assert fwd(keep=None) == L.QL_ERR_NULL
+    assert fwd(keep=MIS) == L.QL_ERR_ALIGN
+    assert fwd(p=1.0) == L.QL_ERR_UNSUPPORTED
+    assert fwd(p=-0.1) == L.QL_ERR_UNSUPPORTED
+    assert fwd(wsb=need - 1) == L.QL_ERR_WORKSPACE
+    assert fwd(T=0) == L.QL_OK
+    bneed = lib.qlora_linear_bwd_dropout_workspace(256, 256, 64, 8)
+
+    def bwd(keep=P, p=0.1, wsb=bneed):
+        return lib.qlora_linear_bwd_dropout(_weight(L), P, P2, 64, P3, P, 8, 2.0, keep, p, None, P, P2, P3, 0, P, wsb,
+                                            None)
+
+    assert bwd(keep=None) == L.QL_ERR_NULL
+    assert bwd(p=1.5) == L.QL_ERR_UNSUPPORTED
+    assert bwd(wsb=bneed - 1) == L.QL_ERR_WORKSPACE
+
+
 def test_timer_ids(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 
