@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-stage cold-cache measurements")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager launches (default: replays of the step captured in a HIP graph; "
+                         "the per-kernel timers always come from an eager pass, since events inside a replayed "
+                         "graph give no elapsed times)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--suite", action="store_true",
@@ -612,22 +616,47 @@ def main():
         run_step(qn, inp)
     torch.cuda.synchronize()
 
+    # eager steps with the library's kernel timers armed: the per-kernel
+    # durations of the roofline (HIP events on the launch stream)
     timers = {k: qn.KernelTimer(v) for k, v in KERNELS.items()}
     for t in timers.values():
         t.arm()
-    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    print("bench: timing %d eager steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         run_step(qn, inp)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager = time.perf_counter() - t0
     kstats = {}
     for k, t in timers.items():
         n, ms = t.read()
         t.disarm()
         kstats[k] = (n, ms)
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step_eager = elapsed_eager * 1e3 / args.steps
+    if args.eager:
+        ms_per_step = ms_per_step_eager
+    else:
+        # the same step captured once into a HIP graph (every call of the
+        # library issues only kernel launches) and replayed: the launch gaps
+        # of the host-side calls are gone, the work is the same
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_step(qn, inp)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step(qn, inp)
+        for _ in range(args.warmup):
+            graph.replay()
+        print("bench: timing %d graph replays of the step" % args.steps, file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ideal = ideal_step_seconds(inp)
     value = 100.0 * ideal / (ms_per_step / 1e3)
 
@@ -654,6 +683,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(ms_per_step_eager, 4),
+        "step_launch": "eager" if args.eager else "hip_graph_replay",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -343,19 +343,23 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
             // The last split of this token block to arrive (a per-block
             // counter tagged with the launch token; a counter carrying another
             // token counts as zero) adds the partials in split order, so the
-            // result does not depend on the arrival order. The wait orders
-            // the partial stores before the count.
+            // result does not depend on the arrival order. The last arrival
+            // leaves the count at zero, so a launch replayed with the same
+            // token (a captured graph) starts from zero as well. The wait
+            // orders the partial stores before the count.
             __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
             __syncthreads();
             if (tid == 0) {
                 uint64_t* c = p.cnt + blockIdx.x;
                 uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 uint64_t nv;
+                int arrived;
                 do {
-                    nv = ((old >> 8) == p.token) ? old + 1 : ((p.token << 8) | 1u);
+                    arrived = static_cast<int>(((old >> 8) == p.token) ? (old & 0xFFu) : 0u) + 1;
+                    nv = (p.token << 8) | static_cast<uint64_t>(arrived == nsplit ? 0 : arrived);
                 } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT));
-                s_last = static_cast<int>(nv & 0xFFu) == nsplit;
+                s_last = arrived == nsplit;
             }
             __syncthreads();
             if (s_last) {
@@ -403,7 +407,9 @@ int cu_count() {
 }
 
 // A fresh 56-bit token per launch, so that split counters left in a reused
-// workspace by earlier launches count as zero.
+// workspace by earlier launches count as zero (a launch that ends normally
+// leaves its counters at zero anyway; the token covers a workspace that held
+// anything else before).
 uint64_t next_token() {
     static std::atomic<uint64_t> ctr{
         (static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) * 0x9E3779B97F4A7C15ull) >>

@@ -32,7 +32,10 @@
  *     different streams race.
  *   - Workspace buffers need no initialisation and may hold anything between
  *     calls (the arrival counters kept in them are tagged with a token that
- *     is new for every launch).
+ *     is new for every launch, and a launch leaves them at zero).
+ *   - Calls may be captured into a HIP graph and replayed: they issue only
+ *     kernel launches (no memset or copy nodes, no host synchronisation), and
+ *     a replayed launch reusing its token finds its counters at zero.
  *   - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
  *   - All arguments are validated before anything is launched; on an error
  *     nothing is written. No C++ exception crosses this interface.
@@ -310,7 +313,9 @@ const char* qlora_last_error(void);
  * library records a pair of HIP events on the launch stream around every
  * launch of that kernel. qlora_timer_read() waits for the recorded events and
  * returns the number of launches and their summed duration. Kernel ids are
- * the QL_KERNEL_* values. Not meant to be armed from several threads at once.
+ * the QL_KERNEL_* values. Not meant to be armed from several threads at once,
+ * nor while launches are captured into a HIP graph (events recorded inside a
+ * replayed graph give no elapsed times: qlora_timer_read returns QL_ERR_HIP).
  */
 #define QL_KERNEL_QUANTIZE 1
 #define QL_KERNEL_DQ_ENCODE 2

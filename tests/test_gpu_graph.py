@@ -1,0 +1,60 @@
+"""The library's calls captured in a HIP graph (torch.cuda.graph) and replayed:
+every replay, with unrelated eager work and synchronizations between the
+replays, must give the eager results bit for bit. The captured step covers
+quantization with double quantization, the forward and backward GEMM path
+with split rank projections (their arrival counters must work when a launch
+is replayed with the same token) and the decode GEMV."""
+
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import bit_nf4_quantized_16_amd as qn
+
+    assert torch.cuda.is_available()
+    return qn
+
+
+def test_graph_replay_matches_eager(qn):
+    N = K = 5120
+    T, r = 256, 16
+    W = workloads.normal_weight(N, K, 0.02, seed=31).cuda()
+    case = workloads.lora_case("graph", W.cpu(), T, r, 32.0, 1 / K, 0.05, seed=31)
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    X1 = X[:1].contiguous()
+    s = case.scale
+
+    def step():
+        w = qn.quantize_weight(W)
+        Y, U = qn.qlora_linear_fwd(w, X, A, B, s)
+        dX, dA, dB = qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U)
+        y1, _ = qn.qlora_linear_fwd(w, X1, A, B, s)
+        return [w.packed, w.c8, w.dq_scale, w.dq_mean, Y, U, dX, dA, dB, y1]
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    other = workloads.normal_weight(1024, 2048, 0.02, seed=32).cuda()
+    for rep in range(3):
+        qn.quantize_weight(other)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), "replay %d: output %d differs from the eager run" % (rep, i)
