@@ -58,3 +58,58 @@ def test_graph_replay_matches_eager(qn):
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs, eager)):
             assert torch.equal(a, b), "replay %d: output %d differs from the eager run" % (rep, i)
+
+
+def test_two_stream_graph_matches_serial(qn):
+    # weights quantized on a second stream while the first runs the layer of
+    # the previous weight (event waits in between), captured and replayed
+    Ws = [workloads.normal_weight(1024, 2048, 0.02, seed=40 + i).cuda() for i in range(3)]
+    case = workloads.lora_case("streams", Ws[0].cpu(), 96, 16, 32.0, 1 / 2048, 0.05, seed=40)
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    s = case.scale
+
+    def serial():
+        outs = []
+        for W in Ws:
+            w = qn.quantize_weight(W)
+            Y, U = qn.qlora_linear_fwd(w, X, A, B, s)
+            outs += [w.packed, Y, U, *qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U)]
+        return outs
+
+    side = torch.cuda.Stream()
+
+    def two_streams():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        ws, evs = [], []
+        with torch.cuda.stream(side):
+            for W in Ws:
+                ws.append(qn.quantize_weight(W))
+                ev = torch.cuda.Event()
+                ev.record(side)
+                evs.append(ev)
+        outs = []
+        for w, ev in zip(ws, evs):
+            main.wait_event(ev)
+            Y, U = qn.qlora_linear_fwd(w, X, A, B, s)
+            outs += [w.packed, Y, U, *qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U)]
+        main.wait_stream(side)
+        return outs
+
+    ref = [t.clone() for t in serial()]
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
+        two_streams()
+    torch.cuda.current_stream().wait_stream(warm)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = two_streams()
+    for rep in range(3):
+        qn.quantize_weight(Ws[1])  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), "replay %d: output %d differs from the serial run" % (rep, i)
