@@ -142,6 +142,7 @@ struct FwdWs {
     uint16_t* Bp = nullptr;  // bf16 [N, rp64], GEMM path when r % 8 != 0
     void* proj = nullptr;    // split partials of the U projection
     float* split = nullptr;  // fp32 split-K partials of the GEMM path
+    void* gemv = nullptr;    // GEMV path: fp32 U and its projection's partials
     size_t bytes = 0;
 };
 
@@ -153,7 +154,10 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool drop 
     Carver c(ws);
     FwdWs f;
     const int rp = rank_pad64(r);
-    if (T > kGemvMaxT || drop) {  // the GEMV path needs no workspace
+    if (T <= kGemvMaxT && !drop) {
+        const size_t gb = gemv_ws_bytes(T, K, r);
+        if (gb) f.gemv = c.take<char>(gb);
+    } else {
         if (r > 0) {
             if (drop) f.Xd = c.take<uint16_t>(static_cast<size_t>(T) * K);
             f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
@@ -362,7 +366,7 @@ int linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint1
     hipStream_t st = static_cast<hipStream_t>(stream);
     const FwdWs f = carve_fwd(ws, N, K, T, r, drop);
     const NF4Dev wd = to_dev(w);
-    if (T <= kGemvMaxT && !drop) return launch_gemv(wd, X, T, N, K, A, B, r, scale, Y, U_out, st);
+    if (T <= kGemvMaxT && !drop) return launch_gemv(wd, X, T, N, K, A, B, r, scale, Y, U_out, f.gemv, st);
     const int rp = rank_pad64(r);
     const uint16_t* Bsrc = B;
     int64_t ld_b = r;

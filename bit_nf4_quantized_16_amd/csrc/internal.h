@@ -81,14 +81,21 @@ struct ProjArgs {
 // Workspace of a projection over T tokens, rank rq, reduction kred (0 when
 // its reduction is not split); ws must hold that many bytes, 16-B aligned.
 size_t lora_proj_ws_bytes(int64_t T, int rq, int64_t kred, bool q_cols);
+
+// A fresh 56-bit token per launch for the counters that kernels keep in a
+// workspace (a counter carrying another token counts as zero).
+uint64_t next_token();
 int launch_lora_proj(const ProjArgs& a, bool q_cols, void* ws, hipStream_t stream);
 
 // dst[i][j] = src[i][j] for j < cols, 0 for cols <= j < ldd.
 int launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, int64_t ldd, hipStream_t stream);
 
-// Y[t][n] = sum_k X[t][k] W'[n][k] + scale sum_j U[t][j] B[n][j] for T <= 16.
+// Y[t][n] = sum_k X[t][k] W'[n][k] + scale sum_j U[t][j] B[n][j] for T <= 16,
+// U = X A^T computed first (fp32, into U_out or the workspace) when r > 0;
+// ws holds gemv_ws_bytes(T, K, r) bytes, 16-B aligned.
+size_t gemv_ws_bytes(int64_t T, int64_t K, int r);
 int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const uint16_t* A,
-                const uint16_t* B, int r, float scale, uint16_t* Y, float* U_out, hipStream_t stream);
+                const uint16_t* B, int r, float scale, uint16_t* Y, float* U_out, void* ws, hipStream_t stream);
 
 // Tile / split-K plan of the dequant GEMMs for an MA x T output with a
 // reduction of RED, and the fp32 workspace its split partials need.

@@ -15,6 +15,7 @@
 // kernel computes dA and dB in one grid.
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <chrono>
 
 #include "common.h"
@@ -391,6 +392,17 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
     }
 }
 
+// A fresh 56-bit token per launch, so that split counters left in a reused
+// workspace by earlier launches count as zero (a launch that ends normally
+// leaves its counters at zero anyway; the token covers a workspace that held
+// anything else before).
+uint64_t next_token() {
+    static std::atomic<uint64_t> ctr{
+        (static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) * 0x9E3779B97F4A7C15ull) >>
+        8};
+    return ctr.fetch_add(1) & ((1ull << 56) - 1);
+}
+
 namespace {
 
 int cu_count() {
@@ -406,17 +418,6 @@ int cu_count() {
     return cached;
 }
 
-// A fresh 56-bit token per launch, so that split counters left in a reused
-// workspace by earlier launches count as zero (a launch that ends normally
-// leaves its counters at zero anyway; the token covers a workspace that held
-// anything else before).
-uint64_t next_token() {
-    static std::atomic<uint64_t> ctr{
-        (static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) * 0x9E3779B97F4A7C15ull) >>
-        8};
-    return ctr.fetch_add(1) & ((1ull << 56) - 1);
-}
-
 int proj_rt(int rq) {
     const int tiles = (rq + 15) / 16;
     return tiles <= 2 ? tiles : (tiles <= 4 ? 4 : 8);
@@ -428,13 +429,18 @@ int proj_waves(int rt) { return rt == 1 ? ProjDma<1>::NW : rt == 2 ? ProjDma<2>:
 // split keeping at least five steps per wave (with fewer, splitting
 // measured slower than not: the partial-sum hand-off costs a few memory
 // round trips); at most 8, and 1 for the register-path kernel.
+// QLORA_NF4_PROJ_SPLITS=n forces n (at most 32, at least one step per wave).
 int proj_splits(int64_t T, int rq, int64_t kred, bool q_cols) {
     if (q_cols && rq % 4 != 0) return 1;
     const int64_t nblk = ceil_div(T, 16);
     const int64_t nst = ceil_div(kred, 64);
+    const int nw = proj_waves(proj_rt(rq));
     int64_t s = cu_count() / nblk;
-    s = std::min<int64_t>(s, nst / (5 * proj_waves(proj_rt(rq))));
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 8)));
+    s = std::min<int64_t>(s, nst / (5 * nw));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, 8));
+    if (const char* e = std::getenv("QLORA_NF4_PROJ_SPLITS"))
+        s = std::max<int64_t>(1, std::min<int64_t>({static_cast<int64_t>(std::atoi(e)), 32, nst / nw}));
+    return static_cast<int>(s);
 }
 
 }  // namespace

@@ -55,17 +55,6 @@ __device__ __forceinline__ bf16x8_t lds_rows8(const uint16_t* tile, int r0, int 
 // byte j of x, where x holds four codes already multiplied by 4, one a byte.
 __device__ __forceinline__ uint32_t code_byte(uint32_t x, int j) { return (x >> (8 * j)) & 0xFFu; }
 
-// OCP FP8 E4M3FN code -> fp32, exact, without branches: the subnormal value
-// m 2^-9 and the normal one (1 + m/8) 2^(e-7) are both formed and one is
-// kept by a bit mask; the sign bit is copied last.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    const uint32_t e = (c >> 3) & 0xFu, m = c & 0x7u;
-    const uint32_t sub = __float_as_uint(static_cast<float>(m) * 0x1p-9f);
-    const uint32_t nrm = ((e + 120u) << 23) | (m << 20);
-    const uint32_t is_sub = 0u - ((e - 1u) >> 31);  // all ones when e == 0
-    return __uint_as_float((sub & is_sub) | (nrm & ~is_sub) | ((c & 0x80u) << 24));
-}
-
 // Codes, block constant and B operands of one 16-row block for one lane.
 template <int NS>
 struct MergeIn {

@@ -38,6 +38,18 @@ __device__ __forceinline__ BlockConst load_block_const(const NF4Dev& w, int64_t 
     return r;
 }
 
+// OCP FP8 E4M3FN code -> fp32, exact, without branches (a data-dependent
+// branch would make the compiler wait for every load in flight): the
+// subnormal value m 2^-9 and the normal one (1 + m/8) 2^(e-7) are both formed
+// and one is kept by a bit mask; the sign bit is copied last.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 0x7u;
+    const uint32_t sub = __float_as_uint(static_cast<float>(m) * 0x1p-9f);
+    const uint32_t nrm = ((e + 120u) << 23) | (m << 20);
+    const uint32_t is_sub = 0u - ((e - 1u) >> 31);  // all ones when e == 0
+    return __uint_as_float((sub & is_sub) | (nrm & ~is_sub) | ((c & 0x80u) << 24));
+}
+
 __device__ __forceinline__ float block_value(const BlockConst& c, int dq, float mu) {
     if (!dq) return c.s;
     const float prod = e4m3_decode(c.c8) * c.s;
@@ -117,6 +129,36 @@ __device__ __forceinline__ uint4 dequant8_lut(uint32_t w, const Lut16& L) {
     r.y = __builtin_amdgcn_perm(ya, xa, 0x07060302u);
     r.z = __builtin_amdgcn_perm(yb, xb, 0x05040100u);
     r.w = __builtin_amdgcn_perm(yb, xb, 0x07060302u);
+    return r;
+}
+
+// The same eight values in the order the lookup yields them, without the
+// final interleave: element slots (e0, e2, e4, e6, e1, e3, e5, e7). An MFMA
+// operand in this order pairs with a B operand in the same order
+// (x_slot_order), which the product does not see: only the pairing matters.
+__device__ __forceinline__ uint4 dequant8_lut_slots(uint32_t w, const Lut16& L) {
+    const uint32_t se = (w >> 4) & 0x07070707u;
+    const uint32_t so = w & 0x07070707u;
+    const uint32_t me = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+    const uint32_t mo = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);
+    const uint32_t le = lut_bytes(L.lo, se, me), he = lut_bytes(L.hi, se, me);
+    const uint32_t lo = lut_bytes(L.lo, so, mo), ho = lut_bytes(L.hi, so, mo);
+    uint4 r;
+    r.x = __builtin_amdgcn_perm(he, le, 0x05010400u);  // e0 | e2 << 16
+    r.y = __builtin_amdgcn_perm(he, le, 0x07030602u);  // e4 | e6 << 16
+    r.z = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // e1 | e3 << 16
+    r.w = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // e5 | e7 << 16
+    return r;
+}
+
+// Eight consecutive bf16 values (v.x = x0 | x1 << 16, ...) -> the slot order
+// of dequant8_lut_slots: (x0, x2), (x4, x6), (x1, x3), (x5, x7).
+__device__ __forceinline__ uint4 x_slot_order(uint4 v) {
+    uint4 r;
+    r.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+    r.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+    r.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+    r.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
     return r;
 }
 

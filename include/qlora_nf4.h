@@ -31,11 +31,16 @@
  *     Calls are re-entrant; calls that share output or workspace buffers on
  *     different streams race.
  *   - Workspace buffers need no initialisation and may hold anything between
- *     calls (the arrival counters kept in them are tagged with a token that
- *     is new for every launch, and a launch leaves them at zero).
+ *     calls (the arrival counters and flags kept in them are tagged with a
+ *     token that is new for every launch, and a launch leaves them clear).
  *   - Calls may be captured into a HIP graph and replayed: they issue only
  *     kernel launches (no memset or copy nodes, no host synchronisation), and
- *     a replayed launch reusing its token finds its counters at zero.
+ *     a replayed launch reusing its token finds its counters and flags clear.
+ *   - Some kernels hand partial results from one workgroup to another inside
+ *     a launch (device-scope stores and loads). Where a workgroup waits for
+ *     another, the wait is bounded; if it runs out, the workgroup computes
+ *     the result itself in the same order (same bits). Such kernels rely on
+ *     no other work writing their workspace during the launch.
  *   - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
  *   - All arguments are validated before anything is launched; on an error
  *     nothing is written. No C++ exception crosses this interface.
@@ -227,8 +232,10 @@ int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, in
  *          when that size is 0)
  *
  * r == 0 (A and B may then be NULL) runs the base matmul alone. T <= 16 takes
- * the single dequant-GEMV kernel (LoRA branch included, workspace size 0),
- * larger T the dequant-in-LDS MFMA GEMM.
+ * the dequant-GEMV kernel: one launch, the adapter branch included (its
+ * first workgroups compute U for the others; the workspace holds U's
+ * partial sums and their flags, size 0 when r == 0); larger T the
+ * dequant-in-LDS MFMA GEMM.
  * K must be a multiple of 64. Y must not alias any input.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE (T < 0, K % 64 != 0, r < 0 or
  * r > QL_MAX_RANK), QL_ERR_UNSUPPORTED, QL_ERR_ALIGN, QL_ERR_WORKSPACE,

@@ -113,3 +113,35 @@ def test_two_stream_graph_matches_serial(qn):
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs, ref)):
             assert torch.equal(a, b), "replay %d: output %d differs from the serial run" % (rep, i)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_decode_graph_replays_with_new_inputs(qn, T):
+    """A captured decode call (the GEMV keeps token-tagged counters in its
+    workspace, and a replay reuses the token): replays with new x give the
+    eager results for that x."""
+    N, K, r = 4096, 4096, 16
+    W = workloads.normal_weight(N, K, 0.02, seed=41).cuda()
+    case = workloads.lora_case("graph_decode", W.cpu(), T, r, 32.0, 1 / K, 0.05, seed=41)
+    A, B = case.A.cuda(), case.B.cuda()
+    w = qn.quantize_weight(W)
+    X = torch.empty(T, K, dtype=torch.bfloat16, device="cuda")
+    xs = [workloads.bf16_normal((T, K), 1.0, seed=50 + i).cuda() for i in range(4)]
+    X.copy_(xs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qn.qlora_linear_fwd(w, X, A, B, case.scale)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Y, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    for rep in range(1, 4):
+        X.copy_(xs[rep])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        Ye, Ue = qn.qlora_linear_fwd(w, xs[rep], A, B, case.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Ye) and torch.equal(U, Ue), "replay %d differs from the eager call" % rep

@@ -73,7 +73,8 @@ def test_ragged_shapes_and_ranks(qn, N, K, T, r):
 # 8 tiles of 16), a half last K step (K % 128 == 64), N below one 16-row tile,
 # several passes over K (K = 4160: 33 steps of 128) and the base alone
 @pytest.mark.parametrize("N,K,T,r", [(200, 320, 3, 5), (136, 64, 1, 24), (264, 192, 16, 40), (520, 1088, 7, 100),
-                                     (8, 128, 2, 128), (96, 4160, 16, 16), (48, 4160, 5, 64), (72, 256, 1, 0)])
+                                     (8, 128, 2, 128), (96, 4160, 16, 16), (48, 4160, 5, 64), (72, 256, 1, 0),
+                                     (24, 1472, 16, 8), (24, 1536, 16, 8), (40, 11008, 2, 16), (40, 11008, 3, 16)])
 def test_gemv_ranks_and_ragged_k(qn, N, K, T, r):
     W = workloads.normal_weight(N, K, 0.02, seed=N + 3 * K)
     case = workloads.lora_case("gemv_N%dK%dT%dr%d" % (N, K, T, r), W, T, r, 2.0 * max(r, 1), 1 / K, 0.05,
@@ -87,6 +88,34 @@ def test_gemv_ranks_and_ragged_k(qn, N, K, T, r):
         assert normwise_rel_err(bf16_to_np(Y), H) <= TOL
     else:
         _run(qn, case)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_gemv_output_without_saved_u(qn, T):
+    """The decode path gives the same Y, bit for bit, whether U goes to the
+    caller's buffer or to the workspace."""
+    W = workloads.normal_weight(264, 1024, 0.02, seed=7)
+    case = workloads.lora_case("gemv_u", W, T, 16, 32.0, 1 / 1024, 0.05, seed=8)
+    w = qn.quantize_weight(W.cuda())
+    X, A, B = (t.cuda() for t in (case.X, case.A, case.B))
+    Y1, U1 = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    Y2, U2 = qn.qlora_linear_fwd(w, X, A, B, case.scale, save_u=False)
+    assert U2 is None and torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("N,K,T,r", [(264, 1024, 1, 16), (200, 4160, 5, 40), (96, 1536, 16, 128), (40, 11008, 3, 16)])
+def test_gemv_local_u_is_bitwise_the_shared_one(qn, monkeypatch, N, K, T, r):
+    """Forcing every workgroup to compute U itself (the path taken should the
+    wait for the shared U ever run out) gives the same Y and U bit for bit."""
+    W = workloads.normal_weight(N, K, 0.02, seed=K + r)
+    case = workloads.lora_case("gemv_ulocal", W, T, r, 2.0 * r, 1 / K, 0.05, seed=T + r)
+    w = qn.quantize_weight(W.cuda())
+    X, A, B = (t.cuda() for t in (case.X, case.A, case.B))
+    Y1, U1 = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    monkeypatch.setenv("QLORA_NF4_GEMV_SPIN", "0")
+    Y2, U2 = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(U1, U2)
 
 
 def test_without_double_quant(qn):
