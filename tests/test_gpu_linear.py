@@ -74,7 +74,10 @@ def test_ragged_shapes_and_ranks(qn, N, K, T, r):
 # several passes over K (K = 4160: 33 steps of 128) and the base alone
 @pytest.mark.parametrize("N,K,T,r", [(200, 320, 3, 5), (136, 64, 1, 24), (264, 192, 16, 40), (520, 1088, 7, 100),
                                      (8, 128, 2, 128), (96, 4160, 16, 16), (48, 4160, 5, 64), (72, 256, 1, 0),
-                                     (24, 1472, 16, 8), (24, 1536, 16, 8), (40, 11008, 2, 16), (40, 11008, 3, 16)])
+                                     (24, 1472, 16, 8), (24, 1536, 16, 8), (40, 11008, 2, 16), (40, 11008, 3, 16),
+                                     # more 256-wide steps per wave than are issued up front (the ring of
+                                     # loads) for each width of x: T <= 2, <= 4, <= 8
+                                     (24, 16448, 1, 16), (24, 8256, 4, 8), (24, 6208, 8, 8)])
 def test_gemv_ranks_and_ragged_k(qn, N, K, T, r):
     W = workloads.normal_weight(N, K, 0.02, seed=N + 3 * K)
     case = workloads.lora_case("gemv_N%dK%dT%dr%d" % (N, K, T, r), W, T, r, 2.0 * max(r, 1), 1 / K, 0.05,
