@@ -462,11 +462,27 @@ def run_suite(torch, qn):
         ng, msg = tg.read()
         tg.disarm()
         sec = msg / 1e3
+        # the same pass captured once into a HIP graph and replayed, as a
+        # decode loop would run it: no host-side gap between the launches
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            gemv_pass()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gemv_pass()
+        graph_s = timed(graph.replay, reps=5)
+        del graph
         nbytes = sum(gemv_bytes(n, k, T, 16) for _, n, k, _ in stack)
         res["c4_gemv_pass_T%d" % T] = {"calls": ng, "kernel_ms": round(msg, 3), "wall_ms": round(wall * 1e3, 3),
                                        "GB": round(nbytes / 1e9, 3), "GB/s": round(nbytes / sec / 1e9, 1),
                                        "frac": round(nbytes / sec / PEAK_HBM, 4),
-                                       "kernel_us_per_call": round(msg * 1e3 / max(ng, 1), 2)}
+                                       "kernel_us_per_call": round(msg * 1e3 / max(ng, 1), 2),
+                                       "graph_ms": round(graph_s * 1e3, 3),
+                                       "graph_GB/s": round(nbytes / graph_s / 1e9, 1),
+                                       "graph_frac": round(nbytes / graph_s / PEAK_HBM, 4)}
         del outs
 
     def gemm_rows(shapes, T, r, alpha, std, seed0, weights=None):

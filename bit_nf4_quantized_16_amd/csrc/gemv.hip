@@ -302,6 +302,20 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs p) {
         }
     }
 
+    // First try at the U words (one element a thread, all its slices at once),
+    // issued before the reduction so that their latency overlaps it
+    constexpr int kEarlyKs = 16;
+    const int nur = T * r;
+    const bool early = r > 0 && nur <= 512 && p.nks <= kEarlyKs;
+    uint64_t raw[kEarlyKs];
+    if (early && tid < nur) {
+#pragma unroll
+        for (int ks = 0; ks < kEarlyKs; ++ks)
+            raw[ks] = ks < p.nks ? __hip_atomic_load(p.uword + static_cast<int64_t>(ks) * nur + tid, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0;
+    }
+
     // D[4 g + rr][li]: rows n0 + 4 g + rr, token li
     put_tile(acc);
     if (r > 0) {
@@ -312,11 +326,26 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs p) {
     __syncthreads();
     const float base = tid < 256 ? sum_tile(tid) : 0.0f;
     if (r > 0) {
-        const int nur = T * r;
         constexpr int kUE = 16 * QL_MAX_RANK / 512;  // U elements a thread adds
         float uv[kUE];
         int ok = 0;
-        for (int it = 0; it < p.spin; ++it) {
+        if (early && p.spin > 0) {
+            bool bad = false;
+            float v = 0.0f;
+            if (tid < nur) {
+#pragma unroll
+                for (int ks = 0; ks < kEarlyKs; ++ks)
+                    if (ks < p.nks) {
+                        bad = bad || static_cast<uint32_t>(raw[ks] >> 32) != p.tag;
+                        v += __uint_as_float(static_cast<uint32_t>(raw[ks]));
+                    }
+            }
+            uv[0] = v;
+#pragma unroll
+            for (int q = 1; q < kUE; ++q) uv[q] = 0.0f;
+            ok = !__syncthreads_or(bad);  // also: every wave's partial tile has been read
+        }
+        for (int it = 0; !ok && it < p.spin; ++it) {
             bool bad = false;
 #pragma unroll
             for (int q = 0; q < kUE; ++q) {
