@@ -111,8 +111,17 @@ __device__ __forceinline__ int gemv_block_of(int g) { return (g & 1) ? (g >> 1) 
 
 // NS > 0: every wave has NS steps, or NS - 1 (all issued up front);
 // NS == 0: a ring of gemv_ring_depth<TX>() steps, refilled as they are used.
+// Four waves per SIMD (two workgroups per CU) where that costs no spills: the
+// ring for the widest x needs more registers, and spilling them measured
+// slower than one workgroup per CU.
 template <int TX, int NS>
-__global__ __launch_bounds__(512) void gemv_kernel(GemvArgs p) {
+constexpr int gemv_min_waves() {
+    return (TX == 8 && NS == 0) ? 1 : 4;
+}
+
+template <int TX, int NS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_waves<TX, NS>()))) void gemv_kernel(
+    GemvArgs p) {
     constexpr int D = NS > 0 ? NS : gemv_ring_depth<TX>();
     // each wave's x slot (2 TX tokens x 32 pieces); after its last step the
     // wave's 16 x 16 fp32 partial tile takes the slot's first KiB
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs p) {
 
     // First try at the U words (one element a thread, all its slices at once),
     // issued before the reduction so that their latency overlaps it
-    constexpr int kEarlyKs = 16;
+    constexpr int kEarlyKs = TX <= 2 ? 16 : 8;  // fewer registers where x takes more
     const int nur = T * r;
     const bool early = r > 0 && nur <= 512 && p.nks <= kEarlyKs;
     uint64_t raw[kEarlyKs];
