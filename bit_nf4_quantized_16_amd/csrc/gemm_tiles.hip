@@ -10,7 +10,8 @@
 //
 // One kernel template serves both. The MFMA "A side" is the output feature
 // dimension (n for the forward, k for dX); the "B side" is the tokens. A
-// workgroup of four waves owns a TA x TT output tile (2 x 2 waves). Each
+// workgroup owns a TA x TT output tile: eight waves (4 along A x 2 along the
+// tokens) for the 256 x 256 tile, four (2 x 2) for the 128 x 128 one. Each
 // reduction step of 64 reads a token tile and an expanded bf16 weight tile
 // from LDS; both are double buffered. The token tile arrives by direct
 // global-to-LDS loads (no registers; 128-byte rows with an XOR swizzle of the
