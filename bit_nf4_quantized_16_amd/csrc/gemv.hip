@@ -40,7 +40,7 @@ namespace qlnf4 {
 // [T, r]) is computed once per call inside the same launch: the first
 // workgroups of the grid each multiply one 16-row tile of A by one slice of
 // kGemvUSteps steps of x (the same wave-per-step layout, A in registers) and
-// stores each element of its partial as one 64-bit word: the fp32 value and
+// store each element of their partial as one 64-bit word: the fp32 value and
 // a tag of the launch (device-scope stores). A row workgroup, once its own
 // rows are done, loads the words (device-scope loads) and adds the partials
 // in slice order; if any tag is not this launch's yet, it sleeps a little
@@ -53,8 +53,10 @@ namespace qlnf4 {
 // one for the kGemvSub groups; single atomic adds, as atomics on one word are
 // served one after another); the last one clears the words, so a replay
 // finds no word of the previous one. An eager launch has a token of its own
-// and skips the count. Lanes of tokens >= T read token T-1
-// and their outputs are dropped; rows past N read row N-1 and are dropped.
+// and skips the count.
+//
+// Lanes of tokens >= T read token T-1 and their outputs are dropped; rows
+// past N read row N-1 and are dropped.
 // ===========================================================================
 constexpr int kGemvRows = 16;
 constexpr int kGemvWaves = 8;
@@ -78,11 +80,9 @@ struct GemvArgs {
     uint64_t token;   // 40 bits
     uint32_t tag;     // nonzero, from the token (a cleared word is 0)
     int count_done;   // the launch is captured: count the row workgroups, clear the words
-    int nu, nks, rt;  // U workgroups = rt (16-row tiles of A) x nks (slices of eight steps)
-    int spin;         // polls of the U count before computing U locally
+    int nu, nks, rt;  // U workgroups = rt (16-row tiles of A) x nks (slices of kGemvUSteps steps)
+    int spin;         // loads of the U words before computing U locally
 };
-
-
 
 // Steps whose loads one wave keeps in flight, by TX = 16-byte x loads per
 // lane and step (T <= 2 * TX): fewer when x needs more registers.
@@ -109,8 +109,6 @@ struct GemvStage {
 // Block of the step that lane group g holds after the swap.
 __device__ __forceinline__ int gemv_block_of(int g) { return (g & 1) ? (g >> 1) : 2 + (g >> 1); }
 
-// NS > 0: every wave has NS steps, or NS - 1 (all issued up front);
-// NS == 0: a ring of gemv_ring_depth<TX>() steps, refilled as they are used.
 // Four waves per SIMD (two workgroups per CU) where that costs no spills: the
 // ring for the widest x needs more registers, and spilling them measured
 // slower than one workgroup per CU.
@@ -119,6 +117,8 @@ constexpr int gemv_min_waves() {
     return (TX == 8 && NS == 0) ? 1 : 4;
 }
 
+// NS > 0: every wave has NS steps, or NS - 1 (all issued up front);
+// NS == 0: a ring of gemv_ring_depth<TX>() steps, refilled as they are used.
 template <int TX, int NS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_waves<TX, NS>()))) void gemv_kernel(
     GemvArgs p) {
