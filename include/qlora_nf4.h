@@ -47,6 +47,12 @@
  *     qlora_last_error() gives a message for the calling thread.
  *   - Results are bitwise reproducible run to run (no floating-point
  *     atomics).
+ *   - Environment overrides, for tuning and tests only: QLORA_NF4_GEMM_TILE
+ *     (128 or 256) and QLORA_NF4_GEMM_SPLITS (split count of the 256 tile) for
+ *     the T > 16 GEMMs, QLORA_NF4_PROJ_SPLITS for the rank-r projections, and
+ *     QLORA_NF4_GEMV_SPIN (loads of the shared U before a decode workgroup
+ *     computes U itself; 0 forces that path). Results stay within the stated
+ *     tolerances under any of them.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
