@@ -25,6 +25,7 @@ __all__ = [
     "qlora_merge",
     "q4_quant_error",
     "qlora_linear_fwd",
+    "qlora_linear_fwd_group",
     "qlora_linear_bwd",
     "quantize_weight",
     "QLoRALinearFunction",
@@ -215,6 +216,32 @@ def qlora_linear_fwd(w, X, A=None, B=None, scale=1.0, save_u=True, out=None, kee
                                          _ptr(ws), wsb, _stream())
         )
     return Y, U
+
+
+def qlora_linear_fwd_group(ws, X, As=None, Bs=None, scale=1.0, save_u=True):
+    """qlora_linear_fwd for up to four layers that read the same X (q/k/v,
+    gate/up): one launch when T <= 16. ``ws`` NF4Weights sharing ``cols``;
+    ``As``/``Bs`` lists of adapters (None for r = 0). Returns a list of
+    (Y, U) pairs, as qlora_linear_fwd."""
+    nw = len(ws)
+    T = X.shape[0]
+    r = 0 if As is None else As[0].shape[0]
+    dev = X.device
+    Ys = [torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev) for w in ws]
+    Us = [torch.empty(T, r, dtype=torch.float32, device=dev) if (save_u and r > 0) else None for _ in ws]
+    descs = [w.descriptor() for w in ws]
+    arr = lambda ts: (ctypes.c_void_p * max(nw, 1))(*[_ptr(t) for t in ts])
+    wp = (ctypes.c_void_p * max(nw, 1))(*[ctypes.addressof(d) for d in descs])
+    rows = (ctypes.c_int64 * max(nw, 1))(*[w.rows for w in ws])
+    cols = ws[0].cols if nw else 0
+    ws_, wsb = _workspace(lib.qlora_linear_fwd_group_workspace(rows, nw, cols, max(T, 1), r), dev)
+    As_ = arr([_bits(a) for a in As]) if As is not None else None
+    Bs_ = arr([_bits(b) for b in Bs]) if Bs is not None else None
+    _check(
+        lib.qlora_linear_fwd_group(wp, nw, _ptr(_bits(X)), T, As_, Bs_, r, float(scale), arr(Ys), arr(Us), _ptr(ws_),
+                                   wsb, _stream())
+    )
+    return list(zip(Ys, Us))
 
 
 def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, need_da=True, need_db=True, dA=None,

@@ -72,6 +72,8 @@ SIGNATURES = {
     "q4_quant_error": (_I, [_P, _I, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_fwd_group_workspace": (_SZ, [_P, _I32, _I64, _I64, _I32]),
+    "qlora_linear_fwd_group": (_I, [_P, _I32, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd_dropout": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),

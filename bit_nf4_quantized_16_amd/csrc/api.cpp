@@ -402,6 +402,66 @@ int linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint1
     return launch_gemm_fwd(wd, X, f.Us, Bsrc, ld_b, r_b, rp, Y, T, N, K, f.split, st);
 }
 
+size_t group_fwd_ws(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
+    if (rows == nullptr || nw < 1 || nw > kGemvMaxGroup || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    size_t m = 0;
+    for (int i = 0; i < nw; ++i) {
+        if (rows[i] <= 0) return 0;
+        m = std::max(m, carve_fwd(nullptr, rows[i], cols, T, r).bytes);
+    }
+    // decode: one launch, a workspace slice per weight; larger T: the weights
+    // one after another, sharing one workspace
+    return T <= kGemvMaxT ? static_cast<size_t>(nw) * gemv_ws_bytes(T, cols, r) : m;
+}
+
+int linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,
+                     const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale, uint16_t* const* Y,
+                     float* const* U_out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if (nw < 1 || nw > kGemvMaxGroup) return set_error(QL_ERR_SHAPE, "%d weights in a group (1 to %d)", nw, kGemvMaxGroup);
+    // w, A, B, Y and U_out are host arrays of pointers: only NULL is an error
+    if (w == nullptr || Y == nullptr) return set_error(QL_ERR_NULL, "%s array is NULL", w == nullptr ? "w" : "Y");
+    if (r > 0 && (A == nullptr || B == nullptr))
+        return set_error(QL_ERR_NULL, "%s array is NULL", A == nullptr ? "A" : "B");
+    int64_t rows[kGemvMaxGroup];
+    for (int i = 0; i < nw; ++i) {
+        if ((s = check_weight(w[i])) != QL_OK) return s;
+        if ((s = check_linear_shape(w[i], T, r)) != QL_OK) return s;
+        if (w[i]->cols != w[0]->cols)
+            return set_error(QL_ERR_SHAPE, "weight %d has %lld columns, weight 0 %lld", i, (long long)w[i]->cols,
+                             (long long)w[0]->cols);
+        rows[i] = w[i]->rows;
+        if ((s = check_ptr(Y[i], "Y[i]")) != QL_OK) return s;
+        if (r > 0) {
+            if ((s = check_ptr(A[i], "A[i]")) != QL_OK) return s;
+            if ((s = check_ptr(B[i], "B[i]")) != QL_OK) return s;
+            if (U_out != nullptr && U_out[i] != nullptr && (s = check_ptr(U_out[i], "U_out[i]")) != QL_OK) return s;
+        }
+    }
+    if (T == 0) return QL_OK;
+    if ((s = check_ptr(X, "X")) != QL_OK) return s;
+    const int64_t K = w[0]->cols;
+    if (T > kGemvMaxT) {
+        for (int i = 0; i < nw; ++i)
+            if ((s = linear_fwd(w[i], X, T, r > 0 ? A[i] : nullptr, r > 0 ? B[i] : nullptr, r, scale, nullptr, 0.0f,
+                                Y[i], (r > 0 && U_out != nullptr) ? U_out[i] : nullptr, ws, ws_bytes, stream)) != QL_OK)
+                return s;
+        return QL_OK;
+    }
+    const size_t need = group_fwd_ws(rows, nw, K, T, r);
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes, need);
+        if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    GemvCall calls[kGemvMaxGroup];
+    for (int i = 0; i < nw; ++i)
+        calls[i] = GemvCall{to_dev(w[i]), rows[i], r > 0 ? A[i] : nullptr, r > 0 ? B[i] : nullptr, Y[i],
+                            (r > 0 && U_out != nullptr) ? U_out[i] : nullptr};
+    return launch_gemv_group(calls, nw, X, T, K, r, scale, ws, static_cast<hipStream_t>(stream));
+}
+
 int linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T, const uint16_t* A,
                const uint16_t* B, int32_t r, float scale, const uint8_t* keep, float p, const float* U_saved,
                uint16_t* dX, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
@@ -515,6 +575,16 @@ extern "C" {
 int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A, const uint16_t* B,
                      int32_t r, float scale, uint16_t* Y, float* U_out, void* ws, size_t ws_bytes, void* stream) {
     return linear_fwd(w, X, T, A, B, r, scale, nullptr, 0.0f, Y, U_out, ws, ws_bytes, stream);
+}
+
+size_t qlora_linear_fwd_group_workspace(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
+    return group_fwd_ws(rows, nw, cols, T, r);
+}
+
+int qlora_linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,
+                           const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                           uint16_t* const* Y, float* const* U_out, void* ws, size_t ws_bytes, void* stream) {
+    return linear_fwd_group(w, nw, X, T, A, B, r, scale, Y, U_out, ws, ws_bytes, stream);
 }
 
 int qlora_linear_fwd_dropout(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,

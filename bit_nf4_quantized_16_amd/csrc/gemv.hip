@@ -63,25 +63,38 @@ constexpr int kGemvWaves = 8;
 constexpr int kGemvSub = 32;    // first level of the done count
 constexpr int kGemvUSteps = 4;  // steps of x in one U workgroup's slice (waves 0..3)
 
-struct GemvArgs {
+// One weight of a launch: a launch serves up to kGemvGroup weights that share
+// x (the same K, T, rank and scale), each with its own U workgroups, row
+// workgroups, outputs and workspace.
+constexpr int kGemvGroup = kGemvMaxGroup;
+
+struct GemvWeight {
     NF4Dev w;
-    const uint16_t* X;
-    int T;
-    int64_t N, K;
+    int64_t N;
     const uint16_t* A;
     const uint16_t* B;
+    uint16_t* Y;
+    float* U_out;     // [T, r] fp32 = X A^T, or null
+    uint64_t* uword;  // [nks][T][r]: slice ks of U, tag << 32 | fp32 bits (r > 0)
+    uint64_t* done;   // [kGemvSub + 1]: token << 24 | count; row workgroups done with U (r > 0)
+    int nu, nrow;     // its U and row workgroups
+    int ub, rb;       // the grid index of its first U and first row workgroup
+};
+
+struct GemvArgs {
+    const uint16_t* X;
+    int T;
+    int64_t K;
     int r;
     float scale;
-    uint16_t* Y;
-    float* U_out;  // [T, r] fp32 = X A^T, or null
-    // r > 0: the tagged U partials and the done counter (workspace), the launch token
-    uint64_t* uword;  // [nks][T][r]: slice ks of U, tag << 32 | fp32 bits
-    uint64_t* done;   // [kGemvSub + 1]: token << 24 | count; row workgroups done with U
     uint64_t token;   // 40 bits
     uint32_t tag;     // nonzero, from the token (a cleared word is 0)
     int count_done;   // the launch is captured: count the row workgroups, clear the words
-    int nu, nks, rt;  // U workgroups = rt (16-row tiles of A) x nks (slices of kGemvUSteps steps)
+    int nks, rt;      // U workgroups of a weight = rt (16-row tiles of A) x nks (slices of kGemvUSteps steps)
     int spin;         // loads of the U words before computing U locally
+    int ngroup;       // weights in this launch
+    int nu_all;       // U workgroups of all weights (they come first in the grid)
+    GemvWeight g[kGemvGroup];
 };
 
 // Steps whose loads one wave keeps in flight, by TX = 16-byte x loads per
@@ -130,11 +143,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     __shared__ float sU[16 * QL_MAX_RANK];
     __shared__ uint16_t sB[kGemvRows * QL_MAX_RANK];
     __shared__ int s_last;
-    const NF4Dev& w = p.w;
+    // this workgroup's weight (the U workgroups of all weights come first)
+    const int bid = static_cast<int>(blockIdx.x);
+    const bool is_u = bid < p.nu_all;
+    int wi = 0;
+    while (wi + 1 < p.ngroup && bid >= (is_u ? p.g[wi + 1].ub : p.g[wi + 1].rb)) ++wi;
+    const GemvWeight& gw = p.g[wi];
+    const NF4Dev& w = gw.w;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar step loop
     const int li = lane & 15, g = lane >> 4;
-    const int64_t K = p.K, N = p.N;
+    const int64_t K = p.K, N = gw.N;
     const int T = p.T, r = p.r;
     const int64_t nblk = K / 64, rowbytes = K / 2;
     const int nbs = static_cast<int>((nblk + 3) / 4);
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
             const int64_t arow = std::min(16 * jt + li, r - 1);
 #pragma unroll
             for (int m = 0; m < 8; ++m)
-                av[m] = *reinterpret_cast<const uint4*>(p.A + arow * K +
+                av[m] = *reinterpret_cast<const uint4*>(gw.A + arow * K +
                                                         std::min<int64_t>(256 * s + 64 * pb + 8 * m, K - 8));
             put_x(x);
             const bool kin = 4 * s + pb < nblk;  // a block past K adds zeros
@@ -202,15 +221,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
         return v;
     };
 
-    if (static_cast<int>(blockIdx.x) < p.nu) {
+    if (is_u) {
         // a U workgroup: its slice of one 16-row tile of U^T, published
-        const int jt = blockIdx.x % p.rt, ks = blockIdx.x / p.rt;
+        const int local = bid - gw.ub;
+        const int jt = local % p.rt, ks = local / p.rt;
         put_tile(u_unit(jt, ks));
-        if (tid == 0 && blockIdx.x == 0 && p.count_done) {
+        if (tid == 0 && local == 0 && p.count_done) {
             // U workgroup 0 starts the done count of this launch before its
             // words: the row workgroups count only after they have all words
             for (int k = 0; k <= kGemvSub; ++k)
-                __hip_atomic_store(p.done + k, p.token << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(gw.done + k, p.token << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
         }
         __syncthreads();
@@ -218,14 +238,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
             const int j = 16 * jt + (tid >> 4), t = tid & 15;
             const float v = sum_tile(tid);
             if (t < T && j < r)  // device scope: read on other XCDs
-                __hip_atomic_store(p.uword + (static_cast<int64_t>(ks) * T + t) * r + j,
+                __hip_atomic_store(gw.uword + (static_cast<int64_t>(ks) * T + t) * r + j,
                                    (uint64_t{p.tag} << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
     }
 
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x - p.nu) * kGemvRows;
+    const int64_t n0 = static_cast<int64_t>(bid - gw.rb) * kGemvRows;
     const int64_t row = std::min<int64_t>(n0 + li, N - 1);
     const int nsw = wave < nbs ? (nbs - 1 - wave) / kGemvWaves + 1 : 0;  // steps of this wave
     const uint8_t* const rowcodes = w.packed + row * rowbytes;
@@ -247,7 +267,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     if (r > 0) {
         const int64_t last = N * r - 1;
 #pragma unroll
-        for (int q = 0; q < kBQ; ++q) bpre[q] = p.B[std::min<int64_t>(n0 * r + std::min(tid + 512 * q, nb - 1), last)];
+        for (int q = 0; q < kBQ; ++q) bpre[q] = gw.B[std::min<int64_t>(n0 * r + std::min(tid + 512 * q, nb - 1), last)];
     }
 
     auto issue = [&](GemvStage<TX>& st, int k) {
@@ -320,7 +340,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     if (early && tid < nur) {
 #pragma unroll
         for (int ks = 0; ks < kEarlyKs; ++ks)
-            raw[ks] = ks < p.nks ? __hip_atomic_load(p.uword + static_cast<int64_t>(ks) * nur + tid, __ATOMIC_RELAXED,
+            raw[ks] = ks < p.nks ? __hip_atomic_load(gw.uword + static_cast<int64_t>(ks) * nur + tid, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT)
                                  : 0;
     }
@@ -362,7 +382,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                 float v = 0.0f;
                 if (e < nur)
                     for (int ks = 0; ks < p.nks; ++ks) {
-                        const uint64_t wd = __hip_atomic_load(p.uword + static_cast<int64_t>(ks) * nur + e,
+                        const uint64_t wd = __hip_atomic_load(gw.uword + static_cast<int64_t>(ks) * nur + e,
                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         bad = bad || static_cast<uint32_t>(wd >> 32) != p.tag;
                         v += __uint_as_float(static_cast<uint32_t>(wd));
@@ -396,13 +416,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                 }
         }
         if (tid == 0 && p.count_done) {
-            const int nrow = static_cast<int>(gridDim.x) - p.nu, b = static_cast<int>(blockIdx.x) - p.nu;
+            const int nrow = gw.nrow, b = bid - gw.rb;
             const int k = b % kGemvSub, groups = std::min(nrow, kGemvSub);
             const int in_k = nrow / kGemvSub + (k < nrow % kGemvSub ? 1 : 0);  // workgroups counted on k
             int last = 0;
-            uint64_t old = __hip_atomic_fetch_add(p.done + k, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint64_t old = __hip_atomic_fetch_add(gw.done + k, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((old >> 24) == p.token && static_cast<int>(old & 0xFFFFFFu) + 1 == in_k) {
-                old = __hip_atomic_fetch_add(p.done + kGemvSub, uint64_t{1}, __ATOMIC_RELAXED,
+                old = __hip_atomic_fetch_add(gw.done + kGemvSub, uint64_t{1}, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
                 last = (old >> 24) == p.token && static_cast<int>(old & 0xFFFFFFu) + 1 == groups;
             }
@@ -413,9 +433,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
         __syncthreads();
         if (s_last)  // the last row workgroup: clear the words for the next launch
             for (int e = tid; e < p.nks * nur; e += 512)
-                __hip_atomic_store(p.uword + e, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.U_out != nullptr && n0 == 0)
-            for (int e = tid; e < nur; e += 512) p.U_out[e] = sU[e];
+                __hip_atomic_store(gw.uword + e, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (gw.U_out != nullptr && n0 == 0)
+            for (int e = tid; e < nur; e += 512) gw.U_out[e] = sU[e];
     }
     if (tid < 256) {
         const int ol = tid >> 4, ot = tid & 15;  // output (row n0 + ol, token ot)
@@ -427,7 +447,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                 for (int j = 0; j < r; ++j) lora = __builtin_fmaf(sU[ot * r + j], bf16_to_f32(sB[ol * r + j]), lora);
                 sum += p.scale * lora;
             }
-            p.Y[ot * N + n] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
+            gw.Y[ot * N + n] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
         }
     }
 }
@@ -453,7 +473,7 @@ GemvUPlan gemv_u_plan(int64_t T, int64_t K, int r) {
 size_t gemv_ws_bytes(int64_t T, int64_t K, int r) {
     if (r <= 0) return 0;
     const GemvUPlan u = gemv_u_plan(T, K, r);
-    return u.part_bytes + (kGemvSub + 1) * sizeof(uint64_t);
+    return (u.part_bytes + (kGemvSub + 1) * sizeof(uint64_t) + 255) / 256 * 256;
 }
 
 namespace {
@@ -483,25 +503,19 @@ void launch_gemv_tx(int ns, dim3 grid, const GemvArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const uint16_t* A,
-                const uint16_t* B, int r, float scale, uint16_t* Y, float* U_out, void* ws, hipStream_t stream) {
+int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t T, int64_t K, int r, float scale,
+                      void* ws, hipStream_t stream) {
+    if (nw < 1 || nw > kGemvGroup) return set_error(QL_ERR_SHAPE, "dequant GEMV: %d weights in one launch", nw);
     GemvArgs g{};
-    g.w = w;
     g.X = X;
     g.T = static_cast<int>(T);
-    g.N = N;
     g.K = K;
-    g.B = B;
     g.r = r;
     g.scale = scale;
-    g.Y = Y;
-    g.A = A;
-    g.U_out = U_out;
-    g.spin = 0;
+    g.ngroup = nw;
+    int nu = 0;
     if (r > 0) {
         const GemvUPlan u = gemv_u_plan(T, K, r);
-        g.uword = static_cast<uint64_t*>(ws);
-        g.done = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + u.part_bytes);
         g.token = next_token() & ((uint64_t{1} << 40) - 1);
         g.tag = static_cast<uint32_t>(g.token % 0xFFFFFFFFull) + 1u;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -509,14 +523,38 @@ int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_
         g.count_done = cs != hipStreamCaptureStatusNone ? 1 : 0;
         g.rt = u.rt;
         g.nks = u.nks;
-        g.nu = u.rt * u.nks;
+        nu = u.rt * u.nks;
         // QLORA_NF4_GEMV_SPIN=n: loads of the U words before computing U locally
         // (0: every workgroup computes U itself)
         const char* e = std::getenv("QLORA_NF4_GEMV_SPIN");
         g.spin = e ? std::max(0, std::atoi(e)) : (1 << 14);
     }
+    // grid: the U workgroups of every weight, then the row workgroups of every weight
+    const size_t wsb = gemv_ws_bytes(T, K, r);
+    int64_t total = static_cast<int64_t>(nu) * nw;
+    g.nu_all = static_cast<int>(total);
+    for (int i = 0; i < nw; ++i) {
+        GemvWeight& gw = g.g[i];
+        gw.w = calls[i].w;
+        gw.N = calls[i].N;
+        gw.A = calls[i].A;
+        gw.B = calls[i].B;
+        gw.Y = calls[i].Y;
+        gw.U_out = calls[i].U_out;
+        if (r > 0) {
+            char* wbase = static_cast<char*>(ws) + wsb * i;
+            gw.uword = reinterpret_cast<uint64_t*>(wbase);
+            gw.done = reinterpret_cast<uint64_t*>(wbase + gemv_u_plan(T, K, r).part_bytes);
+        }
+        gw.nu = nu;
+        gw.ub = nu * i;
+        gw.nrow = static_cast<int>(ceil_div(calls[i].N, kGemvRows));
+        gw.rb = static_cast<int>(total);
+        total += gw.nrow;
+    }
+    if (total >= (int64_t{1} << 31)) return set_error(QL_ERR_SHAPE, "dequant GEMV: grid too large");
     timer_begin(QL_KERNEL_GEMV, stream);
-    const dim3 grid(static_cast<uint32_t>(g.nu + ceil_div(N, kGemvRows)));
+    const dim3 grid(static_cast<uint32_t>(total));
     const int64_t nbs = ceil_div(K / 64, 4);
     const int ns = static_cast<int>(std::min<int64_t>(ceil_div(nbs, kGemvWaves), 1 << 20));
     const int tx = T <= 2 ? 1 : (T <= 4 ? 2 : (T <= 8 ? 4 : 8));
@@ -528,6 +566,12 @@ int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_
     }
     timer_end(QL_KERNEL_GEMV, stream);
     return check_launch("dequant GEMV");
+}
+
+int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const uint16_t* A,
+                const uint16_t* B, int r, float scale, uint16_t* Y, float* U_out, void* ws, hipStream_t stream) {
+    const GemvCall c{w, N, A, B, Y, U_out};
+    return launch_gemv_group(&c, 1, X, T, K, r, scale, ws, stream);
 }
 
 }  // namespace qlnf4

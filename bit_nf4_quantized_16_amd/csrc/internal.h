@@ -96,6 +96,20 @@ int launch_pad_copy(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* d
 size_t gemv_ws_bytes(int64_t T, int64_t K, int r);
 int launch_gemv(const NF4Dev& w, const uint16_t* X, int64_t T, int64_t N, int64_t K, const uint16_t* A,
                 const uint16_t* B, int r, float scale, uint16_t* Y, float* U_out, void* ws, hipStream_t stream);
+// Up to four such weights that share X (the same K, T, rank and scale) in
+// one launch; weight i uses gemv_ws_bytes(T, K, r) bytes of ws from i times
+// that size on (a multiple of 256).
+struct GemvCall {
+    NF4Dev w;
+    int64_t N;
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* Y;
+    float* U_out;
+};
+constexpr int kGemvMaxGroup = 4;
+int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t T, int64_t K, int r, float scale,
+                      void* ws, hipStream_t stream);
 
 // Tile / split-K plan of the dequant GEMMs for an MA x T output with a
 // reduction of RED, and the fp32 workspace its split partials need.

@@ -253,6 +253,31 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_group — qlora_linear_fwd for up to four layers that read
+ * the same input X (adapters sit on every attention projection, q/k/v among
+ * them, and sometimes on the MLP: [aivaro] §10), e.g. q/k/v or gate/up.
+ *
+ *   w[i], A[i], B[i], Y[i], U_out[i]   per layer i < nw, as qlora_linear_fwd;
+ *          w, A, B, Y and U_out are host arrays of nw pointers (A and B may
+ *          be NULL when r == 0, U_out NULL or U_out[i] NULL to skip U)
+ *   nw     1..4 layers; all share K = w[i]->cols, r and scale
+ *   ws     workspace of qlora_linear_fwd_group_workspace(rows, nw, K, T, r)
+ *          bytes, rows = the nw values w[i]->rows
+ *
+ * T <= 16 runs all layers in one dequant-GEMV launch (each layer's U and
+ * outputs bitwise equal to qlora_linear_fwd's); larger T runs the layers one
+ * after another through qlora_linear_fwd on the one workspace. Each Y[i] and
+ * U_out[i] must not alias an input or another output.
+ * Errors: as qlora_linear_fwd, plus QL_ERR_SHAPE for nw outside 1..4 or
+ * layers of different K; the workspace query returns 0 for invalid sizes.
+ */
+size_t qlora_linear_fwd_group_workspace(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r);
+int qlora_linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,
+                           const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                           uint16_t* const* Y, float* const* U_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
  * qlora_linear_fwd_dropout — the forward with dropout on the adapter input
  * ([codex] §3.4: dropout on the adapters, 0.05-0.1 for small data; [aivaro]
  * §11: lora_dropout = 0.05). Inverted dropout of the adapter branch only, the

@@ -146,6 +146,59 @@ def test_linear_fwd_rejects(lib):
     assert call(T=0) == L.QL_OK  # empty batch: no-op, nothing launched
 
 
+def test_linear_fwd_group_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    def descs(shapes):
+        ws = []
+        for rows, cols in shapes:
+            w = L.QlNf4Weight()
+            w.rows, w.cols, w.blocksize, w.dq_blocksize = rows, cols, 64, 256
+            w.packed, w.absmax, w.c8, w.dq_scale, w.dq_mean = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+            ws.append(w)
+        return ws
+
+    def ptrs(vals, n):
+        return (ctypes.c_void_p * max(n, 1))(*vals)
+
+    def rows(*r):
+        return (ctypes.c_int64 * len(r))(*r)
+
+    # decode sizes: one GEMV workspace slice per layer; larger T: the largest
+    # single-layer workspace, the layers running one after another
+    one = lib.qlora_linear_fwd_workspace(256, 256, 16, 8)
+    assert lib.qlora_linear_fwd_group_workspace(rows(256, 256, 512), 3, 256, 16, 8) == 3 * one
+    assert lib.qlora_linear_fwd_group_workspace(rows(256, 512), 2, 256, 64, 8) == max(
+        lib.qlora_linear_fwd_workspace(256, 256, 64, 8), lib.qlora_linear_fwd_workspace(512, 256, 64, 8))
+    assert lib.qlora_linear_fwd_group_workspace(rows(256), 0, 256, 16, 8) == 0
+    assert lib.qlora_linear_fwd_group_workspace(rows(256, 256, 256, 256, 256), 5, 256, 16, 8) == 0
+    assert lib.qlora_linear_fwd_group_workspace(rows(256, 0), 2, 256, 16, 8) == 0
+    assert lib.qlora_linear_fwd_group_workspace(None, 1, 256, 16, 8) == 0
+
+    def call(shapes=((256, 256), (512, 256)), nw=None, T=4, r=8, X=P, A=True, B=True, Y=P, wsb=None, ws=P):
+        ds = descs(shapes)
+        n = len(ds) if nw is None else nw
+        wp = ptrs([ctypes.addressof(d) for d in ds], len(ds))
+        need = lib.qlora_linear_fwd_group_workspace(rows(*[d.rows for d in ds]), len(ds), ds[0].cols, T, r)
+        return lib.qlora_linear_fwd_group(wp, n, X, T, ptrs([P2] * len(ds), len(ds)) if A else None,
+                                          ptrs([P3] * len(ds), len(ds)) if B else None, r, 2.0,
+                                          ptrs([Y] * len(ds), len(ds)), None, ws,
+                                          need if wsb is None else wsb, None)
+
+    assert call(nw=0) == L.QL_ERR_SHAPE
+    assert call(shapes=((256, 256),) * 5) == L.QL_ERR_SHAPE
+    assert call(shapes=((256, 256), (256, 320))) == L.QL_ERR_SHAPE  # layers of different K
+    assert call(shapes=((256, 256), (100, 256))) == L.QL_ERR_SHAPE  # N % 8
+    assert call(r=129) == L.QL_ERR_SHAPE
+    assert call(A=False) == L.QL_ERR_NULL
+    assert call(X=None) == L.QL_ERR_NULL
+    assert call(Y=MIS) == L.QL_ERR_ALIGN
+    assert call(wsb=0) == L.QL_ERR_WORKSPACE
+    assert call(T=64, wsb=0) == L.QL_ERR_WORKSPACE  # the one-after-another path checks it too
+    assert call(T=0) == L.QL_OK
+    assert lib.qlora_linear_fwd_group(None, 1, P, 4, None, None, 0, 1.0, None, None, None, 0, None) == L.QL_ERR_NULL
+
+
 def test_linear_bwd_rejects(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 

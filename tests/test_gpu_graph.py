@@ -145,3 +145,39 @@ def test_decode_graph_replays_with_new_inputs(qn, T):
         Ye, Ue = qn.qlora_linear_fwd(w, xs[rep], A, B, case.scale)
         torch.cuda.synchronize()
         assert torch.equal(Y, Ye) and torch.equal(U, Ue), "replay %d differs from the eager call" % rep
+
+
+def test_grouped_decode_graph_replays_with_new_inputs(qn):
+    """The grouped decode call captured once: each layer keeps its own tagged
+    counters in its slice of the workspace; every replay with a new x gives
+    the eager single-layer results."""
+    T, K, r = 1, 4096, 16
+    ws, As, Bs = [], [], []
+    for i, N in enumerate((4096, 1024, 1024)):
+        W = workloads.normal_weight(N, K, 0.02, seed=60 + i)
+        case = workloads.lora_case("graph_group%d" % i, W, T, r, 32.0, 1 / K, 0.05, seed=60 + i)
+        ws.append(qn.quantize_weight(W.cuda()))
+        As.append(case.A.cuda())
+        Bs.append(case.B.cuda())
+    s = case.scale
+    X = torch.empty(T, K, dtype=torch.bfloat16, device="cuda")
+    xs = [workloads.bf16_normal((T, K), 1.0, seed=70 + i).cuda() for i in range(4)]
+    X.copy_(xs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qn.qlora_linear_fwd_group(ws, X, As, Bs, s)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = qn.qlora_linear_fwd_group(ws, X, As, Bs, s)
+    for rep in range(1, 4):
+        X.copy_(xs[rep])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, w in enumerate(ws):
+            Ye, Ue = qn.qlora_linear_fwd(w, xs[rep], As[i], Bs[i], s)
+            torch.cuda.synchronize()
+            assert torch.equal(outs[i][0], Ye) and torch.equal(outs[i][1], Ue), "replay %d, layer %d" % (rep, i)

@@ -121,6 +121,36 @@ def test_gemv_local_u_is_bitwise_the_shared_one(qn, monkeypatch, N, K, T, r):
     assert torch.equal(Y1, Y2) and torch.equal(U1, U2)
 
 
+@pytest.mark.parametrize("shapes,K,T,r", [(((264, 1024), (72, 1024), (520, 1024)), 1024, 1, 16),
+                                           (((200, 4160), (8, 4160)), 4160, 5, 40),
+                                           (((96, 1536), (136, 1536), (24, 1536), (264, 1536)), 1536, 16, 8),
+                                           (((264, 320), (72, 320)), 320, 3, 0),
+                                           (((4096, 4096),) * 3, 4096, 1, 16),
+                                           (((11008, 4096),) * 2, 4096, 16, 64),
+                                           (((256, 320), (520, 320)), 320, 40, 16)])
+def test_fwd_group_is_bitwise_the_single_calls(qn, shapes, K, T, r):
+    """Layers that share X in one grouped call give the same Y and U, bit for
+    bit, as one qlora_linear_fwd call each (T <= 16: one GEMV launch over all
+    of them; T = 40: the layers one after another)."""
+    ws, As, Bs = [], [], []
+    for i, (N, _) in enumerate(shapes):
+        W = workloads.normal_weight(N, K, 0.02, seed=N + i)
+        # (r = 0: the case's adapters of rank 1 are not passed)
+        case = workloads.lora_case("grp%d" % i, W, T, max(r, 1), 2.0 * max(r, 1), 1 / K, 0.05, seed=T + 11 * i)
+        ws.append(qn.quantize_weight(W.cuda()))
+        As.append(case.A.cuda())
+        Bs.append(case.B.cuda())
+        if i == 0:
+            X, s = case.X.cuda(), case.scale
+    outs = qn.qlora_linear_fwd_group(ws, X, As if r else None, Bs if r else None, s)
+    for i, w in enumerate(ws):
+        Y1, U1 = qn.qlora_linear_fwd(w, X, As[i] if r else None, Bs[i] if r else None, s)
+        Y2, U2 = outs[i]
+        torch.cuda.synchronize()
+        assert torch.equal(Y1, Y2), "layer %d: Y differs" % i
+        assert (U1 is None and U2 is None) or torch.equal(U1, U2), "layer %d: U differs" % i
+
+
 def test_without_double_quant(qn):
     case = workloads.tiny_256()
     _run(qn, case, dq=False)
