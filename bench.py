@@ -483,6 +483,39 @@ def run_suite(torch, qn):
                                        "graph_ms": round(graph_s * 1e3, 3),
                                        "graph_GB/s": round(nbytes / graph_s / 1e9, 1),
                                        "graph_frac": round(nbytes / graph_s / PEAK_HBM, 4)}
+
+        # the same pass with the layers that read the same x grouped into one
+        # launch (q/k/v and gate/up): 4 launches per transformer layer, not 7
+        groups = []
+        for layer in range(32):
+            ws_ = [w for _, _, _, w in stack[7 * layer:7 * layer + 7]]
+            groups += [ws_[0:3], ws_[3:4], ws_[4:6], ws_[6:7]]
+
+        def grouped_pass():
+            for ws_ in groups:
+                k = ws_[0].cols
+                qn.qlora_linear_fwd_group(ws_, Xs[k], [lora[(w.rows, k)][0] for w in ws_],
+                                          [lora[(w.rows, k)][1] for w in ws_], 2.0, save_u=False)
+
+        tg.arm()
+        grouped_pass()
+        torch.cuda.synchronize()
+        ngg, msgg = tg.read()
+        tg.disarm()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            grouped_pass()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            grouped_pass()
+        ggraph_s = timed(graph.replay, reps=5)
+        del graph
+        res["c4_gemv_pass_T%d" % T].update({"grouped_launches": ngg, "grouped_kernel_ms": round(msgg, 3),
+                                            "grouped_graph_ms": round(ggraph_s * 1e3, 3),
+                                            "grouped_graph_GB/s": round(nbytes / ggraph_s / 1e9, 1),
+                                            "grouped_graph_frac": round(nbytes / ggraph_s / PEAK_HBM, 4)})
         del outs
 
     def gemm_rows(shapes, T, r, alpha, std, seed0, weights=None):
