@@ -176,7 +176,16 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     };
 
     // ---- weight codes: registers, two steps ahead ----------------------------
-    const int wrow = tid / TPR, wcol = (tid % TPR) * CPT;
+    // dX with 8 threads per weight-tile row: the rows are 576 B apart (16
+    // banks mod 64) and a row's threads 64 B apart, so with the plain order
+    // (8 lanes to a row) the threads of a row four apart write the same banks
+    // on every 16-byte store. Lanes 0-15 of a wave take 4 rows x threads 0-3
+    // instead (lanes 16-31 the same rows, threads 4-7): with the column
+    // swizzle of the layout their 16 stores fall in 16 different 4-bank
+    // groups. The wave still loads the same 8 code rows, only in another
+    // lane order.
+    const int wrow = (DX && TPR == 8) ? (tid >> 6) * 8 + (((tid >> 5) & 1) << 2) + ((tid >> 2) & 3) : tid / TPR;
+    const int wcol = ((DX && TPR == 8) ? (((tid >> 4) & 1) << 2) + (tid & 3) : tid % TPR) * CPT;
     auto gcodes = [&](int step, Codes<CC>& cs) {
         const int64_t r0 = static_cast<int64_t>(step) * kStep;
         int64_t e;
