@@ -55,6 +55,13 @@ namespace qlnf4 {
 // finds no word of the previous one. An eager launch has a token of its own
 // and skips the count.
 //
+// One launch can serve up to kGemvGroup layers that read the same x (q/k/v,
+// gate/up): the argument holds a descriptor per layer (weight, adapters,
+// outputs, its own workspace slice of words and counters), the grid puts all
+// layers' U workgroups first and then all their row workgroups, and each
+// workgroup finds its layer from its index. Per layer the arithmetic and its
+// order are those of a launch for that layer alone.
+//
 // Lanes of tokens >= T read token T-1 and their outputs are dropped; rows
 // past N read row N-1 and are dropped.
 // ===========================================================================
