@@ -48,12 +48,10 @@ namespace qlnf4 {
 // so the U workgroups never wait on anything; should the retries still run
 // out, the workgroup computes U itself from the same partial products in the
 // same order (bit-identical). A launch being captured into a graph (its
-// replays reuse the token) also counts its row workgroups done, in two
-// levels (kGemvSub counters for the workgroups b with b % kGemvSub = k, and
-// one for the kGemvSub groups; single atomic adds, as atomics on one word are
-// served one after another); the last one clears the words, so a replay
-// finds no word of the previous one. An eager launch has a token of its own
-// and skips the count.
+// replays reuse the token) also counts its U and row workgroups done (a
+// token-tagged compare-and-swap count in two levels); the last one clears
+// the words, so a replay finds no word of the previous one. An eager launch
+// has a token of its own and skips the count.
 //
 // One launch can serve up to kGemvGroup layers that read the same x (q/k/v,
 // gate/up): the argument holds a descriptor per layer (weight, adapters,
@@ -83,7 +81,7 @@ struct GemvWeight {
     uint16_t* Y;
     float* U_out;     // [T, r] fp32 = X A^T, or null
     uint64_t* uword;  // [nks][T][r]: slice ks of U, tag << 32 | fp32 bits (r > 0)
-    uint64_t* done;   // [kGemvSub + 1]: token << 24 | count; row workgroups done with U (r > 0)
+    uint64_t* done;   // [kGemvSub + 1]: token << 24 | count of workgroups done with the words (r > 0)
     int nu, nrow;     // its U and row workgroups
     int ub, rb;       // the grid index of its first U and first row workgroup
 };
@@ -96,7 +94,7 @@ struct GemvArgs {
     float scale;
     uint64_t token;   // 40 bits
     uint32_t tag;     // nonzero, from the token (a cleared word is 0)
-    int count_done;   // the launch is captured: count the row workgroups, clear the words
+    int count_done;   // the launch is captured: count the workgroups done, the last clears the words
     int nks, rt;      // U workgroups of a weight = rt (16-row tiles of A) x nks (slices of kGemvUSteps steps)
     int spin;         // loads of the U words before computing U locally
     int ngroup;       // weights in this launch
@@ -228,18 +226,48 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
         return v;
     };
 
+    // A captured launch (its replays reuse the token and tag) counts every
+    // workgroup of the weight that touches the U words: a U workgroup once its
+    // words are stored, a row workgroup once it has U (from the words or
+    // computed itself). The last of them clears the words, so a replay finds
+    // none of the previous replay's; as every U workgroup counts too, no word
+    // can be stored after the clear. Counters hold token << 24 | count; one
+    // holding another token counts as zero, and each counter's last arrival
+    // leaves it at zero (compare-and-swap), so nothing needs resetting at
+    // launch start. Two levels: workgroup i counts on counter i % kGemvSub,
+    // the last on each of those on counter kGemvSub (atomics on one word are
+    // served one after another).
+    auto count_done_and_clear = [&](int i) {
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): this thread's word accesses are done
+        __syncthreads();
+        if (tid == 0) {
+            auto arrive = [&](uint64_t* c, int n) {
+                uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                int arrived;
+                uint64_t nv;
+                do {
+                    arrived = static_cast<int>((old >> 24) == p.token ? (old & 0xFFFFFFu) : 0u) + 1;
+                    nv = (p.token << 24) | static_cast<uint64_t>(arrived == n ? 0 : arrived);
+                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT));
+                return arrived == n;
+            };
+            const int total = gw.nu + gw.nrow;
+            const int k = i % kGemvSub, groups = std::min(total, kGemvSub);
+            const int in_k = total / kGemvSub + (k < total % kGemvSub ? 1 : 0);  // arrivals on counter k
+            s_last = arrive(gw.done + k, in_k) && arrive(gw.done + kGemvSub, groups);
+        }
+        __syncthreads();
+        if (s_last)
+            for (int e = tid; e < p.nks * T * r; e += 512)
+                __hip_atomic_store(gw.uword + e, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
     if (is_u) {
         // a U workgroup: its slice of one 16-row tile of U^T, published
         const int local = bid - gw.ub;
         const int jt = local % p.rt, ks = local / p.rt;
         put_tile(u_unit(jt, ks));
-        if (tid == 0 && local == 0 && p.count_done) {
-            // U workgroup 0 starts the done count of this launch before its
-            // words: the row workgroups count only after they have all words
-            for (int k = 0; k <= kGemvSub; ++k)
-                __hip_atomic_store(gw.done + k, p.token << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
-        }
         __syncthreads();
         if (tid < 256) {
             const int j = 16 * jt + (tid >> 4), t = tid & 15;
@@ -249,6 +277,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                                    (uint64_t{p.tag} << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
+        if (p.count_done) count_done_and_clear(local);
         return;
     }
 
@@ -422,25 +451,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                     }
                 }
         }
-        if (tid == 0 && p.count_done) {
-            const int nrow = gw.nrow, b = bid - gw.rb;
-            const int k = b % kGemvSub, groups = std::min(nrow, kGemvSub);
-            const int in_k = nrow / kGemvSub + (k < nrow % kGemvSub ? 1 : 0);  // workgroups counted on k
-            int last = 0;
-            uint64_t old = __hip_atomic_fetch_add(gw.done + k, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((old >> 24) == p.token && static_cast<int>(old & 0xFFFFFFu) + 1 == in_k) {
-                old = __hip_atomic_fetch_add(gw.done + kGemvSub, uint64_t{1}, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-                last = (old >> 24) == p.token && static_cast<int>(old & 0xFFFFFFu) + 1 == groups;
-            }
-            s_last = last;
-        } else if (tid == 0) {
-            s_last = 0;
-        }
-        __syncthreads();
-        if (s_last)  // the last row workgroup: clear the words for the next launch
-            for (int e = tid; e < p.nks * nur; e += 512)
-                __hip_atomic_store(gw.uword + e, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.count_done)
+            count_done_and_clear(gw.nu + (bid - gw.rb));  // (its barriers also order sU)
+        else
+            __syncthreads();  // sU is complete
         if (gw.U_out != nullptr && n0 == 0)
             for (int e = tid; e < nur; e += 512) gw.U_out[e] = sU[e];
     }

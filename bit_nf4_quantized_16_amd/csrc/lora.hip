@@ -346,8 +346,11 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
             // token counts as zero) adds the partials in split order, so the
             // result does not depend on the arrival order. The last arrival
             // leaves the count at zero, so a launch replayed with the same
-            // token (a captured graph) starts from zero as well. The wait
-            // orders the partial stores before the count.
+            // token (a captured graph) starts from zero as well. Every thread
+            // waits for its partial stores (vmcnt counts per wave) before the
+            // barrier; the count is an agent-scope acquire-release exchange, so
+            // those stores happen before it and the last split's loads of the
+            // partials after it.
             __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
             __syncthreads();
             if (tid == 0) {
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
                 do {
                     arrived = static_cast<int>(((old >> 8) == p.token) ? (old & 0xFFu) : 0u) + 1;
                     nv = (p.token << 8) | static_cast<uint64_t>(arrived == nsplit ? 0 : arrived);
-                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT));
                 s_last = arrived == nsplit;
             }

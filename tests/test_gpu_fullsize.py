@@ -13,6 +13,7 @@ import torch
 import oracle
 import workloads
 from gpu_util import TOL, bf16_to_np, f32_to_np, normwise_rel_err, oracle_cols, oracle_constants, oracle_rows
+from gpu_util import oracle_weight
 from gpu_util import sample_indices, u8_to_np
 
 pytestmark = pytest.mark.gpu
@@ -27,6 +28,7 @@ def qn():
 
 
 CASES = {
+    "attn_4096x4096_T1_r16": lambda: workloads.attn_proj_7b(1),
     "attn_4096x4096_T16_r16": lambda: workloads.attn_proj_7b(16),
     "mlp_gate_11008x4096_T1024_r16": lambda: workloads.mlp_7b("gate"),
     "mlp_down_4096x11008_T1024_r16": lambda: workloads.mlp_7b("down"),
@@ -81,3 +83,33 @@ def test_full_size_sampled_outputs(qn, name):
     print(name, {k: "%.2e" % v for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= TOL, "%s: %s error %.3e > %.0e" % (name, k, v, TOL)
+
+
+@pytest.mark.parametrize("zero_w", [False, True])
+def test_decode_full_4096x4096_every_output(qn, zero_w):
+    """The decode forward at the 4096 x 4096 attention shape (0.1 % outliers
+    x20, r = 16, alpha = 32) at T = 1 and T = 16, in the launch configuration
+    the benchmark times: every packed code bit for bit, and every element of
+    Y and U against the oracle. With an all-zero weight (every code 7) only
+    the adapter branch is left, so Y = s (X A^T) B^T checks that branch at
+    this size, where it is under 1 % of H otherwise."""
+    case = workloads.attn_proj_7b(16)
+    W = torch.zeros(4096, 4096) if zero_w else case.W
+    print("decode full 4096x4096 zero_w=%s" % zero_w, flush=True)
+    w = qn.quantize_weight(W.cuda(), double_quant=True)
+    A, B = case.A.cuda(), case.B.cuda()
+    ref = oracle_weight(W.numpy())
+    if not zero_w:
+        assert np.array_equal(u8_to_np(w.packed), ref["packed"]), "packed NF4 codes differ"
+    An, Bn = bf16_to_np(case.A), bf16_to_np(case.B)
+    for T in (1, 16):
+        X = case.X[:T].contiguous()
+        Y, U = qn.qlora_linear_fwd(w, X.cuda(), A, B, case.scale)
+        torch.cuda.synchronize()
+        H, Uo = oracle.lora_forward(bf16_to_np(X), ref["wd"], An, Bn, case.scale)
+        eh, eu = normwise_rel_err(bf16_to_np(Y), H), normwise_rel_err(f32_to_np(U), Uo)
+        print("T=%d H %.2e U %.2e" % (T, eh, eu), flush=True)
+        assert eh <= TOL and eu <= TOL, (T, eh, eu)
+        if zero_w:
+            # nothing but the adapter term: fp32 sums of bf16 products, one bf16 rounding
+            assert eh < 1e-2

@@ -115,11 +115,17 @@ def test_two_stream_graph_matches_serial(qn):
             assert torch.equal(a, b), "replay %d: output %d differs from the serial run" % (rep, i)
 
 
+@pytest.mark.parametrize("spin", [None, "1"])
 @pytest.mark.parametrize("T", [1, 16])
-def test_decode_graph_replays_with_new_inputs(qn, T):
+def test_decode_graph_replays_with_new_inputs(qn, monkeypatch, T, spin):
     """A captured decode call (the GEMV keeps token-tagged counters in its
     workspace, and a replay reuses the token): replays with new x give the
-    eager results for that x."""
+    eager results for that x. With QLORA_NF4_GEMV_SPIN=1 the row workgroups
+    give up waiting for the shared U almost at once and compute it
+    themselves, so their done counts and the U workgroups' stores race with
+    each other: the words must still be cleared after the last of them."""
+    if spin is not None:
+        monkeypatch.setenv("QLORA_NF4_GEMV_SPIN", spin)
     N, K, r = 4096, 4096, 16
     W = workloads.normal_weight(N, K, 0.02, seed=41).cuda()
     case = workloads.lora_case("graph_decode", W.cpu(), T, r, 32.0, 1 / K, 0.05, seed=41)
@@ -137,20 +143,24 @@ def test_decode_graph_replays_with_new_inputs(qn, T):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         Y, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
-    for rep in range(1, 4):
-        X.copy_(xs[rep])
+    for rep in range(1, 7):
+        X.copy_(xs[rep % 4])
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        Ye, Ue = qn.qlora_linear_fwd(w, xs[rep], A, B, case.scale)
+        Ye, Ue = qn.qlora_linear_fwd(w, xs[rep % 4], A, B, case.scale)
         torch.cuda.synchronize()
         assert torch.equal(Y, Ye) and torch.equal(U, Ue), "replay %d differs from the eager call" % rep
 
 
-def test_grouped_decode_graph_replays_with_new_inputs(qn):
+@pytest.mark.parametrize("spin", [None, "1"])
+def test_grouped_decode_graph_replays_with_new_inputs(qn, monkeypatch, spin):
     """The grouped decode call captured once: each layer keeps its own tagged
     counters in its slice of the workspace; every replay with a new x gives
-    the eager single-layer results."""
+    the eager single-layer results (also when the row workgroups give up
+    waiting for U almost at once)."""
+    if spin is not None:
+        monkeypatch.setenv("QLORA_NF4_GEMV_SPIN", spin)
     T, K, r = 1, 4096, 16
     ws, As, Bs = [], [], []
     for i, N in enumerate((4096, 1024, 1024)):

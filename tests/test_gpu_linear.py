@@ -77,7 +77,13 @@ def test_ragged_shapes_and_ranks(qn, N, K, T, r):
                                      (24, 1472, 16, 8), (24, 1536, 16, 8), (40, 11008, 2, 16), (40, 11008, 3, 16),
                                      # more 256-wide steps per wave than are issued up front (the ring of
                                      # loads) for each width of x: T <= 2, <= 4, <= 8
-                                     (24, 16448, 1, 16), (24, 8256, 4, 8), (24, 6208, 8, 8)])
+                                     (24, 16448, 1, 16), (24, 8256, 4, 8), (24, 6208, 8, 8),
+                                     # 2..5 steps per wave, all issued up front (K = 4096 .. 10240),
+                                     # for the three narrowest widths of x (T = 1, 3, 6); the widths
+                                     # whose register budget is smaller take the ring there instead
+                                     (40, 4096, 1, 16), (40, 6144, 1, 16), (40, 8192, 1, 16), (40, 10240, 1, 16),
+                                     (40, 4096, 3, 16), (40, 6144, 3, 16), (40, 8192, 3, 16), (40, 10240, 3, 16),
+                                     (40, 4096, 6, 16), (40, 6144, 6, 16), (40, 8192, 6, 16), (40, 10240, 6, 16)])
 def test_gemv_ranks_and_ragged_k(qn, N, K, T, r):
     W = workloads.normal_weight(N, K, 0.02, seed=N + 3 * K)
     case = workloads.lora_case("gemv_N%dK%dT%dr%d" % (N, K, T, r), W, T, r, 2.0 * max(r, 1), 1 / K, 0.05,

@@ -129,6 +129,74 @@ def test_codes_equal_midpoint_rule_exhaustively_near_every_midpoint():
     assert np.array_equal(got, want.astype(np.uint8))
 
 
+def _exact_nearest_codes(x):
+    """Nearest NF4 value to each fp32 x by brute force in exact arithmetic:
+    argmin over the sixteen codes of |x - T_c|, the lower code on a tie
+    (np.argmin keeps the first minimum). No midpoint appears anywhere.
+
+    Every fp32 of magnitude >= 2^-37 and every table value is an integer
+    multiple of 2^-60 below 2^60, so the distances are exact in int64; the
+    few smaller |x| are done with Fractions."""
+    x = np.asarray(x, dtype=np.float32).ravel()
+    scale = 2.0**60
+    ti = (T.astype(np.float64) * scale).astype(np.int64)
+    assert np.array_equal(ti.astype(np.float64), T.astype(np.float64) * scale)
+    small = np.abs(x) < np.float32(2.0**-37)
+    out = np.empty(x.size, dtype=np.uint8)
+    big = x[~small].astype(np.float64) * scale
+    xi = big.astype(np.int64)
+    assert np.array_equal(xi.astype(np.float64), big)  # the scaling is exact
+    for s in range(0, xi.size, 1 << 16):
+        d = np.abs(xi[s : s + (1 << 16), None] - ti[None, :])
+        out[np.flatnonzero(~small)[s : s + (1 << 16)]] = np.argmin(d, axis=1)
+    tf = [Fraction(float(t)) for t in T]
+    for i in np.flatnonzero(small):
+        xf = Fraction(float(x[i]))
+        dist = [abs(xf - t) for t in tf]
+        out[i] = dist.index(min(dist))
+    return out
+
+
+def test_codes_equal_exact_argmin_exhaustively_near_every_midpoint_and_code():
+    """Every fp32 within 2000 ulps of every midpoint and of every code value,
+    plus random and special values: the oracle's code equals the exact
+    brute-force nearest value with ties to the lower code (an independent
+    formulation: distances to all sixteen values, not a count of midpoints)."""
+    vals = []
+    anchors = [(float(T[j]) + float(T[j + 1])) / 2 for j in range(15)] + [float(t) for t in T]
+    for m in anchors:
+        c = int(np.float32(m).view(np.int32))
+        r = np.arange(-2000, 2001, dtype=np.int64) + c
+        v = r.astype(np.int32).view(np.float32)
+        vals.append(v[np.isfinite(v) & (np.abs(v) <= 1.0)])
+    vals.append(np.random.default_rng(321).uniform(-1, 1, 200_000).astype(np.float32))
+    vals.append(np.array([0.0, -0.0, 1e-45, -1e-45, 1e-38, -1e-38, 3e-12, -3e-12, 1.0, -1.0], dtype=np.float32))
+    x = np.concatenate(vals).astype(np.float32)
+    want = _exact_nearest_codes(x)
+    got = _codes_of(x)
+    assert np.array_equal(got, want)
+    # the set really contains exact ties (fp32 midpoints), so the tie rule is exercised
+    ties = [m for m in anchors[:15] if float(np.float32(m)) == m]
+    assert ties and all(_exact_nearest_codes([m])[0] == anchors.index(m) for m in ties)
+
+
+def test_exact_argmin_pin_catches_planted_mistakes():
+    """The brute-force pin is sharp enough to see a plausible slip: ties sent
+    to the upper code, or midpoints taken in fp32 instead of exactly."""
+    mids = np.array([(float(T[j]) + float(T[j + 1])) / 2 for j in range(15)])
+    x = []
+    for m in mids:
+        c = int(np.float32(m).view(np.int32))
+        x.append((np.arange(-3, 4, dtype=np.int64) + c).astype(np.int32).view(np.float32))
+    x = np.concatenate(x)
+    want = _exact_nearest_codes(x)
+    ties_up = np.searchsorted(mids, x.astype(np.float64), side="right")
+    assert not np.array_equal(ties_up.astype(np.uint8), want)
+    mids32 = mids.astype(np.float32)
+    rounded = np.sum(x[:, None] > mids32[None, :], axis=1)
+    assert not np.array_equal(rounded.astype(np.uint8), want)
+
+
 def test_exact_midpoint_tie_goes_to_lower_code():
     mids = _exact_midpoints()
     exact = [m for m in mids if float(np.float32(m)) == m]
