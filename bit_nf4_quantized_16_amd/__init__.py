@@ -218,6 +218,24 @@ def qlora_linear_fwd(w, X, A=None, B=None, scale=1.0, save_u=True, out=None, kee
     return Y, U
 
 
+def qlora_linear_fwd_noalloc(w, X, A=None, B=None, scale=1.0, save_u=True, out=None, U_out=None):
+    """qlora_linear_fwd through the entry point that allocates nothing (its
+    scratch is a device array of the library, shared by every call on a GPU).
+    Pass ``out`` (and ``U_out``) to keep this function from allocating the
+    outputs as well. Returns (Y, U or None)."""
+    T = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = X.device
+    Y = out if out is not None else torch.empty(T, w.rows, dtype=torch.bfloat16, device=dev)
+    U = U_out
+    if U is None and save_u and r > 0:
+        U = torch.empty(T, r, dtype=torch.float32, device=dev)
+    d = w.descriptor()
+    _check(lib.qlora_linear_fwd_noalloc(ctypes.byref(d), _ptr(_bits(X)), T, _ptr(_bits(A)), _ptr(_bits(B)), r,
+                                        float(scale), _ptr(Y), _ptr(U), _stream()))
+    return Y, U
+
+
 def qlora_linear_fwd_group(ws, X, As=None, Bs=None, scale=1.0, save_u=True):
     """qlora_linear_fwd for up to four layers that read the same X (q/k/v,
     gate/up): one launch when T <= 16. ``ws`` NF4Weights sharing ``cols``;

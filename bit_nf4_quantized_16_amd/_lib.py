@@ -32,6 +32,7 @@ QL_KERNEL_MERGE = 8
 QL_KERNEL_QERROR = 9
 QL_KERNEL_KEEP_APPLY = 10
 QL_KERNEL_DX_KEEP = 11
+QL_NOALLOC_SCRATCH_BYTES = 96 << 20  # include/qlora_nf4.h
 QL_GRID_NF4 = 0
 QL_GRID_UNIFORM = 1
 
@@ -72,6 +73,7 @@ SIGNATURES = {
     "q4_quant_error": (_I, [_P, _I, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_fwd_noalloc": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P]),
     "qlora_linear_fwd_group_workspace": (_SZ, [_P, _I32, _I64, _I64, _I32]),
     "qlora_linear_fwd_group": (_I, [_P, _I32, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),

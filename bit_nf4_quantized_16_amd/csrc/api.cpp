@@ -625,6 +625,66 @@ int qlora_linear_bwd_dropout(const ql_nf4_weight* w, const uint16_t* X, const ui
     return linear_bwd(w, X, dY, T, A, B, r, scale, keep, p, U_saved, dX, dA, dB, accumulate, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---- the forward without a workspace -------------------------------------
+// Scratch of qlora_linear_fwd_noalloc: device memory of the library itself,
+// one copy on every GPU the library runs on, held until the process ends.
+// In host code the array's name is a host-side stand-in, not a device
+// address; the address of each GPU's copy comes from hipGetSymbolAddress
+// (with that GPU current) and only that address is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[QL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the GPU that `stream` runs on, looked up
+// once per device on its first call.
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = 0;
+    const hipError_t eq = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+    if (eq != hipSuccess) return set_error(QL_ERR_HIP, "device of the stream: %s", hipGetErrorString(eq));
+    if (dev < 0 || dev >= kMaxDevices) return set_error(QL_ERR_UNSUPPORTED, "device %d (at most %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return set_error(QL_ERR_HIP, "hipGetDevice failed");
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return set_error(QL_ERR_HIP, "hipSetDevice(%d) failed", dev);
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || ptr == nullptr)
+            return set_error(QL_ERR_HIP, "address of the scratch array on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return QL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd_noalloc(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float scale, uint16_t* Y, float* U_out, void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if ((s = check_weight(w)) != QL_OK) return s;
+    if ((s = check_linear_shape(w, T, r)) != QL_OK) return s;
+    if (T == 0) return QL_OK;
+    const size_t need = carve_fwd(nullptr, w->rows, w->cols, T, r).bytes;
+    if (need > QL_NOALLOC_SCRATCH_BYTES)
+        return set_error(QL_ERR_WORKSPACE,
+                         "qlora_linear_fwd_noalloc: this call needs %zu bytes of scratch, the library holds %zu "
+                         "(qlora_linear_fwd takes a workspace of any size)",
+                         need, static_cast<size_t>(QL_NOALLOC_SCRATCH_BYTES));
+    void* ptr = nullptr;
+    if (need > 0 && (s = scratch_address(static_cast<hipStream_t>(stream), &ptr)) != QL_OK) return s;
+    return linear_fwd(w, X, T, A, B, r, scale, nullptr, 0.0f, Y, U_out, ptr, need > 0 ? QL_NOALLOC_SCRATCH_BYTES : 0,
+                      stream);
+}
+
 const char* qlora_status_string(int status) {
     switch (status) {
         case QL_OK: return "ok";

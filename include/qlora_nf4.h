@@ -253,6 +253,30 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_noalloc — qlora_linear_fwd without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The call
+ * allocates nothing; the kernels' scratch (what qlora_linear_fwd_workspace
+ * reports for the same sizes) lives in a device array of the library of
+ * QL_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process ends.
+ *
+ * Arguments, layouts and results as qlora_linear_fwd (the same kernels and
+ * launch plan). A call whose scratch need exceeds QL_NOALLOC_SCRATCH_BYTES
+ * returns QL_ERR_WORKSPACE before anything is launched. The first call on a
+ * GPU looks up that GPU's copy of the array (hipGetSymbolAddress); make it
+ * outside graph capture. Every call on a GPU shares its one array: calls
+ * that overlap on one GPU (other streams, other threads) race and give
+ * undefined results; calls ordered on one stream, or captured in one graph
+ * and replayed in order, do not. The array keeps the last call's contents;
+ * nothing in it needs clearing (its counters and flags are tagged per
+ * launch, as in a workspace).
+ * Errors: as qlora_linear_fwd.
+ */
+#define QL_NOALLOC_SCRATCH_BYTES (96u << 20)
+int qlora_linear_fwd_noalloc(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float scale, uint16_t* Y, float* U_out, void* stream);
+
+/*
  * qlora_linear_fwd_group — qlora_linear_fwd for up to four layers that read
  * the same input X (adapters sit on every attention projection, q/k/v among
  * them, and sometimes on the MLP: [aivaro] §10), e.g. q/k/v or gate/up.

@@ -146,6 +146,29 @@ def test_linear_fwd_rejects(lib):
     assert call(T=0) == L.QL_OK  # empty batch: no-op, nothing launched
 
 
+def test_linear_fwd_noalloc_rejects(lib):
+    """The entry point without a workspace validates like qlora_linear_fwd and
+    turns down, before touching the GPU, a call whose scratch need is larger
+    than the library's array."""
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    def call(w=None, T=64, r=8, X=P, A=P2, B=P3, Y=P):
+        return lib.qlora_linear_fwd_noalloc(w if w is not None else _weight(L), X, T, A, B, r, 2.0, Y, None, None)
+
+    assert call(w=_weight(L, cols=96)) == L.QL_ERR_SHAPE
+    assert call(w=_weight(L, rows=100)) == L.QL_ERR_SHAPE
+    assert call(r=129) == L.QL_ERR_SHAPE
+    assert call(T=-1) == L.QL_ERR_SHAPE
+    assert call(T=0) == L.QL_OK
+    m = re.search(r"#define QL_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.QL_NOALLOC_SCRATCH_BYTES
+    # 2^20 tokens at rank 128: 256 MiB of bf16 s U staging alone
+    big = 1 << 20
+    assert lib.qlora_linear_fwd_workspace(256, 256, big, 128) > L.QL_NOALLOC_SCRATCH_BYTES
+    assert call(T=big, r=128) == L.QL_ERR_WORKSPACE
+    assert b"noalloc" in lib.qlora_last_error()
+
+
 def test_linear_fwd_group_rejects(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 
