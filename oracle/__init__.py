@@ -14,7 +14,9 @@ Sources (web pages on QLoRA; cited by title and section):
     equation and the four configuration knobs)
   * ai-reference-codex "QLoRA 与 PEFT 全家", §3.1-§3.3, §3.4 (dropout), §3.6
     (merge), §3.2 and §5 (the uniform 4-bit grid, for the quantization-error
-    comparison)
+    comparison), §3.3 and §4 (the paged AdamW optimizer of the adapters)
+  * apxml.com, the paged-optimizer paragraph; aivaro.ru §6 (Adam's two
+    moments per trained parameter, paged between GPU and CPU memory)
 
 Precision: the quantization steps take their integer decisions (codes) in
 fp32, as the kernels do; sums that set a bit-exact value (the mean of the
@@ -54,3 +56,4 @@ from .nf4 import (  # noqa: F401
 )
 from .linear import lora_forward, lora_backward, lora_merge, lora_forward_dropout, lora_backward_dropout  # noqa: F401
 from .q4error import UNIFORM4, GRIDS, quantize_dequantize, quant_error  # noqa: F401
+from .optim import adamw_step  # noqa: F401
