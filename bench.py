@@ -71,6 +71,9 @@ def parse():
                          "an eager serial pass, since events inside a replayed graph give no elapsed times)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--cpu-suite", action="store_true",
+                    help="host only: the oracle on 7B stack layer 0 (x32 extrapolated) and one 65B-shaped matrix of "
+                         "each shape at T = 4096, one JSON line")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step: the wider measurement set (32-layer 7B stack, 65B linears, "
                          "a GEMV pass over the stack, residency, torch.matmul context), one JSON line")
@@ -116,7 +119,12 @@ def run_step_streams(torch, qn, inp, side):
     dequantization and decode GEMVs, while the current stream runs the MLP
     forward and backward passes, each waiting only for its own weight. The
     172-tile GEMMs leave a third of the CUs idle, which the HBM-bound side
-    work fills. Same kernels, same inputs, same results as run_step."""
+    work fills. Same kernels, same inputs, same results as run_step.
+    Unlike run_step, the decode GEMVs here follow the attention weight's own
+    quantization and dequantization, so they read a cache-warm weight (8.4
+    MB of a 256 MB last-level cache); moving them behind the MLP weights'
+    quantization, as in run_step, made the replayed step 8 % slower (the
+    GEMVs then wait for CUs behind the split-K GEMMs)."""
     main = torch.cuda.current_stream()
     side.wait_stream(main)
     ready = []
@@ -269,6 +277,7 @@ def measure_rows(torch, qn, inp, flush):
     # quantization-error measurement on the uniform grid, fp32 weight read once
     sec = timed(9, lambda: qn.q4_quant_error(m["W"], "uniform"))
     rows["quant_error_uniform_f32_11008x4096"] = _hbm_row(4 * N * K, sec)
+    rows.update(measure_adamw_rows(torch, qn, flush))
     # dispatch floor: the same HIP-event timing around a kernel that does
     # nothing measurable (a one-element fill), cold cache as above
     tiny = torch.empty(1, device="cuda")
@@ -285,6 +294,66 @@ def measure_rows(torch, qn, inp, flush):
     return rows
 
 
+def measure_adamw_rows(torch, qn, flush):
+    """The paged AdamW step of every adapter of the 32-layer 7B-shaped stack at
+    r = 16 (A and B of its 224 linears: 40.0 M fp32 parameters), with the
+    state in device memory (HBM-bound: 16 B read, 14 B written per
+    parameter with the bf16 copy) and paged out to pinned host memory (the
+    host link bounds it: 8 B in and 8 B out per parameter; a plain pinned
+    copy of the same bytes in each direction, timed the same way, is the
+    measured ceiling). Library HIP-event timer over the whole call."""
+    n = 32 * sum(16 * (nn + kk) for _, nn, kk in LLAMA7B_LAYER)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    P = torch.randn(n, device="cuda", generator=g) * 0.02
+    G = torch.randn(n, device="cuda", generator=g) * 1e-3
+    P16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    Md, Vd = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    Mh, Vh = torch.zeros(n, pin_memory=True), torch.zeros(n, pin_memory=True)
+    cs = torch.cuda.Stream()
+    rows = {}
+
+    def timed(fn, reps=3):
+        t = qn.KernelTimer(12)
+        fn(1)
+        torch.cuda.synchronize()
+        t.arm()
+        for i in range(reps):
+            flush()
+            fn(2 + i)
+        cnt, ms = t.read()
+        t.disarm()
+        return ms / max(cnt, 1) / 1e3
+
+    sec = timed(lambda t: qn.paged_adamw_step(P, G, Md, Vd, t, weight_decay=0.01, param_bf16=P16))
+    rows["adamw_device_state_7b_r16"] = dict(_hbm_row(30 * n, sec), params=n)
+    sec_p = timed(lambda t: qn.paged_adamw_step(P, G, Mh, Vh, t, weight_decay=0.01, param_bf16=P16, copy_stream=cs))
+    # the host link's ceiling: the same bytes as plain pinned copies, in and out at once on two streams
+    Dm, Dv = torch.empty(n, device="cuda"), torch.empty(n, device="cuda")
+    Hm, Hv = torch.empty(n, pin_memory=True), torch.empty(n, pin_memory=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cps = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        e0.record()
+        cs.wait_stream(torch.cuda.current_stream())
+        Dm.copy_(Mh, non_blocking=True)
+        Dv.copy_(Vh, non_blocking=True)
+        with torch.cuda.stream(cs):
+            Hm.copy_(Md, non_blocking=True)
+            Hv.copy_(Vd, non_blocking=True)
+        torch.cuda.current_stream().wait_stream(cs)
+        e1.record()
+        torch.cuda.synchronize()
+        cps.append(e0.elapsed_time(e1) / 1e3)
+    cp = sorted(cps)[1]
+    rows["adamw_paged_state_7b_r16"] = {"us": round(sec_p * 1e6, 1), "host_link_GB/s": round(16 * n / sec_p / 1e9, 1),
+                                        "plain_copy_us": round(cp * 1e6, 1),
+                                        "frac_of_plain_copy": round(cp / sec_p, 4), "params": n}
+    del P, G, P16, Md, Vd, Mh, Vh, Dm, Dv, Hm, Hv
+    return rows
+
+
 def _hbm_row(nbytes, sec):
     gbs = nbytes / sec / 1e9
     return {"us": round(sec * 1e6, 2), "GB/s": round(gbs, 1), "frac": round(gbs * 1e9 / PEAK_HBM, 4)}
@@ -295,64 +364,189 @@ def _mfma_row(flops, sec):
     return {"us": round(sec * 1e6, 2), "TFLOP/s": round(tf, 1), "frac": round(tf * 1e12 / PEAK_BF16, 4)}
 
 
-def cpu_baseline(inp, ideal_s):
-    """The CPU oracle on a bounded sample of the step; the full-step CPU time is
-    extrapolated linearly from the sample (stated in 'sample')."""
-    import numpy as np
-
-    import oracle
-
+def _host_threads():
     try:
         from threadpoolctl import threadpool_info
 
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas_threads = 1
-    cores = len(os.sched_getaffinity(0))
-    est = 0.0
-    rows_q = 128
-    # quantize + double quant + dequantize: a 128-row slice of each weight
-    for W, full_rows in [(inp.attn.W, 4096)] + [(c.W, c.W.shape[0]) for c in inp.mlp]:
-        Wn = W[:rows_q].numpy()
-        t0 = time.perf_counter()
-        p, a = oracle.quantize(Wn)
-        c8, s, mu = oracle.double_quant(a)
-        ae = oracle.dequant_absmax(c8, s, mu)
-        oracle.dequantize(p, ae, Wn.size)
-        est += (time.perf_counter() - t0) * full_rows / rows_q
-    # decode GEMVs: full size (fp64 matmul)
-    ref = oracle.bf16_bits_to_f32(oracle.dequantize(*oracle.quantize(inp.attn.W[:512].numpy()), 512 * 4096))
-    Wd = np.tile(ref.reshape(512, 4096), (8, 1))
+        blas = 1
+    return len(os.sched_getaffinity(0)), blas
+
+
+def _oracle_weight(W):
+    """The oracle's quantize + double quant + dequantize of fp32 numpy W:
+    returns the dequantized bf16 values as fp32 [N, K]."""
+    import oracle
+
+    packed, absmax = oracle.quantize(W)
+    c8, scale, mean = oracle.double_quant(absmax)
+    a_eff = oracle.dequant_absmax(c8, scale, mean)
+    return oracle.bf16_bits_to_f32(oracle.dequantize(packed, a_eff, W.size)).reshape(W.shape)
+
+
+def cpu_baseline(inp, ideal_s):
+    """The CPU oracle runs one whole step of the benchmark on the host, every
+    stage on the full tensors (no sampling, no extrapolation): the 4096 x 4096
+    attention weight's quantize + double quant + dequantize and its decode
+    forward at T = 1 and 16, and for each 7B MLP weight quantize + double
+    quant + dequantize, forward and backward at T = 1024. The 256 x 256
+    configuration is timed alongside. Same unit as the GPU line."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    cores, blas = _host_threads()
+    per = {}
+
+    def tick():
+        return time.perf_counter()
+
+    c1 = workloads.tiny_256()
+    t0 = tick()
+    wd = _oracle_weight(c1.W.numpy())
+    X, dY, A, B = (t.float().numpy() for t in (c1.X, c1.dY, c1.A, c1.B))
+    oracle.lora_forward(X, wd, A, B, c1.scale)
+    oracle.lora_backward(X, dY, wd, A, B, c1.scale)
+    per["c1_256x256_T4_r8"] = {"s": round(tick() - t0, 4)}
+
+    step = 0.0
+    t0 = tick()
+    wd = _oracle_weight(inp.attn.W.numpy())
+    tq = tick() - t0
     X16 = inp.attn.X.float().numpy()
     A, B = inp.attn.A.float().numpy(), inp.attn.B.float().numpy()
-    t0 = time.perf_counter()
-    oracle.lora_forward(X16[:1], Wd, A, B, inp.attn.scale)
-    oracle.lora_forward(X16, Wd, A, B, inp.attn.scale)
-    est += time.perf_counter() - t0
-    # MLP forward + backward: 64 of the 1024 tokens, scaled by 1024 / 64
-    t_s = 64
+    t1 = tick()
+    oracle.lora_forward(X16[:1], wd, A, B, inp.attn.scale)
+    oracle.lora_forward(X16, wd, A, B, inp.attn.scale)
+    tg = tick() - t1
+    per["c2_attn_4096x4096"] = {"quantize_dq_dequant_s": round(tq, 3), "decode_fwd_T1_T16_s": round(tg, 3)}
+    step += tq + tg
     for c in inp.mlp:
+        t0 = tick()
+        wd = _oracle_weight(c.W.numpy())
+        tq = tick() - t0
+        X, dY, A, B = (t.float().numpy() for t in (c.X, c.dY, c.A, c.B))
+        t1 = tick()
+        oracle.lora_forward(X, wd, A, B, c.scale)
+        tf = tick() - t1
+        t1 = tick()
+        oracle.lora_backward(X, dY, wd, A, B, c.scale)
+        tb = tick() - t1
         N, K = c.W.shape
-        Wd = np.random.default_rng(0).standard_normal((N, K)).astype(np.float32) * 0.02
-        Xn = c.X[:t_s].float().numpy()
-        dYn = c.dY[:t_s].float().numpy()
-        An, Bn = c.A.float().numpy(), c.B.float().numpy()
-        t0 = time.perf_counter()
-        oracle.lora_forward(Xn, Wd, An, Bn, c.scale)
-        oracle.lora_backward(Xn, dYn, Wd, An, Bn, c.scale)
-        est += (time.perf_counter() - t0) * c.X.shape[0] / t_s
+        T, r = c.X.shape[0], c.r
+        per["c3_%s" % c.name] = {"quantize_dq_dequant_s": round(tq, 3), "fwd_s": round(tf, 3), "bwd_s": round(tb, 3),
+                                 "fwd_GFLOP/s": round(fwd_flops(N, K, T, r) / tf / 1e9, 1),
+                                 "bwd_GFLOP/s": round(bwd_flops(N, K, T, r) / tb / 1e9, 1),
+                                 "quantize_GB/s": round((BPW_QUANT_F32 + BPW_DQ + BPW_DEQUANT) * N * K / tq / 1e9, 3)}
+        step += tq + tf + tb
     return {
-        "value": round(100.0 * ideal_s / est, 6),
+        "value": round(100.0 * ideal_s / step, 6),
         "unit": "% of MI355X roofline",
-        "cores": int(min(cores, blas_threads)) if blas_threads > 1 else 1,
+        "cores": int(blas) if blas > 1 else 1,
         "kind": "oracle",
-        "sample": "numpy oracle: quantize+double-quant+dequantize of 128 rows of each weight (x rows/128), "
-                  "both decode GEMVs in full, MLP fwd+bwd on 64 of 1024 tokens (x16); "
-                  "extrapolated step time %.2f s; elementwise numpy single-threaded, fp64 matmuls on %d BLAS "
-                  "threads, %d host cores" % (est, blas_threads, cores),
-        "step_seconds_est": round(est, 3),
+        "sample": "the whole benchmark step on the numpy oracle, full tensors, run once (%.1f s): elementwise "
+                  "numpy single-threaded, fp64 matmuls on %d BLAS threads; %d host cores" % (step, blas, cores),
+        "step_seconds": round(step, 3),
+        "configs": per,
     }
 
+
+def cpu_suite():
+    """--cpu-suite: the oracle on the larger configurations, run once each:
+    layer 0 of the 32-layer 7B-shaped stack at T = 4096, r = 64 (its seven
+    linears: quantize + double quant + dequantize, forward, backward; the
+    stack's time is 32 x that, extrapolated) and one 65B-shaped matrix of each
+    shape at T = 4096, r = 64. Host-only; prints one JSON line."""
+    import oracle
+    import workloads
+
+    cores, blas = _host_threads()
+    res = {"host_cores": cores, "blas_threads": blas}
+
+    def run(case):
+        N, K = case.W.shape
+        T, r = case.X.shape[0], case.r
+        t0 = time.perf_counter()
+        wd = _oracle_weight(case.W.numpy())
+        tq = time.perf_counter() - t0
+        X, dY, A, B = (t.float().numpy() for t in (case.X, case.dY, case.A, case.B))
+        t1 = time.perf_counter()
+        oracle.lora_forward(X, wd, A, B, case.scale)
+        tf = time.perf_counter() - t1
+        t1 = time.perf_counter()
+        oracle.lora_backward(X, dY, wd, A, B, case.scale)
+        tb = time.perf_counter() - t1
+        return {"quantize_dq_dequant_s": round(tq, 2), "fwd_s": round(tf, 2), "bwd_s": round(tb, 2),
+                "fwd_GFLOP/s": round(fwd_flops(N, K, T, r) / tf / 1e9, 1),
+                "bwd_GFLOP/s": round(bwd_flops(N, K, T, r) / tb / 1e9, 1)}
+
+    layer = {}
+    for name, _, _ in LLAMA7B_LAYER:
+        print("cpu suite: 7B layer 0 %s" % name, file=sys.stderr, flush=True)
+        layer[name] = run(workloads.llama7b_layer_linear(name))
+    tot = sum(v["quantize_dq_dequant_s"] + v["fwd_s"] + v["bwd_s"] for v in layer.values())
+    res["c4_layer0_T4096_r64"] = layer
+    res["c4_stack_x32_extrapolated_s"] = round(32 * tot, 1)
+    c5 = {}
+    for name, _, _ in LLAMA65B:
+        print("cpu suite: 65B %s" % name, file=sys.stderr, flush=True)
+        c5[name] = run(workloads.llama65b_linear(name))
+    res["c5_one_matrix_each_T4096_r64"] = c5
+    return res
+
+
+def clock_samples(torch, replay, seconds=1.5):
+    """The shader clock while the step runs: the replayed step is run back to
+    back for ``seconds`` while a thread samples `amd-smi metric -c` (current
+    clocks) every ~0.2 s. Returns the GFX clock readings in MHz (and the
+    first raw sample's clock lines)."""
+    import re
+    import subprocess
+    import threading
+
+    samples, raw = [], []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c"], capture_output=True, text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            lines = r.stdout.splitlines()
+            if not raw:
+                raw.extend(ln.strip() for ln in lines if ln.strip())
+            # the GFX block's "CLK:" lines in MHz
+            gfx = False
+            for ln in lines:
+                t = ln.strip()
+                if t.upper().startswith("GFX"):
+                    gfx = True
+                elif t and t.endswith(":") and not t.upper().startswith("GFX") and not t.upper().startswith("CLK"):
+                    gfx = False
+                m = re.match(r"CLK:\s*([0-9.]+)\s*MHz", t)
+                if gfx and m:
+                    samples.append(float(m.group(1)))
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            replay()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    busy = [x for x in samples if x > 0]
+    out = {"gfx_clk_MHz_samples": len(busy), "raw_first_sample": raw[:40]}
+    if busy:
+        busy.sort()
+        out.update({"gfx_clk_MHz_median": busy[len(busy) // 2], "gfx_clk_MHz_min": busy[0],
+                    "gfx_clk_MHz_max": busy[-1]})
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -670,6 +864,9 @@ def main():
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (--gpus 1); no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_suite:
+        print(json.dumps({"cpu_suite": cpu_suite()}), flush=True)
+        return
     import torch
 
     import bit_nf4_quantized_16_amd as qn
@@ -743,6 +940,8 @@ def main():
         same = all(torch.equal(a, b) for o, r in zip(outs, ref) for a, b in zip(o, r))
         if not same:
             raise SystemExit("bench: the replayed step's outputs differ from the eager step's")
+        print("bench: sampling the clock under the replayed step", file=sys.stderr, flush=True)
+        clock = clock_samples(torch, graph.replay)
     ideal = ideal_step_seconds(inp)
     value = 100.0 * ideal / (ms_per_step / 1e3)
 
@@ -786,6 +985,8 @@ def main():
         "roofline": roof,
         "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kstats.items()},
     }
+    if not args.eager:
+        out["clock"] = clock
     if not args.no_rows:
         flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         print("bench: per-stage cold-cache rows", file=sys.stderr, flush=True)

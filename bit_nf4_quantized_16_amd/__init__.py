@@ -297,6 +297,29 @@ def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, 
     return dX, dA, dB
 
 
+def paged_adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr=2e-4, betas=(0.9, 0.999), eps=1e-8,
+                     weight_decay=0.0, param_bf16=None, copy_stream=None):
+    """One AdamW step (fp32 state) of a flat fp32 parameter tensor in place.
+    ``exp_avg`` / ``exp_avg_sq``: fp32 tensors of the same size, both on the
+    GPU or both in pinned host memory (``pin_memory=True``): paged-out state
+    streams through a device staging buffer, its copies on ``copy_stream``
+    (a torch.cuda.Stream; None runs them on the current stream).
+    ``param_bf16``: optional bf16 tensor that receives the updated values."""
+    n = param.numel()
+    for t in (param, grad, exp_avg, exp_avg_sq):
+        assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == n
+    if param_bf16 is not None:
+        assert param_bf16.dtype == torch.bfloat16 and param_bf16.is_contiguous() and param_bf16.numel() == n
+    ws, wsb = (None, 0)
+    if not exp_avg.is_cuda:
+        ws, wsb = _workspace(lib.qlora_paged_adamw_workspace(n), param.device)
+    cs = ctypes.c_void_p(copy_stream.cuda_stream) if copy_stream is not None else None
+    _check(lib.qlora_paged_adamw(_ptr(param), _ptr(param_bf16), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n,
+                                 int(step), float(lr), float(betas[0]), float(betas[1]), float(eps),
+                                 float(weight_decay), _ptr(ws), wsb, _stream(), cs))
+    return param
+
+
 class QLoRALinearFunction(torch.autograd.Function):
     """autograd wrapper: forward / backward run in the HIP library; W is frozen
     (no gradient), A and B receive fp32 gradients cast to their dtype."""

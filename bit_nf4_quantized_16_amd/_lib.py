@@ -32,6 +32,7 @@ QL_KERNEL_MERGE = 8
 QL_KERNEL_QERROR = 9
 QL_KERNEL_KEEP_APPLY = 10
 QL_KERNEL_DX_KEEP = 11
+QL_KERNEL_ADAMW = 12
 QL_NOALLOC_SCRATCH_BYTES = 96 << 20  # include/qlora_nf4.h
 QL_GRID_NF4 = 0
 QL_GRID_UNIFORM = 1
@@ -82,6 +83,8 @@ SIGNATURES = {
     "qlora_linear_bwd": (_I, [_WP, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
     "qlora_linear_bwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_bwd_dropout": (_I, [_WP, _P, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
+    "qlora_paged_adamw_workspace": (_SZ, [_I64]),
+    "qlora_paged_adamw": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _F, _F, _F, _F, _F, _P, _SZ, _P, _P]),
     "qlora_status_string": (ctypes.c_char_p, [_I]),
     "qlora_last_error": (ctypes.c_char_p, []),
     "qlora_timer_arm": (_I, [_I]),

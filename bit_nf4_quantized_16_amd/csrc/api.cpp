@@ -685,6 +685,56 @@ int qlora_linear_fwd_noalloc(const ql_nf4_weight* w, const uint16_t* X, int64_t 
                       stream);
 }
 
+size_t qlora_paged_adamw_workspace(int64_t n) { return n <= 0 ? 0 : adamw_page_ws_bytes(n); }
+
+int qlora_paged_adamw(float* param, uint16_t* param_bf16, const float* grad, float* exp_avg, float* exp_avg_sq,
+                      int64_t n, int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                      void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
+    g_last_error[0] = '\0';
+    if (n <= 0) return set_error(QL_ERR_SHAPE, "n = %lld", (long long)n);
+    if (step < 1) return set_error(QL_ERR_SHAPE, "step = %lld (counted from 1)", (long long)step);
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+        return set_error(QL_ERR_UNSUPPORTED, "betas (%g, %g) outside [0, 1)", (double)beta1, (double)beta2);
+    if (!(eps >= 0.0f) || !(lr >= 0.0f) || !(weight_decay >= 0.0f))
+        return set_error(QL_ERR_UNSUPPORTED, "lr %g, eps %g, weight_decay %g (none may be negative)", (double)lr,
+                         (double)eps, (double)weight_decay);
+    int s;
+    if ((s = check_ptr(param, "param")) != QL_OK) return s;
+    if ((s = check_ptr(grad, "grad")) != QL_OK) return s;
+    if ((s = check_ptr(exp_avg, "exp_avg")) != QL_OK) return s;
+    if ((s = check_ptr(exp_avg_sq, "exp_avg_sq")) != QL_OK) return s;
+    if (param_bf16 != nullptr && (s = check_ptr(param_bf16, "param_bf16")) != QL_OK) return s;
+    // where the state lives: device memory, or pinned host memory (paged out)
+    auto where = [](const void* p, hipMemoryType* t) {
+        hipPointerAttribute_t at{};
+        if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+            (void)hipGetLastError();  // unregistered host memory reports an error here
+            *t = hipMemoryTypeUnregistered;
+        } else {
+            *t = at.type;
+        }
+    };
+    hipMemoryType tm, tv;
+    where(exp_avg, &tm);
+    where(exp_avg_sq, &tv);
+    auto usable = [](hipMemoryType t) { return t == hipMemoryTypeDevice || t == hipMemoryTypeHost; };
+    if (!usable(tm) || !usable(tv) || tm != tv)
+        return set_error(QL_ERR_UNSUPPORTED,
+                         "exp_avg and exp_avg_sq must both be device memory or both pinned host memory "
+                         "(memory types %d and %d)",
+                         (int)tm, (int)tv);
+    const bool paged = tm == hipMemoryTypeHost;
+    if (paged) {
+        const size_t need = adamw_page_ws_bytes(n);
+        if (ws == nullptr || ws_bytes < need)
+            return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes, need);
+        if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    return launch_adamw(param, param_bf16, grad, exp_avg, exp_avg_sq, n, step, lr, beta1, beta2, eps, weight_decay,
+                        paged, static_cast<float*>(ws), static_cast<hipStream_t>(stream),
+                        static_cast<hipStream_t>(copy_stream));
+}
+
 const char* qlora_status_string(int status) {
     switch (status) {
         case QL_OK: return "ok";

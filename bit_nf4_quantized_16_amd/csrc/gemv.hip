@@ -236,7 +236,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     // leaves it at zero (compare-and-swap), so nothing needs resetting at
     // launch start. Two levels: workgroup i counts on counter i % kGemvSub,
     // the last on each of those on counter kGemvSub (atomics on one word are
-    // served one after another).
+    // served one after another). The words are stored and loaded only as
+    // agent-scope atomics (performed at the device's coherence point), and
+    // every thread's accesses complete (vmcnt) before the barrier and the
+    // count, so relaxed counters suffice (see the split projection's count).
     auto count_done_and_clear = [&](int i) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): this thread's word accesses are done
         __syncthreads();
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                 do {
                     arrived = static_cast<int>((old >> 24) == p.token ? (old & 0xFFFFFFu) : 0u) + 1;
                     nv = (p.token << 24) | static_cast<uint64_t>(arrived == n ? 0 : arrived);
-                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT));
                 return arrived == n;
             };

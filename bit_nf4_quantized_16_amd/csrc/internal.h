@@ -159,4 +159,12 @@ struct GradArgs {
 size_t lora_grads_part_bytes(int64_t T, int64_t C0, int64_t C1, int r);
 int launch_lora_grads(GradArgs a, float* part, hipStream_t stream);
 
+// AdamW step (fp32 state). paged: m and v are pinned host memory and pass
+// through ws (adamw_page_ws_bytes(n) bytes of device memory) in chunks,
+// copied on copy_stream (null or stream itself: everything on stream).
+size_t adamw_page_ws_bytes(int64_t n);
+int launch_adamw(float* p, uint16_t* p16, const float* g, float* m, float* v, int64_t n, int64_t step, float lr,
+                 float b1, float b2, float eps, float wd, bool paged, float* ws, hipStream_t stream,
+                 hipStream_t copy_stream);
+
 }  // namespace qlnf4

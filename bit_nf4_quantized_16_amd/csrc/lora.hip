@@ -346,11 +346,16 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
             // token counts as zero) adds the partials in split order, so the
             // result does not depend on the arrival order. The last arrival
             // leaves the count at zero, so a launch replayed with the same
-            // token (a captured graph) starts from zero as well. Every thread
-            // waits for its partial stores (vmcnt counts per wave) before the
-            // barrier; the count is an agent-scope acquire-release exchange, so
-            // those stores happen before it and the last split's loads of the
-            // partials after it.
+            // token (a captured graph) starts from zero as well.
+            // Ordering: the partials are written and read only by agent-scope
+            // atomic stores and loads, which are performed at the device's
+            // coherence point, not in an XCD's own cache. Every thread waits for
+            // its stores to complete (vmcnt counts per wave) before the barrier
+            // and thread 0's count; the last split's loads are issued only after
+            // the count has returned (barrier, branch on s_last). So no cache
+            // write-back or invalidation is needed, which is all an
+            // acquire-release exchange would add here: one L2 write-back per
+            // workgroup, measured at 45 us per benchmark step.
             __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
             __syncthreads();
             if (tid == 0) {
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(64 * ProjDma<RT>::NW) void lora_proj_dma_kernel(Pro
                 do {
                     arrived = static_cast<int>(((old >> 8) == p.token) ? (old & 0xFFu) : 0u) + 1;
                     nv = (p.token << 8) | static_cast<uint64_t>(arrived == nsplit ? 0 : arrived);
-                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT));
                 s_last = arrived == nsplit;
             }

@@ -364,6 +364,55 @@ int qlora_linear_bwd_dropout(const ql_nf4_weight* w, const uint16_t* X, const ui
                              float p, const float* U_saved, uint16_t* dX, float* dA, float* dB, int accumulate,
                              void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * qlora_paged_adamw — one AdamW step of the trained adapter parameters with
+ * 32-bit optimizer state that lives in device memory or, paged out, in host
+ * memory ([apxml], the paged-optimizer paragraph: optimizer state moves
+ * between GPU memory and CPU memory when GPU memory runs short; [codex] §3.3
+ * and §4: paged_adamw_32bit, learning rate 2e-4; [aivaro] §6: Adam keeps the
+ * first and second moment of every trained parameter, paged out to the CPU
+ * and back as needed). The pages give no update formula; this is AdamW as
+ * published (bias-corrected moments, weight decay decoupled from the
+ * gradient), in fp32, for step number t = step >= 1:
+ *
+ *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2
+ *   p = p - lr wd p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ *
+ *   param       [n] fp32, device, updated in place (e.g. every layer's A and
+ *               B laid end to end)
+ *   param_bf16  optional out [n] bf16, device: the updated parameters
+ *               rounded to nearest even (what the layer kernels read), or NULL
+ *   grad        [n] fp32, device (dA and dB from qlora_linear_bwd)
+ *   exp_avg, exp_avg_sq   [n] fp32 m and v, updated in place: both device
+ *               memory, or both pinned host memory (hipHostMalloc); pageable
+ *               or managed memory is refused (QL_ERR_UNSUPPORTED)
+ *   ws          device workspace of qlora_paged_adamw_workspace(n) bytes
+ *               when the state is in host memory (unused, may be NULL, when
+ *               it is in device memory)
+ *   copy_stream hipStream_t for the copies of host-resident state in the
+ *               staged mode below (NULL, or stream itself: on stream)
+ *
+ * Host-resident state is by default updated in place over the host link
+ * (pinned memory is mapped into the device's address space): one kernel
+ * launch on stream, as for device-resident state (ws and copy_stream are
+ * not used). With the environment variable QLORA_NF4_ADAMW_PAGING=staged it
+ * instead streams through ws in chunks: host-to-device copies on copy_stream,
+ * updates and copies back on stream, event hand-offs both ways; the library
+ * keeps a few events per device for this, and paged calls from several
+ * threads are serialised while they are queued. Either way the call behaves
+ * as one operation on stream: it starts after the work already queued there,
+ * and work queued there afterwards (and a synchronisation of stream) sees m
+ * and v updated in host memory. A one-launch call may be captured into a
+ * graph. All device pointers 16-byte aligned.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (n <= 0, step < 1), QL_ERR_UNSUPPORTED
+ * (state memory, beta outside [0, 1), eps or lr or weight_decay negative),
+ * QL_ERR_ALIGN, QL_ERR_WORKSPACE, QL_ERR_HIP.
+ */
+size_t qlora_paged_adamw_workspace(int64_t n);
+int qlora_paged_adamw(float* param, uint16_t* param_bf16, const float* grad, float* exp_avg, float* exp_avg_sq,
+                      int64_t n, int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                      void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
 /* ---- diagnostics ------------------------------------------------------- */
 /* Static text for a status code. */
 const char* qlora_status_string(int status);
@@ -390,7 +439,8 @@ const char* qlora_last_error(void);
 #define QL_KERNEL_QERROR 9
 #define QL_KERNEL_KEEP_APPLY 10
 #define QL_KERNEL_DX_KEEP 11
-#define QL_KERNEL_COUNT 12
+#define QL_KERNEL_ADAMW 12
+#define QL_KERNEL_COUNT 13
 int qlora_timer_arm(int kernel_id);
 int qlora_timer_read(int kernel_id, int64_t* launches, double* total_ms);
 int qlora_timer_disarm(int kernel_id);

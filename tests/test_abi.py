@@ -169,6 +169,35 @@ def test_linear_fwd_noalloc_rejects(lib):
     assert b"noalloc" in lib.qlora_last_error()
 
 
+def test_paged_adamw_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    ok = dict(p=P, p16=None, g=P2, m=P3, v=P, n=1000, step=1, lr=2e-4, b1=0.9, b2=0.999, eps=1e-8, wd=0.0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.qlora_paged_adamw(a["p"], a["p16"], a["g"], a["m"], a["v"], a["n"], a["step"], a["lr"], a["b1"],
+                                     a["b2"], a["eps"], a["wd"], None, 0, None, None)
+
+    assert call(n=0) == L.QL_ERR_SHAPE
+    assert call(step=0) == L.QL_ERR_SHAPE
+    assert call(b1=1.0) == L.QL_ERR_UNSUPPORTED
+    assert call(b2=-0.1) == L.QL_ERR_UNSUPPORTED
+    assert call(eps=-1e-8) == L.QL_ERR_UNSUPPORTED
+    assert call(lr=float("nan")) == L.QL_ERR_UNSUPPORTED
+    assert call(wd=-0.5) == L.QL_ERR_UNSUPPORTED
+    assert call(p=None) == L.QL_ERR_NULL
+    assert call(g=None) == L.QL_ERR_NULL
+    assert call(m=None) == L.QL_ERR_NULL
+    assert call(v=MIS) == L.QL_ERR_ALIGN
+    assert call(p16=MIS) == L.QL_ERR_ALIGN
+    # two staging buffers of m and v, at most 2^21 elements each
+    assert lib.qlora_paged_adamw_workspace(0) == 0
+    assert lib.qlora_paged_adamw_workspace(100) == 4 * 128 * 4
+    assert lib.qlora_paged_adamw_workspace(1 << 30) == 4 * (1 << 21) * 4
+
+
 def test_linear_fwd_group_rejects(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 
