@@ -541,8 +541,9 @@ constexpr int kGradWaves = 8;  // waves per workgroup, taking chunks in turn
 constexpr int kGradLd = kGradCols + 8;
 
 int lora_grad_splits(int64_t T, int64_t cols_total) {
-    // one split (no second kernel) while a workgroup's token loop stays short
-    if (T <= 2048) return 1;
+    // one split (no second kernel) while a workgroup's token loop stays short,
+    // and when neither gradient is asked for (no columns)
+    if (T <= 2048 || cols_total <= 0) return 1;
     const int64_t col_blocks = ceil_div(cols_total, kGradCols);
     int64_t s = ceil_div(512, col_blocks);
     const int64_t max_s = ceil_div(T, kGradWaves * kGradRows);

@@ -146,6 +146,20 @@ def test_linear_fwd_rejects(lib):
     assert call(T=0) == L.QL_OK  # empty batch: no-op, nothing launched
 
 
+def test_backward_sizing_without_adapter_gradients(lib):
+    """dX alone (dA and dB NULL) at T > 2048: the workspace sizing once
+    divided by the number of gradient columns, zero here, and raised SIGFPE
+    in the caller's process. Without a GPU the call gets as far as its first
+    launch and reports the HIP error."""
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    for T in (2049, 4096, 8192):
+        ws = lib.qlora_linear_bwd_workspace(4096, 4096, T, 16)
+        s = lib.qlora_linear_bwd(_weight(L, rows=4096, cols=4096), P, P2, T, P3, P, 16, 2.0, P2, P3, None, None, 0, P,
+                                 ws, None)
+        assert s in (L.QL_OK, L.QL_ERR_HIP)
+
+
 def test_linear_fwd_noalloc_rejects(lib):
     """The entry point without a workspace validates like qlora_linear_fwd and
     turns down, before touching the GPU, a call whose scratch need is larger

@@ -305,3 +305,26 @@ def test_split_reduction(qn, monkeypatch, splits, N, K, T, r):
     W = workloads.normal_weight(N, K, 0.02, seed=N + K + int(splits))
     case = workloads.lora_case("split%s_N%dK%dT%d" % (splits, N, K, T), W, T, r, 2.0 * r, 1 / K, 0.05, seed=T + 1)
     _run(qn, case)
+
+
+@pytest.mark.parametrize("need_da,need_db", [(False, False), (True, False), (False, True)])
+def test_long_batch_backward_with_gradients_skipped(qn, need_da, need_db):
+    """T > 2048 (the adapter gradients split over tokens) with some of dA, dB
+    not asked for; dX alone once crashed the caller's process in the
+    workspace sizing."""
+    T, N, K, r = 2300, 264, 320, 16
+    W = workloads.normal_weight(N, K, 0.02, seed=31)
+    case = workloads.lora_case("longT", W, T, r, 32.0, 1 / K, 0.05, seed=31)
+    w = qn.quantize_weight(W.cuda())
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    dX, dA, dB = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, need_da=need_da, need_db=need_db)
+    torch.cuda.synchronize()
+    ref = oracle_weight(W.numpy())
+    Xn, dYn, An, Bn = (bf16_to_np(t) for t in (case.X, case.dY, case.A, case.B))
+    dXo, dAo, dBo, _, _ = oracle.lora_backward(Xn, dYn, ref["wd"], An, Bn, case.scale)
+    assert normwise_rel_err(bf16_to_np(dX), dXo) <= TOL
+    assert (dA is None) == (not need_da) and (dB is None) == (not need_db)
+    if need_da:
+        assert normwise_rel_err(f32_to_np(dA), dAo) <= TOL
+    if need_db:
+        assert normwise_rel_err(f32_to_np(dB), dBo) <= TOL
