@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdlib>
 
+#include "arrive.h"
 #include "common.h"
 #include "internal.h"
 #include "mm_common.h"
@@ -49,7 +50,7 @@ namespace qlnf4 {
 // out, the workgroup computes U itself from the same partial products in the
 // same order (bit-identical). A launch being captured into a graph (its
 // replays reuse the token) also counts its U and row workgroups done (a
-// token-tagged compare-and-swap count in two levels); the last one clears
+// token-tagged count, tagged_arrive); the last one clears
 // the words, so a replay finds no word of the previous one. An eager launch
 // has a token of its own and skips the count.
 //
@@ -65,7 +66,6 @@ namespace qlnf4 {
 // ===========================================================================
 constexpr int kGemvRows = 16;
 constexpr int kGemvWaves = 8;
-constexpr int kGemvSub = 32;    // first level of the done count
 constexpr int kGemvUSteps = 4;  // steps of x in one U workgroup's slice (waves 0..3)
 
 // One weight of a launch: a launch serves up to kGemvGroup weights that share
@@ -81,7 +81,7 @@ struct GemvWeight {
     uint16_t* Y;
     float* U_out;     // [T, r] fp32 = X A^T, or null
     uint64_t* uword;  // [nks][T][r]: slice ks of U, tag << 32 | fp32 bits (r > 0)
-    uint64_t* done;   // [kGemvSub + 1]: token << 24 | count of workgroups done with the words (r > 0)
+    uint64_t* done;   // [kArriveSub + 1]: token << 24 | count of workgroups done with the words (r > 0)
     int nu, nrow;     // its U and row workgroups
     int ub, rb;       // the grid index of its first U and first row workgroup
 };
@@ -231,35 +231,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     // words are stored, a row workgroup once it has U (from the words or
     // computed itself). The last of them clears the words, so a replay finds
     // none of the previous replay's; as every U workgroup counts too, no word
-    // can be stored after the clear. Counters hold token << 24 | count; one
-    // holding another token counts as zero, and each counter's last arrival
-    // leaves it at zero (compare-and-swap), so nothing needs resetting at
-    // launch start. Two levels: workgroup i counts on counter i % kGemvSub,
-    // the last on each of those on counter kGemvSub (atomics on one word are
-    // served one after another). The words are stored and loaded only as
-    // agent-scope atomics (performed at the device's coherence point), and
-    // every thread's accesses complete (vmcnt) before the barrier and the
-    // count, so relaxed counters suffice (see the split projection's count).
+    // can be stored after the clear (tagged_arrive: token-tagged counters in
+    // two levels that need no reset). The words are stored and loaded only as
+    // agent-scope atomics, and every thread's accesses complete (vmcnt) before
+    // the barrier and the count.
     auto count_done_and_clear = [&](int i) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): this thread's word accesses are done
         __syncthreads();
-        if (tid == 0) {
-            auto arrive = [&](uint64_t* c, int n) {
-                uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                int arrived;
-                uint64_t nv;
-                do {
-                    arrived = static_cast<int>((old >> 24) == p.token ? (old & 0xFFFFFFu) : 0u) + 1;
-                    nv = (p.token << 24) | static_cast<uint64_t>(arrived == n ? 0 : arrived);
-                } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT));
-                return arrived == n;
-            };
-            const int total = gw.nu + gw.nrow;
-            const int k = i % kGemvSub, groups = std::min(total, kGemvSub);
-            const int in_k = total / kGemvSub + (k < total % kGemvSub ? 1 : 0);  // arrivals on counter k
-            s_last = arrive(gw.done + k, in_k) && arrive(gw.done + kGemvSub, groups);
-        }
+        if (tid == 0) s_last = tagged_arrive(gw.done, p.token, i, gw.nu + gw.nrow);
         __syncthreads();
         if (s_last)
             for (int e = tid; e < p.nks * T * r; e += 512)
@@ -497,7 +476,7 @@ GemvUPlan gemv_u_plan(int64_t T, int64_t K, int r) {
 size_t gemv_ws_bytes(int64_t T, int64_t K, int r) {
     if (r <= 0) return 0;
     const GemvUPlan u = gemv_u_plan(T, K, r);
-    return (u.part_bytes + (kGemvSub + 1) * sizeof(uint64_t) + 255) / 256 * 256;
+    return (u.part_bytes + (kArriveSub + 1) * sizeof(uint64_t) + 255) / 256 * 256;
 }
 
 namespace {

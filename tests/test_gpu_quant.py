@@ -153,6 +153,51 @@ def test_double_quant_three_level_tree_mean(qn):
         assert np.array_equal(u8_to_np(c8)[g * 256 : g * 256 + seg.size], want)
 
 
+def test_double_quant_two_level_tree_at_its_largest(qn):
+    # 4096 chunk sums of 4096 constants: the largest two-level tree
+    n1 = 4096 * 4096
+    rng = np.random.default_rng(98)
+    a = (rng.random(n1, dtype=np.float32) * 0.1 + 0.01).astype(np.float32)
+    c8, scale, mean = qn.nf4_double_quant(torch.from_numpy(a).cuda())
+    torch.cuda.synchronize()
+    m_ref = np.float32(oracle.pairwise_tree_sum(a) / np.float64(n1))
+    assert f32_to_np(mean)[0].view(np.uint32) == m_ref.view(np.uint32)
+    for g in [0, 1, 4095, 40_000, n1 // 256 - 1]:
+        seg = a[g * 256 : (g + 1) * 256]
+        d = (seg - m_ref).astype(np.float32)
+        s = np.float32(np.max(np.abs(d)) / np.float32(448.0))
+        assert f32_to_np(scale)[g].view(np.uint32) == s.view(np.uint32)
+        assert np.array_equal(u8_to_np(c8)[g * 256 : (g + 1) * 256], oracle.e4m3fn_encode((d / s).astype(np.float32)))
+
+
+def test_double_quant_graph_replays_with_new_constants(qn):
+    """A captured double quantization replayed with new constants in the same
+    buffer gives the eager results each time."""
+    n1 = 262144
+    rng = np.random.default_rng(7)
+    vals = [torch.from_numpy((rng.random(n1, dtype=np.float32) * 0.1 + 0.01 * (i + 1)).astype(np.float32)).cuda()
+            for i in range(4)]
+    a = vals[0].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qn.nf4_double_quant(a)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = qn.nf4_double_quant(a)
+    for rep in range(1, 7):
+        a.copy_(vals[rep % 4])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = qn.nf4_double_quant(vals[rep % 4])
+        torch.cuda.synchronize()
+        for x, y in zip(out, ref):
+            assert torch.equal(x, y), "replay %d" % rep
+
+
 @pytest.mark.parametrize("shape", [(256, 256), (1, 1), (3, 100), (7, 33), (513, 77), (1, 1024 + 64 * 3 + 5)])
 @pytest.mark.parametrize("dq", [True, False])
 def test_dequantize_matches_oracle(qn, shape, dq):
