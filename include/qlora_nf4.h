@@ -242,9 +242,10 @@ int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, in
  * first workgroups compute U for the others; the workspace holds U's
  * partial sums and their flags, size 0 when r == 0); larger T the
  * dequant-in-LDS MFMA GEMM.
- * K must be a multiple of 64. Y must not alias any input.
- * Errors: QL_ERR_NULL, QL_ERR_SHAPE (T < 0, K % 64 != 0, r < 0 or
- * r > QL_MAX_RANK), QL_ERR_UNSUPPORTED, QL_ERR_ALIGN, QL_ERR_WORKSPACE,
+ * K must be a multiple of 64 and N a multiple of 8. Y must not alias any
+ * input.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (T < 0, K % 64 != 0, N % 8 != 0, r < 0
+ * or r > QL_MAX_RANK), QL_ERR_UNSUPPORTED, QL_ERR_ALIGN, QL_ERR_WORKSPACE,
  * QL_ERR_HIP. T == 0 is a no-op.
  */
 size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
@@ -336,7 +337,8 @@ int qlora_linear_fwd_dropout(const ql_nf4_weight* w, const uint16_t* X, int64_t 
  *               their current contents (gradient accumulation)
  *
  * Any of dX, dA, dB may be NULL to skip it. X is needed for dA and when
- * U_saved is NULL. K must be a multiple of 64. Outputs must not alias inputs.
+ * U_saved is NULL. K must be a multiple of 64 and N a multiple of 8. Outputs
+ * must not alias inputs.
  * Errors: as qlora_linear_fwd.
  */
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
