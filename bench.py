@@ -291,6 +291,16 @@ def measure_rows(torch, qn, inp, flush):
         torch.cuda.synchronize()
         floor.append(e0.elapsed_time(e1))
     rows["launch_floor_us"] = round(sorted(floor)[len(floor) // 2] * 1e3, 2)
+    # Beside each HBM row's event time, the same row less that floor: an
+    # estimate of the kernel's own time (the kernel trace of these launches
+    # gives the measured one)
+    fl = rows["launch_floor_us"] * 1e-6
+    for name, row in rows.items():
+        if isinstance(row, dict) and "GB/s" in row and row["us"] * 1e-6 > fl:
+            sec = row["us"] * 1e-6 - fl
+            nbytes = row["GB/s"] * 1e9 * row["us"] * 1e-6
+            row["us_less_floor"] = round(sec * 1e6, 2)
+            row["frac_less_floor"] = round(nbytes / sec / PEAK_HBM, 4)
     return rows
 
 
@@ -630,6 +640,48 @@ def run_suite(torch, qn):
                                 "quantize_alone_GB/s": round(BPW_QUANT_F32 * nweights / (msq / 1e3) / 1e9, 1)}
     packed_bytes = sum(w.packed.numel() + w.c8.numel() + 4 * w.dq_scale.numel() for _, _, _, w in stack)
     res["c4_stack_resident_GB"] = round(packed_bytes / 1e9, 3)
+
+    # (1b) the same stack from bf16 weights (the same seeded values rounded
+    # to bf16), quantize + double quant; outputs discarded
+    print("suite: quantizing the 7B stack from bf16", file=sys.stderr, flush=True)
+    tq.arm()
+    td.arm()
+    for layer in range(32):
+        for i, (name, n, k) in enumerate(LLAMA7B_LAYER):
+            Wb = dev_randn((n, k), 0.02, 1000 * layer + i, torch.bfloat16)
+            qn.quantize_weight(Wb)
+            del Wb
+    torch.cuda.synchronize()
+    nqb, msqb = tq.read()
+    ndb, msdb = td.read()
+    tq.disarm()
+    td.disarm()
+    qbytes_b = (BPW_QUANT_BF16 + BPW_DQ) * nweights
+    res["c4_stack_quantize_bf16"] = {"quantize_ms": round(msqb, 3), "double_quant_ms": round(msdb, 3),
+                                     "launches": nqb + ndb,
+                                     "GB/s": round(qbytes_b / ((msqb + msdb) / 1e3) / 1e9, 1),
+                                     "frac": round(qbytes_b / ((msqb + msdb) / 1e3) / PEAK_HBM, 4),
+                                     "quantize_alone_GB/s": round(BPW_QUANT_BF16 * nweights / (msqb / 1e3) / 1e9, 1),
+                                     "quantize_alone_frac": round(BPW_QUANT_BF16 * nweights / (msqb / 1e3) / PEAK_HBM,
+                                                                  4)}
+
+    # (1c) the whole packed stack dequantized to bf16 (3.3 GB in, 13 GB out):
+    # one output buffer per shape, overwritten; the library's dequantize timer
+    # summed over the 224 launches
+    print("suite: dequantizing the 7B stack", file=sys.stderr, flush=True)
+    outs_dq = {(n, k): torch.empty(n, k, dtype=torch.bfloat16, device="cuda") for _, n, k in LLAMA7B_LAYER}
+    tdq = qn.KernelTimer(3)
+    tdq.arm()
+    for _, n, k, w in stack:
+        qn.nf4_dequantize(w, out=outs_dq[(n, k)])
+    torch.cuda.synchronize()
+    ndq, msdq = tdq.read()
+    tdq.disarm()
+    dq_bytes = BPW_DEQUANT * nweights
+    res["c4_stack_dequantize_bf16"] = {"launches": ndq, "kernel_ms": round(msdq, 3), "GB": round(dq_bytes / 1e9, 2),
+                                       "GB/s": round(dq_bytes / (msdq / 1e3) / 1e9, 1),
+                                       "frac": round(dq_bytes / (msdq / 1e3) / PEAK_HBM, 4)}
+    del outs_dq
 
     # (2) one decode GEMV pass over all 224 linears, r = 16, T in {1, 16}:
     # the sum of the GEMV kernel times, and the wall time of the pass
