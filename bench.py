@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--cpu-suite", action="store_true",
                     help="host only: the oracle on 7B stack layer 0 (x32 extrapolated) and one 65B-shaped matrix of "
                          "each shape at T = 4096, one JSON line")
+    ap.add_argument("--fwd-u", action="store_true",
+                    help="instead of the step: the 7B gate forward at T = 1024, r = 16 with U inside the GEMM "
+                         "launch and with a separate projection launch first (eager calls and graph replays), "
+                         "one JSON line")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step: the wider measurement set (32-layer 7B stack, 65B linears, "
                          "a GEMV pass over the stack, residency, torch.matmul context), one JSON line")
@@ -198,14 +202,21 @@ def measured_traffic(kernel):
         return None
 
 
-def per_launch_work(inp):
-    """Algorithmic work of one launch of each kernel in the step (all launches
-    of a kernel in the step do the same work, except where noted)."""
-    m = inp.mlp_dev[0]
-    N, K, T, r = m["N"], m["K"], m["T"], m["r"]
+def per_launch_work(qn, inp):
+    """Algorithmic work of one launch of each kernel in the step, averaged
+    over the step's launches of it (the per-kernel timers come from eager
+    steps: there U = X A^T runs inside the forward GEMM launch where the
+    library says so, else in a separate projection launch; G = s dY B always
+    runs outside the dX GEMM)."""
+    fwd, dx = [], []
+    for m in inp.mlp_dev:
+        N, K, T, r = m["N"], m["K"], m["T"], m["r"]
+        u_in = qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r)
+        fwd.append(fwd_flops(N, K, T, r) - (0 if u_in else 2 * T * K * r))
+        dx.append(dx_flops(N, K, T, r) - 2 * T * N * r)
     return {
-        "gemm_fwd": ("mfma", fwd_flops(N, K, T, r) - 2 * T * K * r, "TFLOP/s"),  # U = X A^T runs outside
-        "gemm_dx": ("mfma", dx_flops(N, K, T, r) - 2 * T * N * r, "TFLOP/s"),  # G = s dY B runs outside
+        "gemm_fwd": ("mfma", sum(fwd) / len(fwd), "TFLOP/s"),
+        "gemm_dx": ("mfma", sum(dx) / len(dx), "TFLOP/s"),
     }
 
 
@@ -253,7 +264,11 @@ def measure_rows(torch, qn, inp, flush):
     w = qn.quantize_weight(m["W"])
     N, K, T, r = m["N"], m["K"], m["T"], m["r"]
     sec = timed(5, lambda: qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"]))
-    rows["gemm_fwd_T1024_11008x4096"] = _mfma_row(fwd_flops(N, K, T, r) - 2 * T * K * r, sec)
+    # U = X A^T inside this launch (eager calls where the library says so),
+    # else in a separate projection launch
+    u_in = qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r)
+    rows["gemm_fwd_T1024_11008x4096"] = dict(_mfma_row(fwd_flops(N, K, T, r) - (0 if u_in else 2 * T * K * r), sec),
+                                             u_in_launch=bool(u_in))
     _, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
     sec = timed(6, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U,
                                               need_da=False, need_db=False))
@@ -911,6 +926,50 @@ def run_suite(torch, qn):
                                       reps=11) * 1e6, 1)}
     return res
 
+def compare_fwd_u(torch, qn):
+    """The forward of the 7B gate projection (11008 x 4096, T = 1024, r = 16)
+    issued both ways, in alternating rounds: U = X A^T computed by the
+    GEMM's first workgroups (one launch) and by a separate projection launch
+    before the GEMM (QLORA_NF4_FWD_U=prepass). HIP events around 20
+    back-to-back eager calls; captured launches always take the separate
+    projection, so graph replays of each mode time the same kernels."""
+    N, K, T, r = 11008, 4096, 1024, 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    W = torch.randn(N, K, device="cuda", generator=g) * 0.02
+    X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+    A = (torch.randn(r, K, device="cuda", generator=g) / K).to(torch.bfloat16)
+    B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    w = qn.quantize_weight(W)
+    Y = torch.empty(T, N, dtype=torch.bfloat16, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"shape": [N, K], "T": T, "r": r, "in_launch_applies": qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r)}
+    times = {"in_launch": [], "separate_projection": []}
+    outs = {}
+    for rnd in range(3):
+        for mode in ("in_launch", "separate_projection"):
+            if mode == "separate_projection":
+                os.environ["QLORA_NF4_FWD_U"] = "prepass"
+            else:
+                os.environ.pop("QLORA_NF4_FWD_U", None)
+            for _ in range(3):
+                qn.qlora_linear_fwd(w, X, A, B, 2.0, out=Y)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(20):
+                qn.qlora_linear_fwd(w, X, A, B, 2.0, out=Y)
+            e1.record()
+            torch.cuda.synchronize()
+            times[mode].append(e0.elapsed_time(e1) / 20 * 1e3)
+            outs[mode] = Y.clone()
+    os.environ.pop("QLORA_NF4_FWD_U", None)
+    for mode, v in times.items():
+        res[mode + "_us"] = round(sorted(v)[1], 1)
+        res[mode + "_rounds_us"] = [round(x, 1) for x in v]
+    res["same_bits"] = bool(torch.equal(outs["in_launch"], outs["separate_projection"]))
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -928,6 +987,9 @@ def main():
     torch.cuda.set_device(0)
     if args.suite:
         print(json.dumps({"suite": run_suite(torch, qn)}), flush=True)
+        return
+    if args.fwd_u:
+        print(json.dumps({"fwd_u": compare_fwd_u(torch, qn)}), flush=True)
         return
     print("bench: generating inputs", file=sys.stderr, flush=True)
     inp = Inputs(torch, workloads)
@@ -999,7 +1061,7 @@ def main():
 
     # dominant kernel: the largest total time in the timed steps
     dom = max(kstats, key=lambda k: kstats[k][1])
-    work = per_launch_work(inp)
+    work = per_launch_work(qn, inp)
     roof = None
     if dom in work:
         bound, per_launch, unit = work[dom]

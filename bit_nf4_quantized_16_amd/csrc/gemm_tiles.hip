@@ -31,6 +31,7 @@
 #include <cstring>
 
 #include "mm_common.h"
+#include "proj_dma.h"
 
 namespace qlnf4 {
 
@@ -50,6 +51,16 @@ struct TileArgs {
     int tiles_a, tiles_t;
     int splits;   // > 1: the reduction is split over gridDim.y workgroups
     float* part;  // split partial tiles, fp32 [splits, T, MA]
+    // Forward with U computed inside the launch (nu > 0; one reduction
+    // split, rank r_u <= 16 and a multiple of 8): workgroups [0, nu) run the
+    // projection U = X A^T of one 16-token block each (proj, unsplit) and
+    // store the raw sums as tagged words uword[t][j]; a tile reads its
+    // tokens' words before the rank step, in place of lt, as bf16(s_u v).
+    int nu;
+    ProjArgs proj;
+    int r_u;
+    float s_u;
+    int spin;  // word loads before the tile forms its tokens' U itself
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -135,6 +146,30 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wa = wave / WT, wt = wave % WT;
+    __shared__ int s_flag;
+
+    // ---- U inside the launch (forward, 256 x 256 tile): projection workgroups
+    // The projection's ring slots and partial sums live in the tile's stages.
+    constexpr bool kUin = !DX && TA == 256 && TT == 256 && NW == 8;
+    auto proj_lds = [&]() {
+        using D = ProjDma<1>;
+        return ProjLds<1>{{reinterpret_cast<uint16_t(*)[D::PS]>(sX0), reinterpret_cast<uint16_t(*)[D::PS]>(sX0 + D::PS * D::NW),
+                           reinterpret_cast<uint16_t(*)[D::PS]>(sX1)},
+                          {reinterpret_cast<uint16_t(*)[D::QS]>(sX1 + D::PS * D::NW), reinterpret_cast<uint16_t(*)[D::QS]>(sA0),
+                           reinterpret_cast<uint16_t(*)[D::QS]>(sA0 + D::QS * D::NW)},
+                          reinterpret_cast<float(*)[16][16]>(sA1), &s_flag};
+    };
+    const int ntiles = p.tiles_a * p.tiles_t;
+    if constexpr (kUin) {
+        static_assert(ProjDma<1>::NW == NW, "projection workgroups have the tile's eight waves");
+        static_assert(2 * ProjDma<1>::PS * NW <= TT * kStep && 2 * ProjDma<1>::QS * NW <= S::ROWS_A * LDA &&
+                          NW * 256 * 4 <= S::ROWS_A * LDA * 2,
+                      "the projection's LDS fits in the stages");
+        if (static_cast<int>(blockIdx.x) < p.nu) {
+            proj_dma_block<1, false>(p.proj, static_cast<int>(blockIdx.x), 0, 1, proj_lds());
+            return;
+        }
+    }
     // dX: with eight waves, the two waves that share a SIMD (w and w+4) run
     // the two halves of a step in opposite order, so one expands codes (VALU)
     // while the other feeds the matrix core. The forward instead interleaves
@@ -144,8 +179,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     // Workgroups are handed to the eight XCDs round robin; give each XCD a
     // contiguous range of tiles, token-major, so one XCD's L2 serves the same
     // activation rows to all its workgroups.
-    const int ntiles = p.tiles_a * p.tiles_t;
-    const int g = blockIdx.x, qx = ntiles / 8, rem = ntiles % 8, x = g % 8;
+    const int g = static_cast<int>(blockIdx.x) - p.nu, qx = ntiles / 8, rem = ntiles % 8, x = g % 8;
     const int logical = x * qx + (x < rem ? x : rem) + g / 8;
     const int64_t m0 = static_cast<int64_t>(logical % p.tiles_a) * TA;
     const int64_t t0 = static_cast<int64_t>(logical / p.tiles_a) * TT;
@@ -362,17 +396,104 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     }
     }  // sb < se
 
-    // LoRA term: rp/64 more reduction steps over the rank, staged directly
-    // (by the first split only).
-    for (int ls = 0; ls < (split == 0 ? p.rp / kStep : 0); ++ls) {
-        const int64_t j0 = static_cast<int64_t>(ls) * kStep;
+    // U inside the launch: the token operand of the rank step from the
+    // words of this tile's tokens (TT x r_u, at most 8 a thread), each
+    // converted as the separate projection converts it, bf16(s_u v), and
+    // stored straight into the stage (a retry overwrites it). While any tag
+    // is not this launch's, the workgroup sleeps and loads again, at most
+    // spin times. The projection workgroups come first in the grid and wait
+    // on nothing, so that bound is a safety net only: should it run out, the
+    // tile forms its U values itself, each an fp32 sum of the products in k
+    // order (plain fused multiply-adds, a few registers; the same values up
+    // to rounding, not bit for bit). Ranks r_u .. 63 are zero.
+    auto stage_u_words = [&]() {
+        if constexpr (kUin) {
+        constexpr int WPT = TT * 16 / NTHR;  // words a thread, at most
+        const int lg = p.r_u == 16 ? 4 : 3;  // r_u is 8 or 16
+        const int nw = TT << lg;
+        auto stage_words = [&]() -> bool {
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < WPT; ++i) {
+                const int e = tid + NTHR * i;
+                if (e < nw) {
+                    const int row = e >> lg, j = e & (p.r_u - 1);
+                    const int64_t t = t0 + row;
+                    uint64_t wd = 0;
+                    if (t < p.T) {
+                        wd = __hip_atomic_load(p.proj.uword + (t << lg) + j, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        ok = ok && static_cast<uint32_t>(wd >> 32) == p.proj.tag;
+                    }
+                    sX0[row * kStep + 8 * ((j >> 3) ^ swz(row)) + (j & 7)] =
+                        to_bf16_bits(p.s_u * __uint_as_float(static_cast<uint32_t>(wd)));
+                }
+            }
+            return ok;
+        };
+        auto all_ok = [&](bool ok) -> bool {
+            __syncthreads();
+            if (tid == 0) s_flag = 1;
+            __syncthreads();
+            if (!ok) s_flag = 0;
+            __syncthreads();
+            return s_flag != 0;
+        };
+        bool ok = p.spin >= 0 && all_ok(stage_words());  // spin < 0: always form U locally (tests)
+        for (int it = 0; !ok && it < p.spin; ++it) {
+            __builtin_amdgcn_s_sleep(8);
+            ok = all_ok(stage_words());
+        }
+        if (!ok) {
+#pragma unroll 1
+            for (int i = 0; i < WPT; ++i) {
+                const int e = tid + NTHR * i;
+                if (e >= nw) continue;
+                const int row = e >> lg, j = e & (p.r_u - 1);
+                const int64_t t = t0 + row;
+                float u = 0.0f;
+                if (t < p.T) {
+                    const uint16_t* xr = p.proj.P + t * p.proj.ldp;
+                    const uint16_t* ar = p.proj.Q + j * p.proj.ldq;
+#pragma unroll 1
+                    for (int64_t k = 0; k < p.proj.kred; k += 8) {
+                        const uint4 xv = ld16(xr + k), av = ld16(ar + k);
+                        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            u = fmaf(bf16_to_f32(xw[q] & 0xFFFFu), bf16_to_f32(aw[q] & 0xFFFFu), u);
+                            u = fmaf(bf16_to_f32(xw[q] >> 16), bf16_to_f32(aw[q] >> 16), u);
+                        }
+                    }
+                }
+                sX0[row * kStep + 8 * ((j >> 3) ^ swz(row)) + (j & 7)] = to_bf16_bits(p.s_u * u);
+            }
+        }
+        // ranks r_u .. 63 are zero
 #pragma unroll
         for (int i = 0; i < TT * 8 / NTHR; ++i) {
             const int c = tid + NTHR * i;
             const int row = c >> 3, lc = c & 7;
-            const int64_t t = t0 + row;
-            const uint4 v = (t < p.T) ? ld16(p.lt + t * p.rp + j0 + 8 * lc) : make_uint4(0, 0, 0, 0);
-            st16(sX0 + row * kStep + 8 * (lc ^ swz(row)), v);
+            if (8 * lc >= p.r_u) st16(sX0 + row * kStep + 8 * (lc ^ swz(row)), make_uint4(0, 0, 0, 0));
+        }
+        }
+    };
+
+    // LoRA term: rp/64 more reduction steps over the rank, staged directly
+    // (by the first split only).
+    for (int ls = 0; ls < (split == 0 ? p.rp / kStep : 0); ++ls) {
+        const int64_t j0 = static_cast<int64_t>(ls) * kStep;
+        if (kUin && p.nu > 0) {
+            stage_u_words();  // rp == 64: the one rank step
+        } else {
+#pragma unroll
+            for (int i = 0; i < TT * 8 / NTHR; ++i) {
+                const int c = tid + NTHR * i;
+                const int row = c >> 3, lc = c & 7;
+                const int64_t t = t0 + row;
+                const uint4 v = (t < p.T) ? ld16(p.lt + t * p.rp + j0 + 8 * lc) : make_uint4(0, 0, 0, 0);
+                st16(sX0 + row * kStep + 8 * (lc ^ swz(row)), v);
+            }
         }
         if constexpr (!DX) {
             // B rows n, 64 rank columns
@@ -494,7 +615,7 @@ __global__ void split_reduce_kernel(const float* __restrict__ part, int splits, 
 }
 
 template <bool DX>
-int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStream_t stream) {
+int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStream_t stream, int nu = 0) {
     const int64_t MA = DX ? a.K : a.N;
     const GemmPlan pl = plan_gemm(MA, a.T, DX ? a.N : a.K);
     const int tile = pl.tile;
@@ -503,7 +624,11 @@ int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStr
     a.splits = pl.splits;
     a.part = split_ws;
     if (a.splits > 1 && split_ws == nullptr) return set_error(QL_ERR_WORKSPACE, "%s: split workspace missing", what);
-    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.tiles_a) * a.tiles_t), static_cast<uint32_t>(a.splits));
+    a.nu = nu;
+    if (nu > 0 && (DX || tile != 256 || a.splits != 1))
+        return set_error(QL_ERR_UNSUPPORTED, "%s: U inside the launch needs the unsplit 256 tile", what);
+    const dim3 grid(static_cast<uint32_t>(nu + static_cast<int64_t>(a.tiles_a) * a.tiles_t),
+                    static_cast<uint32_t>(a.splits));
     timer_begin(kid, stream);
     if (tile == 256) {
         if (a.w.dq)
@@ -564,7 +689,7 @@ size_t gemm_split_bytes(int64_t MA, int64_t T, int64_t RED) {
 
 int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, const uint16_t* Bsrc, int64_t ld_b,
                     int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream) {
-    TileArgs a;
+    TileArgs a{};
     a.w = w;
     a.act = X;
     a.ld_act = K;
@@ -580,9 +705,65 @@ int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, cons
     return launch_tiles<false>(a, split_ws, QL_KERNEL_GEMM_FWD, "dequant GEMM forward", stream);
 }
 
+bool gemm_fwd_u_in_launch(int64_t N, int64_t K, int64_t T, int r) {
+    if (r != 8 && r != 16) return false;
+    if (const char* e = std::getenv("QLORA_NF4_FWD_U"))
+        if (std::strcmp(e, "prepass") == 0) return false;
+    const GemmPlan pl = plan_gemm(N, T, K);
+    return pl.tile == 256 && pl.splits == 1 && lora_proj_splits(T, r, K, false) == 1;
+}
+
+size_t gemm_fwd_u_words(int64_t T, int r) { return static_cast<size_t>(T) * r; }
+
+int launch_gemm_fwd_u(const NF4Dev& w, const uint16_t* X, const uint16_t* A, const uint16_t* B, int r, float scale,
+                      uint16_t* Y, float* U_out, int64_t T, int64_t N, int64_t K, uint64_t* words, hipStream_t stream) {
+    TileArgs a{};
+    a.w = w;
+    a.act = X;
+    a.ld_act = K;
+    a.lt = nullptr;
+    a.la = B;
+    a.ld_la = r;
+    a.r_la = r;
+    a.rp = 64;
+    a.out = Y;
+    a.T = T;
+    a.N = N;
+    a.K = K;
+    // the projection workgroups: U = X A^T of one 16-token block each,
+    // fp32 U for the caller and the raw sums as words tagged for this launch
+    ProjArgs& pj = a.proj;
+    pj.proj = 1;
+    pj.P = X;
+    pj.ldp = K;
+    pj.Q = A;
+    pj.ldq = K;
+    pj.rq = r;
+    pj.T = T;
+    pj.kred = K;
+    pj.alpha_f = 1.0f;
+    pj.out_f = U_out;
+    pj.ld_f = r;
+    pj.alpha_b = scale;
+    pj.uword = words;
+    pj.token = next_token();
+    // a fresh tag per launch, so words left in the workspace by earlier
+    // launches never pass for this one's (the caller runs captured launches,
+    // whose replays would reuse it, with the separate projection instead)
+    pj.tag = static_cast<uint32_t>(pj.token % 0xFFFFFFFFull) + 1u;
+    a.r_u = r;
+    a.s_u = scale;
+    // QLORA_NF4_GEMM_SPIN=n: loads of the words before a tile forms U
+    // itself (a negative n: at once, without reading the words)
+    const char* e = std::getenv("QLORA_NF4_GEMM_SPIN");
+    a.spin = e ? std::atoi(e) : (1 << 14);
+    return launch_tiles<false>(a, nullptr, QL_KERNEL_GEMM_FWD, "dequant GEMM forward", stream,
+                               static_cast<int>(ceil_div(T, 16)));
+}
+
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
                    uint16_t* dX, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream) {
-    TileArgs a;
+    TileArgs a{};
     a.w = w;
     a.act = dY;
     a.ld_act = N;

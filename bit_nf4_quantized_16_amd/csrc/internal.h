@@ -77,10 +77,17 @@ struct ProjArgs {
     float* part;
     uint64_t* cnt;
     uint64_t token;
+    // optional: the raw sums v (before alpha_f / alpha_b) as tagged words
+    // uword[t][j] = tag << 32 | fp32 bits, j < rq, device-scope stores (the
+    // GEMM forward's tiles read them inside the same launch)
+    uint64_t* uword;
+    uint32_t tag;
 };
 // Workspace of a projection over T tokens, rank rq, reduction kred (0 when
 // its reduction is not split); ws must hold that many bytes, 16-B aligned.
 size_t lora_proj_ws_bytes(int64_t T, int rq, int64_t kred, bool q_cols);
+// Workgroups per 16-token block of that projection (1: unsplit).
+int lora_proj_splits(int64_t T, int rq, int64_t kred, bool q_cols);
 
 // A fresh 56-bit token per launch for the counters that kernels keep in a
 // workspace (a counter carrying another token counts as zero).
@@ -126,6 +133,17 @@ int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, cons
                     int r_b, int rp, uint16_t* Y, int64_t T, int64_t N, int64_t K, float* split_ws,
                     hipStream_t stream);
 // dX = dY W' + Gp A over the padded rank rp (Gp [T, rp] bf16, A [r, K]).
+// The forward with U = X A^T computed inside the GEMM launch (its first
+// workgroups; no separate projection launch): whether it applies to a
+// forward without dropout (rank 8 or 16, the 256 tile, no reduction split,
+// an unsplit projection; QLORA_NF4_FWD_U=prepass turns it off), and the
+// workspace words it needs (U as tagged words, 8 bytes each). Launches
+// being captured into a graph take the separate projection.
+bool gemm_fwd_u_in_launch(int64_t N, int64_t K, int64_t T, int r);
+size_t gemm_fwd_u_words(int64_t T, int r);
+// Y = X W'^T + s (X A^T) B^T with U_out = X A^T (optional), one launch.
+int launch_gemm_fwd_u(const NF4Dev& w, const uint16_t* X, const uint16_t* A, const uint16_t* B, int r, float scale,
+                      uint16_t* Y, float* U_out, int64_t T, int64_t N, int64_t K, uint64_t* words, hipStream_t stream);
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
                    uint16_t* dX, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream);
 

@@ -241,7 +241,8 @@ int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, in
  * the dequant-GEMV kernel: one launch, the adapter branch included (its
  * first workgroups compute U for the others; the workspace holds U's
  * partial sums and their flags, size 0 when r == 0); larger T the
- * dequant-in-LDS MFMA GEMM.
+ * dequant-in-LDS MFMA GEMM, after a projection launch for U or, where
+ * qlora_linear_fwd_u_in_launch says so, with U computed inside its launch.
  * K must be a multiple of 64 and N a multiple of 8. Y must not alias any
  * input.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE (T < 0, K % 64 != 0, N % 8 != 0, r < 0
@@ -249,6 +250,22 @@ int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, in
  * QL_ERR_HIP. T == 0 is a no-op.
  */
 size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
+/*
+ * qlora_linear_fwd_u_in_launch — 1 when qlora_linear_fwd (and _noalloc)
+ * with these sizes, on a stream that is not being captured into a graph,
+ * computes U = X A^T inside the dequant GEMM launch (its first workgroups,
+ * one per 16 tokens, run on CUs the GEMM's tiles leave free and hand U to
+ * the tiles through words tagged for the launch in the workspace), 0 when a
+ * separate projection launch precedes the GEMM or T <= 16 (the decode GEMV
+ * computes U inside its own launch). It applies to ranks 8 and 16 without
+ * dropout when the GEMM runs unsplit 256 x 256 tiles and the projection is
+ * unsplit; QLORA_NF4_FWD_U=prepass turns it off. A launch being captured
+ * always takes the separate projection (its replays would reuse the tag).
+ * Either way Y and U_out are the same bits (should a tile's bounded wait for
+ * the words run out, it forms its U values itself: equal up to fp32
+ * rounding). No errors: invalid sizes give 0.
+ */
+int qlora_linear_fwd_u_in_launch(int64_t rows, int64_t cols, int64_t T, int32_t r);
 int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
                      const uint16_t* B, int32_t r, float scale, uint16_t* Y, float* U_out,
                      void* ws, size_t ws_bytes, void* stream);

@@ -1,0 +1,124 @@
+"""The forward with U = X A^T computed inside the dequant GEMM launch (its
+first workgroups hand U to the tiles through words tagged for the launch)
+against the forward with a separate projection launch first: Y and U bit
+for bit, the oracle within the usual bar, ragged token counts, and the
+tile's local fallback (forced from the host, so every kernel still ends
+normally). A captured forward takes the separate projection (a replay would
+reuse the launch's tag): its replays with new inputs equal the eager
+in-launch calls bit for bit."""
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import TOL, bf16_to_np, f32_to_np, normwise_rel_err, oracle_weight
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import bit_nf4_quantized_16_amd as qn
+
+    assert torch.cuda.is_available()
+    return qn
+
+
+# (N, K, T, r): several tiles and token blocks, ragged T (a last 16-token
+# block and a last 256-token tile that are partial), rank 8 and 16
+SHAPES = [(1024, 512, 300, 16), (520, 256, 33, 8), (2048, 1024, 257, 16), (264, 192, 1000, 8)]
+
+
+def _case(N, K, T, r, seed):
+    W = workloads.normal_weight(N, K, 0.02, seed=seed)
+    return W, workloads.lora_case("fwd_u_N%dK%dT%d" % (N, K, T), W, T, r, 2.0 * r, 1 / K, 0.05, seed=seed + 1)
+
+
+def _fwd(qn, w, case):
+    X, A, B = (t.cuda() for t in (case.X, case.A, case.B))
+    Y, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    torch.cuda.synchronize()
+    return Y, U
+
+
+@pytest.mark.parametrize("N,K,T,r", SHAPES)
+def test_in_launch_u_equals_prepass_and_oracle(qn, monkeypatch, N, K, T, r):
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    W, case = _case(N, K, T, r, seed=N + T)
+    assert qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r) == 1
+    w = qn.quantize_weight(W.cuda())
+    Y1, U1 = _fwd(qn, w, case)
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    assert qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r) == 0
+    Y2, U2 = _fwd(qn, w, case)
+    assert torch.equal(U1, U2) and torch.equal(Y1, Y2)
+    ref = oracle_weight(W.numpy())
+    H, Uo = oracle.lora_forward(bf16_to_np(case.X), ref["wd"], bf16_to_np(case.A), bf16_to_np(case.B), case.scale)
+    assert normwise_rel_err(bf16_to_np(Y1), H) <= TOL
+    assert normwise_rel_err(f32_to_np(U1), Uo) <= TOL
+
+
+def test_in_launch_u_at_the_7b_mlp_shape(qn, monkeypatch):
+    """The 7B gate shape at T = 1024, r = 16 (the default plan takes the
+    in-launch U there): bitwise equal to the separate projection."""
+    N, K, T, r = 11008, 4096, 1024, 16
+    assert qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r) == 1
+    W = workloads.normal_weight(N, K, 0.02, seed=5)
+    X = workloads.bf16_normal((T, K), 1.0, seed=6).cuda()
+    A = workloads.bf16_normal((r, K), 1.0 / K, seed=7).cuda()
+    B = workloads.bf16_normal((N, r), 0.01, seed=8).cuda()
+    w = qn.quantize_weight(W.cuda())
+    Y1, U1 = qn.qlora_linear_fwd(w, X, A, B, 2.0)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    Y2, U2 = qn.qlora_linear_fwd(w, X, A, B, 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(U1, U2) and torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("N,K,T,r", SHAPES[:2])
+def test_local_u_fallback(qn, monkeypatch, N, K, T, r):
+    """QLORA_NF4_GEMM_SPIN=-1: every tile forms its U values itself (fp32
+    sums in k order) instead of reading the words. U_out still comes from
+    the projection workgroups (bit for bit); Y is within the oracle's bar
+    and within bf16 rounding of the separate-projection result."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    W, case = _case(N, K, T, r, seed=3 * N + T)
+    w = qn.quantize_weight(W.cuda())
+    Y2, U2 = _fwd(qn, w, case)
+    monkeypatch.setenv("QLORA_NF4_GEMM_SPIN", "-1")
+    Y1, U1 = _fwd(qn, w, case)
+    assert torch.equal(U1, U2)
+    assert normwise_rel_err(bf16_to_np(Y1), bf16_to_np(Y2).astype("float64")) <= 1e-2
+    ref = oracle_weight(W.numpy())
+    H, _ = oracle.lora_forward(bf16_to_np(case.X), ref["wd"], bf16_to_np(case.A), bf16_to_np(case.B), case.scale)
+    assert normwise_rel_err(bf16_to_np(Y1), H) <= TOL
+
+
+def test_captured_forward_replays_equal_eager_in_launch(qn, monkeypatch):
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    N, K, T, r = 1024, 512, 300, 16
+    W, case = _case(N, K, T, r, seed=77)
+    w = qn.quantize_weight(W.cuda())
+    A, B = case.A.cuda(), case.B.cuda()
+    X = torch.empty(T, K, dtype=torch.bfloat16, device="cuda")
+    xs = [workloads.bf16_normal((T, K), 1.0, seed=80 + i).cuda() for i in range(4)]
+    X.copy_(xs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qn.qlora_linear_fwd(w, X, A, B, case.scale)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Y, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    for rep in range(1, 7):
+        X.copy_(xs[rep % 4])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        Ye, Ue = qn.qlora_linear_fwd(w, xs[rep % 4], A, B, case.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Ye) and torch.equal(U, Ue), "replay %d differs from the eager call" % rep
