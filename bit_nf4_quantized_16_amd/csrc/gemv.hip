@@ -49,10 +49,10 @@ namespace qlnf4 {
 // so the U workgroups never wait on anything; should the retries still run
 // out, the workgroup computes U itself from the same partial products in the
 // same order (bit-identical). A launch being captured into a graph (its
-// replays reuse the token) also counts its U and row workgroups done (a
-// token-tagged count, tagged_arrive); the last one clears
-// the words, so a replay finds no word of the previous one. An eager launch
-// has a token of its own and skips the count.
+// replays reuse the token) also counts its U and row workgroups done
+// (count_arrival, on counters a fill kernel recorded before it zeroes); the
+// last one clears the words, so a replay finds no word of the previous one.
+// An eager launch has a token of its own and skips the count.
 //
 // One launch can serve up to kGemvGroup layers that read the same x (q/k/v,
 // gate/up): the argument holds a descriptor per layer (weight, adapters,
@@ -64,6 +64,14 @@ namespace qlnf4 {
 // Lanes of tokens >= T read token T-1 and their outputs are dropped; rows
 // past N read row N-1 and are dropped.
 // ===========================================================================
+// The fill kernel recorded before a captured launch: its done counters at zero.
+__global__ void zero_counters_kernel(CounterSet s) {
+    const int i = threadIdx.x;
+    if (i < kArriveWords)
+        for (int j = 0; j < 4; ++j)
+            if (s.c[j] != nullptr) __hip_atomic_store(s.c[j] + i, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int kGemvRows = 16;
 constexpr int kGemvWaves = 8;
 constexpr int kGemvUSteps = 4;  // steps of x in one U workgroup's slice (waves 0..3)
@@ -72,6 +80,7 @@ constexpr int kGemvUSteps = 4;  // steps of x in one U workgroup's slice (waves 
 // x (the same K, T, rank and scale), each with its own U workgroups, row
 // workgroups, outputs and workspace.
 constexpr int kGemvGroup = kGemvMaxGroup;
+static_assert(kGemvGroup <= 4, "one fill kernel zeroes the counters of every weight of a launch");
 
 struct GemvWeight {
     NF4Dev w;
@@ -81,7 +90,7 @@ struct GemvWeight {
     uint16_t* Y;
     float* U_out;     // [T, r] fp32 = X A^T, or null
     uint64_t* uword;  // [nks][T][r]: slice ks of U, tag << 32 | fp32 bits (r > 0)
-    uint64_t* done;   // [kArriveSub + 1]: token << 24 | count of workgroups done with the words (r > 0)
+    uint64_t* done;   // [kArriveWords]: counts of workgroups done with the words (captured launches, r > 0)
     int nu, nrow;     // its U and row workgroups
     int ub, rb;       // the grid index of its first U and first row workgroup
 };
@@ -231,14 +240,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     // words are stored, a row workgroup once it has U (from the words or
     // computed itself). The last of them clears the words, so a replay finds
     // none of the previous replay's; as every U workgroup counts too, no word
-    // can be stored after the clear (tagged_arrive: token-tagged counters in
-    // two levels that need no reset). The words are stored and loaded only as
+    // can be stored after the clear (count_arrival: two levels of counters,
+    // zeroed before the launch). The words are stored and loaded only as
     // agent-scope atomics, and every thread's accesses complete (vmcnt) before
     // the barrier and the count.
     auto count_done_and_clear = [&](int i) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): this thread's word accesses are done
         __syncthreads();
-        if (tid == 0) s_last = tagged_arrive(gw.done, p.token, i, gw.nu + gw.nrow);
+        if (tid == 0) s_last = count_arrival(gw.done, i, gw.nu + gw.nrow);
         __syncthreads();
         if (s_last)
             for (int e = tid; e < p.nks * T * r; e += 512)
@@ -476,7 +485,7 @@ GemvUPlan gemv_u_plan(int64_t T, int64_t K, int r) {
 size_t gemv_ws_bytes(int64_t T, int64_t K, int r) {
     if (r <= 0) return 0;
     const GemvUPlan u = gemv_u_plan(T, K, r);
-    return (u.part_bytes + (kArriveSub + 1) * sizeof(uint64_t) + 255) / 256 * 256;
+    return (u.part_bytes + kArriveWords * sizeof(uint64_t) + 255) / 256 * 256;
 }
 
 namespace {
@@ -557,6 +566,13 @@ int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t 
     }
     if (total >= (int64_t{1} << 31)) return set_error(QL_ERR_SHAPE, "dequant GEMV: grid too large");
     timer_begin(QL_KERNEL_GEMV, stream);
+    if (g.count_done) {
+        // the done counters start every replay at zero (a fill kernel, not a
+        // memset node: captured memsets are avoided on this platform)
+        CounterSet cs{};
+        for (int i = 0; i < nw; ++i) cs.c[i] = g.g[i].done;
+        hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, cs);
+    }
     const dim3 grid(static_cast<uint32_t>(total));
     const int64_t nbs = ceil_div(K / 64, 4);
     const int ns = static_cast<int>(std::min<int64_t>(ceil_div(nbs, kGemvWaves), 1 << 20));
