@@ -122,3 +122,18 @@ def test_captured_forward_replays_equal_eager_in_launch(qn, monkeypatch):
         Ye, Ue = qn.qlora_linear_fwd(w, xs[rep % 4], A, B, case.scale)
         torch.cuda.synchronize()
         assert torch.equal(Y, Ye) and torch.equal(U, Ue), "replay %d differs from the eager call" % rep
+
+
+def test_in_launch_u_without_u_out(qn, monkeypatch):
+    """save_u=False (U_out NULL): the projection workgroups still hand U to
+    the tiles; Y equals the separate projection's bit for bit."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    N, K, T, r = 2048, 1024, 257, 16
+    W, case = _case(N, K, T, r, seed=91)
+    w = qn.quantize_weight(W.cuda())
+    X, A, B = (t.cuda() for t in (case.X, case.A, case.B))
+    Y1, U1 = qn.qlora_linear_fwd(w, X, A, B, case.scale, save_u=False)
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    Y2, _ = qn.qlora_linear_fwd(w, X, A, B, case.scale, save_u=False)
+    torch.cuda.synchronize()
+    assert U1 is None and torch.equal(Y1, Y2)

@@ -37,6 +37,9 @@ PAIRS = [
     # 4096 x 11008 weight at T = 1024, 64 MiB of split-K partials
     ((4096, 11008, 1024, 16), (520, 1088, 40, 16)),
     ((520, 1088, 300, 70), (264, 192, 17, 5)),
+    # GEMM with U computed inside its launch (7B gate at T = 1024, r = 16):
+    # the tagged U words live in the scratch
+    ((11008, 4096, 1024, 16), (1024, 512, 300, 8)),
 ]
 
 
