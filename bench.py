@@ -221,63 +221,87 @@ def per_launch_work(qn, inp):
 
 
 def measure_rows(torch, qn, inp, flush):
-    """Cold-cache throughput of each stage: a 512 MiB buffer is overwritten
-    before every timed repetition; the kernel time is the library's HIP-event
-    timer of that stage's main kernel."""
+    """Cold-cache throughput of each stage: 5 untimed warm-up calls, then 20
+    timed ones, each after a 1 GiB buffer is overwritten (L2 and the 256 MB
+    last-level cache hold none of the inputs); the time of a call is the
+    library's HIP-event timer of that stage's main kernel, recorded on the
+    launch stream. Rows give the median (us) and the minimum (us_min); the
+    throughput is from the median."""
     rows = {}
-    reps = 5
+    reps = 20
+    mins = {}
 
     def timed(kid, fn):
         t = qn.KernelTimer(kid)
-        for _ in range(2):
+        for _ in range(5):
             fn()
         torch.cuda.synchronize()
-        t.arm()
+        ts = []
         for _ in range(reps):
             flush()
+            t.arm()
             fn()
-        n, ms = t.read()
-        t.disarm()
-        return ms / max(n, 1) / 1e3
+            torch.cuda.synchronize()
+            n, ms = t.read()
+            t.disarm()
+            ts.append(ms / max(n, 1) / 1e3)
+        ts.sort()
+        timed.last_min = ts[0]
+        return ts[len(ts) // 2]
 
     na = 4096 * 4096
     W = inp.W_attn
     sec = timed(1, lambda: qn.nf4_quantize(W))
-    rows["quantize_f32_4096x4096"] = _hbm_row(BPW_QUANT_F32 * na, sec)
+    rows["quantize_f32_4096x4096"] = _hbm_row(BPW_QUANT_F32 * na, sec, timed.last_min)
     Wb = W.to(torch.bfloat16)
     sec = timed(1, lambda: qn.nf4_quantize(Wb))
-    rows["quantize_bf16_4096x4096"] = _hbm_row(BPW_QUANT_BF16 * na, sec)
+    rows["quantize_bf16_4096x4096"] = _hbm_row(BPW_QUANT_BF16 * na, sec, timed.last_min)
     Wm = inp.mlp_dev[0]["W"]
     sec = timed(1, lambda: qn.nf4_quantize(Wm))
-    rows["quantize_f32_11008x4096"] = _hbm_row(BPW_QUANT_F32 * Wm.numel(), sec)
+    rows["quantize_f32_11008x4096"] = _hbm_row(BPW_QUANT_F32 * Wm.numel(), sec, timed.last_min)
+    Wmb = Wm.to(torch.bfloat16)
+    sec = timed(1, lambda: qn.nf4_quantize(Wmb))
+    rows["quantize_bf16_11008x4096"] = _hbm_row(BPW_QUANT_BF16 * Wm.numel(), sec, timed.last_min)
+    del Wmb
     _, absmax = qn.nf4_quantize(W)
     sec = timed(2, lambda: qn.nf4_double_quant(absmax))
-    rows["dq_encode_4096x4096"] = _hbm_row((4 + 1 + 4 / 256) / 64 * na, sec)
+    rows["dq_encode_4096x4096"] = _hbm_row((4 + 1 + 4 / 256) / 64 * na, sec, timed.last_min)
     wa = qn.quantize_weight(W)
     sec = timed(3, lambda: qn.nf4_dequantize(wa))
-    rows["dequantize_bf16_4096x4096"] = _hbm_row(BPW_DEQUANT * na, sec)
+    rows["dequantize_bf16_4096x4096"] = _hbm_row(BPW_DEQUANT * na, sec, timed.last_min)
     r = inp.attn.r
     for T, X in ((1, inp.X1), (16, inp.X16)):
         sec = timed(4, lambda: qn.qlora_linear_fwd(wa, X, inp.A_attn, inp.B_attn, inp.s_attn))
-        rows["gemv_T%d_4096x4096" % T] = _hbm_row(gemv_bytes(4096, 4096, T, r), sec)
+        rows["gemv_T%d_4096x4096" % T] = _hbm_row(gemv_bytes(4096, 4096, T, r), sec, timed.last_min)
     m = inp.mlp_dev[0]
     w = qn.quantize_weight(m["W"])
+    sec = timed(3, lambda: qn.nf4_dequantize(w))
+    rows["dequantize_bf16_11008x4096"] = _hbm_row(BPW_DEQUANT * w.rows * w.cols, sec, timed.last_min)
+    # decode GEMVs on the MLP shapes (x of the first T tokens of the layer's input)
+    wd = qn.quantize_weight(inp.mlp_dev[2]["W"])
+    for ww, mm in ((w, m), (wd, inp.mlp_dev[2])):
+        for T in (1, 16):
+            Xt = mm["X"][:T].contiguous()
+            sec = timed(4, lambda: qn.qlora_linear_fwd(ww, Xt, mm["A"], mm["B"], mm["s"]))
+            rows["gemv_T%d_%dx%d" % (T, ww.rows, ww.cols)] = _hbm_row(gemv_bytes(ww.rows, ww.cols, T, mm["r"]), sec,
+                                                                      timed.last_min)
+    del wd
     N, K, T, r = m["N"], m["K"], m["T"], m["r"]
     sec = timed(5, lambda: qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"]))
     # U = X A^T inside this launch (eager calls where the library says so),
     # else in a separate projection launch
     u_in = qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r)
-    rows["gemm_fwd_T1024_11008x4096"] = dict(_mfma_row(fwd_flops(N, K, T, r) - (0 if u_in else 2 * T * K * r), sec),
-                                             u_in_launch=bool(u_in))
+    rows["gemm_fwd_T1024_11008x4096"] = dict(_mfma_row(fwd_flops(N, K, T, r) - (0 if u_in else 2 * T * K * r), sec,
+                                                       timed.last_min), u_in_launch=bool(u_in))
     _, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
     sec = timed(6, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U,
                                               need_da=False, need_db=False))
-    rows["gemm_dx_T1024_11008x4096"] = _mfma_row(dx_flops(N, K, T, r) - 2 * T * N * r, sec)
+    rows["gemm_dx_T1024_11008x4096"] = _mfma_row(dx_flops(N, K, T, r) - 2 * T * N * r, sec, timed.last_min)
     sec = timed(7, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_dx=False))
-    rows["lora_grad_T1024_11008x4096"] = _hbm_row(lora_grad_bytes(N, K, T, r), sec)  # dA and dB, one launch
+    rows["lora_grad_T1024_11008x4096"] = _hbm_row(lora_grad_bytes(N, K, T, r), sec, timed.last_min)  # dA and dB
     # adapter merge of the same weight: codes and constants in, bf16 out, A and B read once
     sec = timed(8, lambda: qn.qlora_merge(w, m["A"], m["B"], m["s"]))
-    rows["merge_r%d_11008x4096" % r] = _hbm_row(BPW_DEQUANT * N * K + 2 * r * (N + K), sec)
+    rows["merge_r%d_11008x4096" % r] = _hbm_row(BPW_DEQUANT * N * K + 2 * r * (N + K), sec, timed.last_min)
     # dropout (p = 0.05) on the adapter input of the same layer: the masking
     # pass (X and the keep bits in, X * keep out) and the masked adapter term
     # of dX (dX, G, the bits in, dX out; A is L2-resident)
@@ -285,13 +309,14 @@ def measure_rows(torch, qn, inp, flush):
 
     bits = workloads.pack_keep_bits(workloads.keep_mask(T, K, 0.05, 31)).cuda()
     sec = timed(10, lambda: qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"], keep=bits, p=0.05))
-    rows["dropout_keep_apply_T1024_K4096"] = _hbm_row(T * K * (2 + 2 + 1 / 8), sec)
+    rows["dropout_keep_apply_T1024_K4096"] = _hbm_row(T * K * (2 + 2 + 1 / 8), sec, timed.last_min)
     sec = timed(11, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_da=False,
                                                need_db=False, keep=bits, p=0.05))
-    rows["dropout_dx_term_T1024_K4096"] = _hbm_row(T * K * (2 + 2 + 1 / 8) + 2 * T * 64 + 2 * r * K, sec)
+    rows["dropout_dx_term_T1024_K4096"] = _hbm_row(T * K * (2 + 2 + 1 / 8) + 2 * T * 64 + 2 * r * K, sec,
+                                                   timed.last_min)
     # quantization-error measurement on the uniform grid, fp32 weight read once
     sec = timed(9, lambda: qn.q4_quant_error(m["W"], "uniform"))
-    rows["quant_error_uniform_f32_11008x4096"] = _hbm_row(4 * N * K, sec)
+    rows["quant_error_uniform_f32_11008x4096"] = _hbm_row(4 * N * K, sec, timed.last_min)
     rows.update(measure_adamw_rows(torch, qn, flush))
     # dispatch floor: the same HIP-event timing around a kernel that does
     # nothing measurable (a one-element fill), cold cache as above
@@ -379,14 +404,20 @@ def measure_adamw_rows(torch, qn, flush):
     return rows
 
 
-def _hbm_row(nbytes, sec):
+def _hbm_row(nbytes, sec, sec_min=None):
     gbs = nbytes / sec / 1e9
-    return {"us": round(sec * 1e6, 2), "GB/s": round(gbs, 1), "frac": round(gbs * 1e9 / PEAK_HBM, 4)}
+    row = {"us": round(sec * 1e6, 2), "GB/s": round(gbs, 1), "frac": round(gbs * 1e9 / PEAK_HBM, 4)}
+    if sec_min is not None:
+        row["us_min"] = round(sec_min * 1e6, 2)
+    return row
 
 
-def _mfma_row(flops, sec):
+def _mfma_row(flops, sec, sec_min=None):
     tf = flops / sec / 1e12
-    return {"us": round(sec * 1e6, 2), "TFLOP/s": round(tf, 1), "frac": round(tf * 1e12 / PEAK_BF16, 4)}
+    row = {"us": round(sec * 1e6, 2), "TFLOP/s": round(tf, 1), "frac": round(tf * 1e12 / PEAK_BF16, 4)}
+    if sec_min is not None:
+        row["us_min"] = round(sec_min * 1e6, 2)
+    return row
 
 
 def _host_threads():
@@ -1102,7 +1133,7 @@ def main():
     if not args.eager:
         out["clock"] = clock
     if not args.no_rows:
-        flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flushbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         print("bench: per-stage cold-cache rows", file=sys.stderr, flush=True)
         out["rows"] = measure_rows(torch, qn, inp, lambda: flushbuf.fill_(1))
     if not args.no_cpu_baseline:
