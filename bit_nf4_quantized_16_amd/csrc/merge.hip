@@ -31,6 +31,8 @@
 
 namespace qlnf4 {
 
+typedef uint32_t u32x4m __attribute__((ext_vector_type(4)));
+
 namespace {
 
 constexpr int kMergeCols = 256;  // columns (k) per workgroup window
@@ -191,7 +193,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(NF4Dev w, int N, i
             const int row = srow + 2 * i;
             const uint4 v = *reinterpret_cast<const uint4*>(sO + row * kMergeLdA + scol);
             const int n = std::min(16 * rbi + row, N - 1);
-            *reinterpret_cast<uint4*>(out + static_cast<int64_t>(n) * K + ocol) = v;
+            // streaming store: the merged weight is written once, not read here
+            __builtin_nontemporal_store(u32x4m{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<u32x4m*>(out + static_cast<int64_t>(n) * K + ocol));
         }
         __syncthreads();
     };
