@@ -159,10 +159,9 @@ FwdWs carve_fwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool drop 
         const size_t gb = gemv_ws_bytes(T, K, r);
         if (gb) f.gemv = c.take<char>(gb);
     } else {
-        // U inside the GEMM launch needs its words; a captured launch takes
-        // the separate projection and its buffers, so both are carved
-        if (r > 0 && !drop && gemm_fwd_u_in_launch(N, K, T, r)) f.uword = c.take<uint64_t>(gemm_fwd_u_words(T, r));
-        if (r > 0) {
+        if (r > 0 && !drop && gemm_fwd_u_in_launch(N, K, T, r)) {
+            f.uword = c.take<uint64_t>(gemm_fwd_u_words(T, r));  // U inside the GEMM launch
+        } else if (r > 0) {
             if (drop) f.Xd = c.take<uint16_t>(static_cast<size_t>(T) * K);
             f.Us = c.take<uint16_t>(static_cast<size_t>(T) * rp);
             if (r % 8 != 0) f.Bp = c.take<uint16_t>(static_cast<size_t>(N) * rp);
@@ -376,16 +375,7 @@ int linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint1
     const FwdWs f = carve_fwd(ws, N, K, T, r, drop);
     const NF4Dev wd = to_dev(w);
     if (T <= kGemvMaxT && !drop) return launch_gemv(wd, X, T, N, K, A, B, r, scale, Y, U_out, f.gemv, st);
-    if (f.uword != nullptr) {
-        // eager launches only: a graph replays a launch with its tag, so words
-        // of the previous replay would pass for the current one's, and
-        // counting the workgroups done to clear them measured slower than the
-        // separate projection launch it saves
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(st, &cs) != hipSuccess) return set_error(QL_ERR_HIP, "forward: capture query");
-        if (cs == hipStreamCaptureStatusNone)
-            return launch_gemm_fwd_u(wd, X, A, B, r, scale, Y, U_out, T, N, K, f.uword, st);
-    }
+    if (f.uword != nullptr) return launch_gemm_fwd_u(wd, X, A, B, r, scale, Y, U_out, T, N, K, f.uword, st);
     const int rp = rank_pad64(r);
     const uint16_t* Bsrc = B;
     int64_t ld_b = r;

@@ -1,5 +1,5 @@
-// Counting the workgroups of a launch done, for launches that a HIP graph
-// may replay with the same token (gfx950).
+// Tags of the words one workgroup hands to another inside a launch, for
+// launches that a HIP graph may replay (gfx950).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,38 +8,35 @@
 namespace qlnf4 {
 
 // ---------------------------------------------------------------------------
-// A captured launch replays with its token and tag, so words it hands from
-// one workgroup to another must be cleared by its last workgroup before the
-// next replay. The kArriveWords counters of such a launch are zeroed by a
-// small fill kernel recorded right before it (in the launch's source file),
-// so each arrival is one fetch-and-add: workgroup i of `total` adds one to
-// counter i % kArriveSub, and the last arrival on that counter adds one to
-// the top counter (atomics on one word are served one after another, so one
-// counter for all would queue them). Called by one thread once the
-// workgroup's accesses to the words have completed (vmcnt); those, and what
-// the last arrival does next, are agent-scope atomics performed at the
-// device's coherence point, so relaxed ordering suffices. Returns true for
-// the last of all `total` arrivals. (A compare-and-swap count that needs no
-// zeroing, token-tagged, cost 24 us per decode call in a graph: its retries
-// queue.)
+// Words handed from one workgroup to another carry a tag of their launch, so
+// a reader can tell this launch's words from those an earlier launch left in
+// the workspace. An eager launch gets a fresh tag from the host. A captured
+// launch is replayed with the tag it was captured with, so its tag also
+// mixes in an epoch word of the workspace that a one-thread kernel recorded
+// just before the launch advances at every replay: every workgroup reads the
+// epoch (the advance completed before the launch started), and the words of
+// the previous replay carry the previous epoch's tag. Nothing is counted or
+// cleared. (Counting the workgroups done so that the last one clears the
+// words cost more: a token-tagged compare-and-swap count 24 us per decode
+// call, its retries queueing; zeroed counters with fetch-and-add, 1.3 us
+// more than this.)
 // ---------------------------------------------------------------------------
-constexpr int kArriveSub = 32;
-constexpr int kArriveWords = kArriveSub + 1;
 
-__device__ __forceinline__ bool count_arrival(uint64_t* counters, int i, int total) {
-    const int k = i % kArriveSub, groups = total < kArriveSub ? total : kArriveSub;
-    const int in_k = total / kArriveSub + (k < total % kArriveSub ? 1 : 0);  // arrivals on counter k
-    if (static_cast<int>(__hip_atomic_fetch_add(counters + k, uint64_t{1}, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)) + 1 != in_k)
-        return false;
-    return static_cast<int>(__hip_atomic_fetch_add(counters + kArriveSub, uint64_t{1}, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)) + 1 == groups;
+// The tag of a launch: its host tag alone, or mixed with the epoch (a
+// captured launch); never zero, so a cleared word never passes.
+__device__ __forceinline__ uint32_t launch_tag(uint32_t host_tag, const uint64_t* epoch) {
+    if (epoch == nullptr) return host_tag;
+    const uint64_t e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t h = (e + 1) * 0x9E3779B97F4A7C15ull ^ (uint64_t{host_tag} << 17);
+    h ^= h >> 29;
+    h *= 0xBF58476D1CE4E5B9ull;
+    h ^= h >> 32;
+    const uint32_t t = static_cast<uint32_t>(h);
+    return t != 0 ? t : 1u;
 }
 
-// Up to four blocks of kArriveWords counters (null: none), for the fill
-// kernel of a launch that serves several weights.
-struct CounterSet {
-    uint64_t* c[4];
-};
+// Records the one-thread kernel that advances `epoch` (before a captured
+// launch; defined with the decode GEMV).
+void launch_advance_epoch(uint64_t* epoch, hipStream_t stream);
 
 }  // namespace qlnf4

@@ -30,6 +30,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "arrive.h"
 #include "mm_common.h"
 #include "proj_dma.h"
 
@@ -61,6 +62,7 @@ struct TileArgs {
     int r_u;
     float s_u;
     int spin;  // word loads before the tile forms its tokens' U itself
+    const uint64_t* epoch;  // captured launch: the epoch word its tag mixes in (launch_tag), else null
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -166,7 +168,9 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                           NW * 256 * 4 <= S::ROWS_A * LDA * 2,
                       "the projection's LDS fits in the stages");
         if (static_cast<int>(blockIdx.x) < p.nu) {
-            proj_dma_block<1, false>(p.proj, static_cast<int>(blockIdx.x), 0, 1, proj_lds());
+            ProjArgs pj = p.proj;
+            pj.tag = launch_tag(p.proj.tag, p.epoch);
+            proj_dma_block<1, false>(pj, static_cast<int>(blockIdx.x), 0, 1, proj_lds());
             return;
         }
     }
@@ -410,6 +414,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         if constexpr (kUin) {
         constexpr int WPT = TT * 16 / NTHR;  // words a thread, at most
         const int lg = p.r_u == 16 ? 4 : 3;  // r_u is 8 or 16
+        const uint32_t tag = launch_tag(p.proj.tag, p.epoch);
         const int nw = TT << lg;
         auto stage_words = [&]() -> bool {
             bool ok = true;
@@ -423,7 +428,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                     if (t < p.T) {
                         wd = __hip_atomic_load(p.proj.uword + (t << lg) + j, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
-                        ok = ok && static_cast<uint32_t>(wd >> 32) == p.proj.tag;
+                        ok = ok && static_cast<uint32_t>(wd >> 32) == tag;
                     }
                     sX0[row * kStep + 8 * ((j >> 3) ^ swz(row)) + (j & 7)] =
                         to_bf16_bits(p.s_u * __uint_as_float(static_cast<uint32_t>(wd)));
@@ -713,7 +718,7 @@ bool gemm_fwd_u_in_launch(int64_t N, int64_t K, int64_t T, int r) {
     return pl.tile == 256 && pl.splits == 1 && lora_proj_splits(T, r, K, false) == 1;
 }
 
-size_t gemm_fwd_u_words(int64_t T, int r) { return static_cast<size_t>(T) * r; }
+size_t gemm_fwd_u_words(int64_t T, int r) { return static_cast<size_t>(T) * r + 1; }  // + the epoch word
 
 int launch_gemm_fwd_u(const NF4Dev& w, const uint16_t* X, const uint16_t* A, const uint16_t* B, int r, float scale,
                       uint16_t* Y, float* U_out, int64_t T, int64_t N, int64_t K, uint64_t* words, hipStream_t stream) {
@@ -748,11 +753,18 @@ int launch_gemm_fwd_u(const NF4Dev& w, const uint16_t* X, const uint16_t* A, con
     pj.uword = words;
     pj.token = next_token();
     // a fresh tag per launch, so words left in the workspace by earlier
-    // launches never pass for this one's (the caller runs captured launches,
-    // whose replays would reuse it, with the separate projection instead)
+    // launches never pass for this one's; a captured launch (replayed with
+    // this tag) also mixes in the epoch word after the words, which a kernel
+    // recorded before it advances at every replay
     pj.tag = static_cast<uint32_t>(pj.token % 0xFFFFFFFFull) + 1u;
     a.r_u = r;
     a.s_u = scale;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return set_error(QL_ERR_HIP, "dequant GEMM: capture query");
+    if (cs != hipStreamCaptureStatusNone) {
+        a.epoch = words + static_cast<size_t>(T) * r;
+        launch_advance_epoch(words + static_cast<size_t>(T) * r, stream);
+    }
     // QLORA_NF4_GEMM_SPIN=n: loads of the words before a tile forms U
     // itself (a negative n: at once, without reading the words)
     const char* e = std::getenv("QLORA_NF4_GEMM_SPIN");

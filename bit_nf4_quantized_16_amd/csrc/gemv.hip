@@ -49,10 +49,9 @@ namespace qlnf4 {
 // so the U workgroups never wait on anything; should the retries still run
 // out, the workgroup computes U itself from the same partial products in the
 // same order (bit-identical). A launch being captured into a graph (its
-// replays reuse the token) also counts its U and row workgroups done
-// (count_arrival, on counters a fill kernel recorded before it zeroes); the
-// last one clears the words, so a replay finds no word of the previous one.
-// An eager launch has a token of its own and skips the count.
+// replays reuse the tag) mixes into its tag an epoch word that a kernel
+// recorded before it advances at every replay (launch_tag), so a replay
+// never takes the previous one's words for its own.
 //
 // One launch can serve up to kGemvGroup layers that read the same x (q/k/v,
 // gate/up): the argument holds a descriptor per layer (weight, adapters,
@@ -64,12 +63,12 @@ namespace qlnf4 {
 // Lanes of tokens >= T read token T-1 and their outputs are dropped; rows
 // past N read row N-1 and are dropped.
 // ===========================================================================
-// The fill kernel recorded before a captured launch: its done counters at zero.
-__global__ void zero_counters_kernel(CounterSet s) {
-    const int i = threadIdx.x;
-    if (i < kArriveWords)
-        for (int j = 0; j < 4; ++j)
-            if (s.c[j] != nullptr) __hip_atomic_store(s.c[j] + i, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__global__ void advance_epoch_kernel(uint64_t* epoch) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(epoch, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+void launch_advance_epoch(uint64_t* epoch, hipStream_t stream) {
+    hipLaunchKernelGGL(advance_epoch_kernel, dim3(1), dim3(64), 0, stream, epoch);
 }
 
 constexpr int kGemvRows = 16;
@@ -80,7 +79,6 @@ constexpr int kGemvUSteps = 4;  // steps of x in one U workgroup's slice (waves 
 // x (the same K, T, rank and scale), each with its own U workgroups, row
 // workgroups, outputs and workspace.
 constexpr int kGemvGroup = kGemvMaxGroup;
-static_assert(kGemvGroup <= 4, "one fill kernel zeroes the counters of every weight of a launch");
 
 struct GemvWeight {
     NF4Dev w;
@@ -90,7 +88,7 @@ struct GemvWeight {
     uint16_t* Y;
     float* U_out;     // [T, r] fp32 = X A^T, or null
     uint64_t* uword;  // [nks][T][r]: slice ks of U, tag << 32 | fp32 bits (r > 0)
-    uint64_t* done;   // [kArriveWords]: counts of workgroups done with the words (captured launches, r > 0)
+
     int nu, nrow;     // its U and row workgroups
     int ub, rb;       // the grid index of its first U and first row workgroup
 };
@@ -103,7 +101,7 @@ struct GemvArgs {
     float scale;
     uint64_t token;   // 40 bits
     uint32_t tag;     // nonzero, from the token (a cleared word is 0)
-    int count_done;   // the launch is captured: count the workgroups done, the last clears the words
+    const uint64_t* epoch;  // captured launch: the epoch word its tag mixes in (launch_tag), else null
     int nks, rt;      // U workgroups of a weight = rt (16-row tiles of A) x nks (slices of kGemvUSteps steps)
     int spin;         // loads of the U words before computing U locally
     int ngroup;       // weights in this launch
@@ -156,7 +154,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     __shared__ uint4 xw[kGemvWaves][2 * TX * 32];
     __shared__ float sU[16 * QL_MAX_RANK];
     __shared__ uint16_t sB[kGemvRows * QL_MAX_RANK];
-    __shared__ int s_last;
     // this workgroup's weight (the U workgroups of all weights come first)
     const int bid = static_cast<int>(blockIdx.x);
     const bool is_u = bid < p.nu_all;
@@ -173,6 +170,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
     const int nbs = static_cast<int>((nblk + 3) / 4);
     const int tok = std::min(li, T - 1);
     const int pb = gemv_block_of(g);
+    const uint32_t tag = launch_tag(p.tag, p.epoch);
     uint4* const slot = xw[wave];
     auto red = [&](int ww) { return reinterpret_cast<float*>(xw[ww]); };
 
@@ -235,25 +233,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
         return v;
     };
 
-    // A captured launch (its replays reuse the token and tag) counts every
-    // workgroup of the weight that touches the U words: a U workgroup once its
-    // words are stored, a row workgroup once it has U (from the words or
-    // computed itself). The last of them clears the words, so a replay finds
-    // none of the previous replay's; as every U workgroup counts too, no word
-    // can be stored after the clear (count_arrival: two levels of counters,
-    // zeroed before the launch). The words are stored and loaded only as
-    // agent-scope atomics, and every thread's accesses complete (vmcnt) before
-    // the barrier and the count.
-    auto count_done_and_clear = [&](int i) {
-        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): this thread's word accesses are done
-        __syncthreads();
-        if (tid == 0) s_last = count_arrival(gw.done, i, gw.nu + gw.nrow);
-        __syncthreads();
-        if (s_last)
-            for (int e = tid; e < p.nks * T * r; e += 512)
-                __hip_atomic_store(gw.uword + e, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-
     if (is_u) {
         // a U workgroup: its slice of one 16-row tile of U^T, published
         const int local = bid - gw.ub;
@@ -265,10 +244,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
             const float v = sum_tile(tid);
             if (t < T && j < r)  // device scope: read on other XCDs
                 __hip_atomic_store(gw.uword + (static_cast<int64_t>(ks) * T + t) * r + j,
-                                   (uint64_t{p.tag} << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                                   (uint64_t{tag} << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (p.count_done) count_done_and_clear(local);
         return;
     }
 
@@ -392,7 +370,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
 #pragma unroll
                 for (int ks = 0; ks < kEarlyKs; ++ks)
                     if (ks < p.nks) {
-                        bad = bad || static_cast<uint32_t>(raw[ks] >> 32) != p.tag;
+                        bad = bad || static_cast<uint32_t>(raw[ks] >> 32) != tag;
                         v += __uint_as_float(static_cast<uint32_t>(raw[ks]));
                     }
             }
@@ -411,7 +389,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                     for (int ks = 0; ks < p.nks; ++ks) {
                         const uint64_t wd = __hip_atomic_load(gw.uword + static_cast<int64_t>(ks) * nur + e,
                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        bad = bad || static_cast<uint32_t>(wd >> 32) != p.tag;
+                        bad = bad || static_cast<uint32_t>(wd >> 32) != tag;
                         v += __uint_as_float(static_cast<uint32_t>(wd));
                     }
                 uv[q] = v;
@@ -442,10 +420,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(gemv_min_wa
                     }
                 }
         }
-        if (p.count_done)
-            count_done_and_clear(gw.nu + (bid - gw.rb));  // (its barriers also order sU)
-        else
-            __syncthreads();  // sU is complete
+        __syncthreads();  // sU is complete
         if (gw.U_out != nullptr && n0 == 0)
             for (int e = tid; e < nur; e += 512) gw.U_out[e] = sU[e];
     }
@@ -485,7 +460,7 @@ GemvUPlan gemv_u_plan(int64_t T, int64_t K, int r) {
 size_t gemv_ws_bytes(int64_t T, int64_t K, int r) {
     if (r <= 0) return 0;
     const GemvUPlan u = gemv_u_plan(T, K, r);
-    return (u.part_bytes + kArriveWords * sizeof(uint64_t) + 255) / 256 * 256;
+    return (u.part_bytes + sizeof(uint64_t) + 255) / 256 * 256;  // the words, then the epoch word
 }
 
 namespace {
@@ -532,7 +507,10 @@ int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t 
         g.tag = static_cast<uint32_t>(g.token % 0xFFFFFFFFull) + 1u;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return set_error(QL_ERR_HIP, "dequant GEMV: capture query");
-        g.count_done = cs != hipStreamCaptureStatusNone ? 1 : 0;
+        // a captured launch: the epoch word of weight 0's workspace slice
+        g.epoch = cs != hipStreamCaptureStatusNone
+                      ? reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + gemv_u_plan(T, K, r).part_bytes)
+                      : nullptr;
         g.rt = u.rt;
         g.nks = u.nks;
         nu = u.rt * u.nks;
@@ -556,7 +534,6 @@ int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t 
         if (r > 0) {
             char* wbase = static_cast<char*>(ws) + wsb * i;
             gw.uword = reinterpret_cast<uint64_t*>(wbase);
-            gw.done = reinterpret_cast<uint64_t*>(wbase + gemv_u_plan(T, K, r).part_bytes);
         }
         gw.nu = nu;
         gw.ub = nu * i;
@@ -566,13 +543,8 @@ int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t 
     }
     if (total >= (int64_t{1} << 31)) return set_error(QL_ERR_SHAPE, "dequant GEMV: grid too large");
     timer_begin(QL_KERNEL_GEMV, stream);
-    if (g.count_done) {
-        // the done counters start every replay at zero (a fill kernel, not a
-        // memset node: captured memsets are avoided on this platform)
-        CounterSet cs{};
-        for (int i = 0; i < nw; ++i) cs.c[i] = g.g[i].done;
-        hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, cs);
-    }
+    if (g.epoch != nullptr)  // every replay advances the epoch before the launch reads it
+        launch_advance_epoch(const_cast<uint64_t*>(g.epoch), stream);
     const dim3 grid(static_cast<uint32_t>(total));
     const int64_t nbs = ceil_div(K / 64, 4);
     const int ns = static_cast<int>(std::min<int64_t>(ceil_div(nbs, kGemvWaves), 1 << 20));

@@ -31,16 +31,23 @@
  *     Calls are re-entrant; calls that share output or workspace buffers on
  *     different streams race.
  *   - Workspace buffers need no initialisation and may hold anything between
- *     calls (the arrival counters and flags kept in them are tagged with a
- *     token that is new for every launch, and a launch leaves them clear).
+ *     calls (the arrival counters and handed-over words kept in them are
+ *     tagged with a token that is new for every launch, and a launch leaves
+ *     its counters clear).
  *   - Calls may be captured into a HIP graph and replayed: they issue only
- *     kernel launches (no memset or copy nodes, no host synchronisation), and
- *     a replayed launch reusing its token finds its counters and flags clear.
+ *     kernel launches (no memset or copy nodes, no host synchronisation). A
+ *     replayed launch reusing its token finds its counters clear, and the
+ *     launches that hand words between workgroups (the decode GEMV, the GEMM
+ *     forward with U inside its launch) record a one-thread kernel before
+ *     them that advances an epoch word in the workspace, which their tags mix
+ *     in, so a replay never takes the previous replay's words.
  *   - Some kernels hand partial results from one workgroup to another inside
  *     a launch (device-scope stores and loads). Where a workgroup waits for
  *     another, the wait is bounded; if it runs out, the workgroup computes
- *     the result itself in the same order (same bits). Such kernels rely on
- *     no other work writing their workspace during the launch.
+ *     the result itself (the decode GEMV in the same order, same bits; the
+ *     GEMM forward's tiles with plain fp32 sums, equal up to rounding). Such
+ *     kernels rely on no other work writing their workspace during the
+ *     launch.
  *   - Device pointers must be 16-byte aligned (QL_ERR_ALIGN otherwise).
  *   - All arguments are validated before anything is launched; on an error
  *     nothing is written. No C++ exception crosses this interface.
@@ -51,7 +58,9 @@
  *     (128 or 256) and QLORA_NF4_GEMM_SPLITS (split count of the 256 tile) for
  *     the T > 16 GEMMs, QLORA_NF4_PROJ_SPLITS for the rank-r projections, and
  *     QLORA_NF4_GEMV_SPIN (loads of the shared U before a decode workgroup
- *     computes U itself; 0 forces that path). Results stay within the stated
+ *     computes U itself; 0 forces that path), QLORA_NF4_GEMM_SPIN (the same
+ *     for a GEMM forward tile; -1 forces it) and QLORA_NF4_FWD_U=prepass (U
+ *     in a separate launch before the GEMM). Results stay within the stated
  *     tolerances under any of them.
  */
 #ifndef QLORA_NF4_H
@@ -252,17 +261,15 @@ int qlora_merge(const ql_nf4_weight* w, const uint16_t* A, const uint16_t* B, in
 size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);
 /*
  * qlora_linear_fwd_u_in_launch — 1 when qlora_linear_fwd (and _noalloc)
- * with these sizes, on a stream that is not being captured into a graph,
- * computes U = X A^T inside the dequant GEMM launch (its first workgroups,
- * one per 16 tokens, run on CUs the GEMM's tiles leave free and hand U to
- * the tiles through words tagged for the launch in the workspace), 0 when a
- * separate projection launch precedes the GEMM or T <= 16 (the decode GEMV
- * computes U inside its own launch). It applies to ranks 8 and 16 without
- * dropout when the GEMM runs unsplit 256 x 256 tiles and the projection is
- * unsplit; QLORA_NF4_FWD_U=prepass turns it off. A launch being captured
- * always takes the separate projection (its replays would reuse the tag).
- * Either way Y and U_out are the same bits (should a tile's bounded wait for
- * the words run out, it forms its U values itself: equal up to fp32
+ * with these sizes computes U = X A^T inside the dequant GEMM launch (its
+ * first workgroups, one per 16 tokens, run on CUs the GEMM's tiles leave
+ * free and hand U to the tiles through words tagged for the launch in the
+ * workspace), 0 when a separate projection launch precedes the GEMM or
+ * T <= 16 (the decode GEMV computes U inside its own launch). It applies to
+ * ranks 8 and 16 without dropout when the GEMM runs unsplit 256 x 256 tiles
+ * and the projection is unsplit; QLORA_NF4_FWD_U=prepass turns it off.
+ * Either way Y and U_out are the same bits (should a tile's bounded wait
+ * for the words run out, it forms its U values itself: equal up to fp32
  * rounding). No errors: invalid sizes give 0.
  */
 int qlora_linear_fwd_u_in_launch(int64_t rows, int64_t cols, int64_t T, int32_t r);

@@ -3,9 +3,9 @@ first workgroups hand U to the tiles through words tagged for the launch)
 against the forward with a separate projection launch first: Y and U bit
 for bit, the oracle within the usual bar, ragged token counts, and the
 tile's local fallback (forced from the host, so every kernel still ends
-normally). A captured forward takes the separate projection (a replay would
-reuse the launch's tag): its replays with new inputs equal the eager
-in-launch calls bit for bit."""
+normally). A captured forward (its tag mixes in an epoch word that a kernel
+recorded before it advances at every replay) replayed with new inputs
+equals the eager calls bit for bit, also when the tiles form U themselves."""
 
 import pytest
 import torch
@@ -96,8 +96,11 @@ def test_local_u_fallback(qn, monkeypatch, N, K, T, r):
     assert normwise_rel_err(bf16_to_np(Y1), H) <= TOL
 
 
-def test_captured_forward_replays_equal_eager_in_launch(qn, monkeypatch):
+@pytest.mark.parametrize("spin", [None, "-1"])
+def test_captured_forward_replays_equal_eager_in_launch(qn, monkeypatch, spin):
     monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    if spin is not None:
+        monkeypatch.setenv("QLORA_NF4_GEMM_SPIN", spin)
     N, K, T, r = 1024, 512, 300, 16
     W, case = _case(N, K, T, r, seed=77)
     w = qn.quantize_weight(W.cuda())

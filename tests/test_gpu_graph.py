@@ -118,12 +118,13 @@ def test_two_stream_graph_matches_serial(qn):
 @pytest.mark.parametrize("spin", [None, "1"])
 @pytest.mark.parametrize("T", [1, 16])
 def test_decode_graph_replays_with_new_inputs(qn, monkeypatch, T, spin):
-    """A captured decode call (the GEMV keeps token-tagged counters in its
-    workspace, and a replay reuses the token): replays with new x give the
-    eager results for that x. With QLORA_NF4_GEMV_SPIN=1 the row workgroups
-    give up waiting for the shared U almost at once and compute it
-    themselves, so their done counts and the U workgroups' stores race with
-    each other: the words must still be cleared after the last of them."""
+    """A captured decode call (the GEMV hands U over in tagged words in its
+    workspace, and a replay reuses the launch's tag, mixed with an epoch
+    word that a kernel recorded before the launch advances): replays with
+    new x give the eager results for that x. With QLORA_NF4_GEMV_SPIN=1 the
+    row workgroups give up waiting for the shared U almost at once and
+    compute it themselves, while the U workgroups' stores land late: no
+    replay may take those for its own."""
     if spin is not None:
         monkeypatch.setenv("QLORA_NF4_GEMV_SPIN", spin)
     N, K, r = 4096, 4096, 16
@@ -156,7 +157,7 @@ def test_decode_graph_replays_with_new_inputs(qn, monkeypatch, T, spin):
 @pytest.mark.parametrize("spin", [None, "1"])
 def test_grouped_decode_graph_replays_with_new_inputs(qn, monkeypatch, spin):
     """The grouped decode call captured once: each layer keeps its own tagged
-    counters in its slice of the workspace; every replay with a new x gives
+    words in its slice of the workspace; every replay with a new x gives
     the eager single-layer results (also when the row workgroups give up
     waiting for U almost at once)."""
     if spin is not None:
