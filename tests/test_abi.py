@@ -160,6 +160,28 @@ def test_backward_sizing_without_adapter_gradients(lib):
         assert s in (L.QL_OK, L.QL_ERR_HIP)
 
 
+def test_fwd_u_in_launch_query(lib, monkeypatch):
+    """Where the forward computes U inside its GEMM launch (host logic only:
+    without a GPU the plan assumes 256 CUs): the 172-tile 7B gate/up shapes
+    at T = 1024 with ranks 8 and 16; not the split-K down shape, other ranks,
+    decode sizes or invalid sizes; QLORA_NF4_FWD_U=prepass turns it off, and
+    the workspace then holds the projection's buffers instead of the words."""
+    assert lib.qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 16) == 1
+    assert lib.qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 8) == 1
+    assert lib.qlora_linear_fwd_u_in_launch(4096, 11008, 1024, 16) == 0  # reduction split 4 ways
+    assert lib.qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 64) == 0
+    assert lib.qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 5) == 0
+    assert lib.qlora_linear_fwd_u_in_launch(11008, 4096, 16, 16) == 0  # decode GEMV
+    for bad in ((0, 4096, 1024, 16), (11008, 0, 1024, 16), (11008, 4096, 0, 16), (11008, 4096, 1024, -1)):
+        assert lib.qlora_linear_fwd_u_in_launch(*bad) == 0
+    words = lib.qlora_linear_fwd_workspace(11008, 4096, 1024, 16)
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    assert lib.qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 16) == 0
+    prepass = lib.qlora_linear_fwd_workspace(11008, 4096, 1024, 16)
+    # words: 1024 x 16 x 8 B + the epoch word; prepass: bf16 s U padded to 64
+    assert words >= 1024 * 16 * 8 + 8 and prepass >= 1024 * 64 * 2 and words != prepass
+
+
 def test_linear_fwd_noalloc_rejects(lib):
     """The entry point without a workspace validates like qlora_linear_fwd and
     turns down, before touching the GPU, a call whose scratch need is larger
