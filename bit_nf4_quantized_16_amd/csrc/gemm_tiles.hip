@@ -25,7 +25,10 @@
 // The weight tile is row-major in both directions (a thread expands one
 // block, or half of one, with a single absmax); dX reads its A operand
 // through ds_read_b64_tr_b16, which hands each lane a column segment. The
-// LoRA term follows as rp/64 extra reduction steps over the rank.
+// LoRA term follows as rp/64 extra reduction steps over the rank. The
+// forward can also compute U = X A^T itself: its first workgroups then run
+// the rank-r projection (proj_dma.h) and hand U to the tiles in tagged
+// words (arrive.h), on CUs the tiles leave free.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
