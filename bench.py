@@ -205,15 +205,16 @@ def measured_traffic(kernel):
 def per_launch_work(qn, inp):
     """Algorithmic work of one launch of each kernel in the step, averaged
     over the step's launches of it (the per-kernel timers come from eager
-    steps: there U = X A^T runs inside the forward GEMM launch where the
-    library says so, else in a separate projection launch; G = s dY B always
-    runs outside the dX GEMM)."""
+    steps: there U = X A^T runs inside the forward GEMM launch, and
+    G = s dY B inside the dX GEMM launch, where the library says so, else in
+    a separate projection launch)."""
     fwd, dx = [], []
     for m in inp.mlp_dev:
         N, K, T, r = m["N"], m["K"], m["T"], m["r"]
         u_in = qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r)
+        g_in = qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r)
         fwd.append(fwd_flops(N, K, T, r) - (0 if u_in else 2 * T * K * r))
-        dx.append(dx_flops(N, K, T, r) - 2 * T * N * r)
+        dx.append(dx_flops(N, K, T, r) - (0 if g_in else 2 * T * N * r))
     return {
         "gemm_fwd": ("mfma", sum(fwd) / len(fwd), "TFLOP/s"),
         "gemm_dx": ("mfma", sum(dx) / len(dx), "TFLOP/s"),
@@ -296,7 +297,9 @@ def measure_rows(torch, qn, inp, flush):
     _, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
     sec = timed(6, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U,
                                               need_da=False, need_db=False))
-    rows["gemm_dx_T1024_11008x4096"] = _mfma_row(dx_flops(N, K, T, r) - 2 * T * N * r, sec, timed.last_min)
+    g_in = qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r)
+    rows["gemm_dx_T1024_11008x4096"] = dict(_mfma_row(dx_flops(N, K, T, r) - (0 if g_in else 2 * T * N * r), sec,
+                                                      timed.last_min), g_in_launch=bool(g_in))
     sec = timed(7, lambda: qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_dx=False))
     rows["lora_grad_T1024_11008x4096"] = _hbm_row(lora_grad_bytes(N, K, T, r), sec, timed.last_min)  # dA and dB
     # adapter merge of the same weight: codes and constants in, bf16 out, A and B read once

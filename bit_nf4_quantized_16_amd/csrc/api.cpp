@@ -184,6 +184,7 @@ struct BwdWs {
     float* gpart = nullptr;  // fp32 token-split partials of dA and dB
     void* proj = nullptr;    // split partials of the G (and U) projections, used in turn
     float* split = nullptr;  // fp32 split-K partials of the dX GEMM
+    uint64_t* gword = nullptr;  // dX GEMM with G inside its launch: G words and the epoch word
     size_t bytes = 0;
 };
 
@@ -195,7 +196,10 @@ BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_
         if (drop && (want_da || want_db)) b.Xd = c.take<uint16_t>(static_cast<size_t>(T) * K);
         const int rp = rank_pad64(r);
         const int rp16 = lora_grad_rp(r);
-        if (want_dx) b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+        if (want_dx && !drop && gemm_dx_g_in_launch(N, K, T, r))
+            b.gword = c.take<uint64_t>(gemm_fwd_u_words(T, r));  // G inside the dX GEMM launch
+        else if (want_dx)
+            b.Gp = c.take<uint16_t>(static_cast<size_t>(T) * rp);
         if (want_da) b.Gt = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
         if (want_db) b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
         const size_t gb = lora_grads_part_bytes(T, want_da ? K : 0, want_db ? N : 0, r);
@@ -328,6 +332,11 @@ size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t
 int qlora_linear_fwd_u_in_launch(int64_t rows, int64_t cols, int64_t T, int32_t r) {
     if (rows <= 0 || cols <= 0 || T <= kGemvMaxT || r < 0 || r > QL_MAX_RANK) return 0;
     return gemm_fwd_u_in_launch(rows, cols, T, r) ? 1 : 0;
+}
+
+int qlora_linear_bwd_g_in_launch(int64_t rows, int64_t cols, int64_t T, int32_t r) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    return gemm_dx_g_in_launch(rows, cols, T, r) ? 1 : 0;
 }
 
 size_t qlora_linear_fwd_dropout_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r) {
@@ -512,6 +521,7 @@ int linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, in
     const int rp = rank_pad64(r);
     const int rp16 = lora_grad_rp(r);
     const int64_t ldv = lora_vt_ld(T);
+    ProjArgs gproj{};
     if (r > 0 && (want_dx || want_da || (want_db && have_u))) {
         // G = s dY B (B read in its own layout): bf16 row-major padded to rp
         // for the dX epilogue, bf16 transposed for dA; U^T from U_saved for dB
@@ -537,7 +547,11 @@ int linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, in
             a.rows_ut = rp16;
             a.ld_ut = ldv;
         }
-        if ((s = launch_lora_proj(a, true, b.proj, st)) != QL_OK) return s;
+        if (b.gword != nullptr) {
+            gproj = a;  // run by the dX GEMM's first workgroups below
+        } else if ((s = launch_lora_proj(a, true, b.proj, st)) != QL_OK) {
+            return s;
+        }
     }
     // dropout: the adapter input X * keep, for dA and a recomputed U
     const bool need_xd = drop && r > 0 && (want_da || (want_db && !have_u));
@@ -562,7 +576,11 @@ int linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, in
     if (want_dx) {
         // with dropout the adapter term is masked per element: the GEMM takes
         // only dY W', a second kernel adds c (G A) * keep
-        if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, drop ? 0 : rp, dX, T, N, K, b.split, st)) != QL_OK) return s;
+        if (b.gword != nullptr) {
+            if ((s = launch_gemm_dx_g(wd, dY, A, r, dX, T, N, K, gproj, b.gword, st)) != QL_OK) return s;
+        } else if ((s = launch_gemm_dx(wd, dY, b.Gp, A, r, drop ? 0 : rp, dX, T, N, K, b.split, st)) != QL_OK) {
+            return s;
+        }
         if (drop && r > 0 && (s = launch_lora_dx_keep(b.Gp, rp, A, r, keep, c, T, K, dX, st)) != QL_OK) return s;
     }
     if (want_da || want_db) {

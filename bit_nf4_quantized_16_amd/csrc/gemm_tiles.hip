@@ -26,9 +26,10 @@
 // block, or half of one, with a single absmax); dX reads its A operand
 // through ds_read_b64_tr_b16, which hands each lane a column segment. The
 // LoRA term follows as rp/64 extra reduction steps over the rank. The
-// forward can also compute U = X A^T itself: its first workgroups then run
-// the rank-r projection (proj_dma.h) and hand U to the tiles in tagged
-// words (arrive.h), on CUs the tiles leave free.
+// launch can also compute that term's token operand itself (U = X A^T for the
+// forward, G = s dY B for dX): its first workgroups then run the rank-r
+// projection (proj_dma.h) and hand it to the tiles in tagged words
+// (arrive.h), on CUs the tiles leave free.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -55,11 +56,12 @@ struct TileArgs {
     int tiles_a, tiles_t;
     int splits;   // > 1: the reduction is split over gridDim.y workgroups
     float* part;  // split partial tiles, fp32 [splits, T, MA]
-    // Forward with U computed inside the launch (nu > 0; one reduction
-    // split, rank r_u <= 16 and a multiple of 8): workgroups [0, nu) run the
-    // projection U = X A^T of one 16-token block each (proj, unsplit) and
-    // store the raw sums as tagged words uword[t][j]; a tile reads its
-    // tokens' words before the rank step, in place of lt, as bf16(s_u v).
+    // The token-side rank operand computed inside the launch (nu > 0; one
+    // reduction split, rank r_u 8 or 16): workgroups [0, nu) run the
+    // projection of one 16-token block each (proj, unsplit; U = X A^T for
+    // the forward, G = s dY B for dX) and store its raw sums as tagged words
+    // uword[t][j]; a tile reads its tokens' words before the rank step, in
+    // place of lt, as bf16(s_u v).
     int nu;
     ProjArgs proj;
     int r_u;
@@ -153,9 +155,10 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     const int wa = wave / WT, wt = wave % WT;
     __shared__ int s_flag;
 
-    // ---- U inside the launch (forward, 256 x 256 tile): projection workgroups
-    // The projection's ring slots and partial sums live in the tile's stages.
-    constexpr bool kUin = !DX && TA == 256 && TT == 256 && NW == 8;
+    // ---- U (forward) or G (dX) inside the launch, 256 x 256 tile: projection
+    // workgroups. The projection's ring slots and partial sums live in the
+    // tile's stages; for dX the projection reads B's rows column-wise.
+    constexpr bool kUin = TA == 256 && TT == 256 && NW == 8;
     auto proj_lds = [&]() {
         using D = ProjDma<1>;
         return ProjLds<1>{{reinterpret_cast<uint16_t(*)[D::PS]>(sX0), reinterpret_cast<uint16_t(*)[D::PS]>(sX0 + D::PS * D::NW),
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         if (static_cast<int>(blockIdx.x) < p.nu) {
             ProjArgs pj = p.proj;
             pj.tag = launch_tag(p.proj.tag, p.epoch);
-            proj_dma_block<1, false>(pj, static_cast<int>(blockIdx.x), 0, 1, proj_lds());
+            proj_dma_block<1, DX>(pj, static_cast<int>(blockIdx.x), 0, 1, proj_lds());
             return;
         }
     }
@@ -403,14 +406,14 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     }
     }  // sb < se
 
-    // U inside the launch: the token operand of the rank step from the
-    // words of this tile's tokens (TT x r_u, at most 8 a thread), each
-    // converted as the separate projection converts it, bf16(s_u v), and
+    // U (forward) or G (dX) inside the launch: the token operand of the rank
+    // step from the words of this tile's tokens (TT x r_u, at most 8 a
+    // thread), each converted as the separate projection converts it, bf16(s_u v), and
     // stored straight into the stage (a retry overwrites it). While any tag
     // is not this launch's, the workgroup sleeps and loads again, at most
     // spin times. The projection workgroups come first in the grid and wait
     // on nothing, so that bound is a safety net only: should it run out, the
-    // tile forms its U values itself, each an fp32 sum of the products in k
+    // tile forms its values itself, each an fp32 sum of the products in k
     // order (plain fused multiply-adds, a few registers; the same values up
     // to rounding, not bit for bit). Ranks r_u .. 63 are zero.
     auto stage_u_words = [&]() {
@@ -462,15 +465,30 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                 float u = 0.0f;
                 if (t < p.T) {
                     const uint16_t* xr = p.proj.P + t * p.proj.ldp;
-                    const uint16_t* ar = p.proj.Q + j * p.proj.ldq;
+                    if constexpr (DX) {
+                        // G: column j of B [kred, ldq], one element a step
+                        const uint16_t* bc = p.proj.Q + j;
 #pragma unroll 1
-                    for (int64_t k = 0; k < p.proj.kred; k += 8) {
-                        const uint4 xv = ld16(xr + k), av = ld16(ar + k);
-                        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, aw[4] = {av.x, av.y, av.z, av.w};
+                        for (int64_t k = 0; k < p.proj.kred; k += 8) {
+                            const uint4 xv = ld16(xr + k);
+                            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            u = fmaf(bf16_to_f32(xw[q] & 0xFFFFu), bf16_to_f32(aw[q] & 0xFFFFu), u);
-                            u = fmaf(bf16_to_f32(xw[q] >> 16), bf16_to_f32(aw[q] >> 16), u);
+                            for (int q = 0; q < 4; ++q) {
+                                u = fmaf(bf16_to_f32(xw[q] & 0xFFFFu), bf16_to_f32(bc[(k + 2 * q) * p.proj.ldq]), u);
+                                u = fmaf(bf16_to_f32(xw[q] >> 16), bf16_to_f32(bc[(k + 2 * q + 1) * p.proj.ldq]), u);
+                            }
+                        }
+                    } else {
+                        const uint16_t* ar = p.proj.Q + j * p.proj.ldq;
+#pragma unroll 1
+                        for (int64_t k = 0; k < p.proj.kred; k += 8) {
+                            const uint4 xv = ld16(xr + k), av = ld16(ar + k);
+                            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                u = fmaf(bf16_to_f32(xw[q] & 0xFFFFu), bf16_to_f32(aw[q] & 0xFFFFu), u);
+                                u = fmaf(bf16_to_f32(xw[q] >> 16), bf16_to_f32(aw[q] >> 16), u);
+                            }
                         }
                     }
                 }
@@ -633,8 +651,8 @@ int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStr
     a.part = split_ws;
     if (a.splits > 1 && split_ws == nullptr) return set_error(QL_ERR_WORKSPACE, "%s: split workspace missing", what);
     a.nu = nu;
-    if (nu > 0 && (DX || tile != 256 || a.splits != 1))
-        return set_error(QL_ERR_UNSUPPORTED, "%s: U inside the launch needs the unsplit 256 tile", what);
+    if (nu > 0 && (tile != 256 || a.splits != 1))
+        return set_error(QL_ERR_UNSUPPORTED, "%s: the projection inside the launch needs the unsplit 256 tile", what);
     const dim3 grid(static_cast<uint32_t>(nu + static_cast<int64_t>(a.tiles_a) * a.tiles_t),
                     static_cast<uint32_t>(a.splits));
     timer_begin(kid, stream);
@@ -719,6 +737,49 @@ bool gemm_fwd_u_in_launch(int64_t N, int64_t K, int64_t T, int r) {
         if (std::strcmp(e, "prepass") == 0) return false;
     const GemmPlan pl = plan_gemm(N, T, K);
     return pl.tile == 256 && pl.splits == 1 && lora_proj_splits(T, r, K, false) == 1;
+}
+
+bool gemm_dx_g_in_launch(int64_t N, int64_t K, int64_t T, int r) {
+    if (r != 8 && r != 16) return false;
+    if (const char* e = std::getenv("QLORA_NF4_FWD_U"))
+        if (std::strcmp(e, "prepass") == 0) return false;
+    const GemmPlan pl = plan_gemm(K, T, N);
+    return pl.tile == 256 && pl.splits == 1 && lora_proj_splits(T, r, N, true) == 1;
+}
+
+int launch_gemm_dx_g(const NF4Dev& w, const uint16_t* dY, const uint16_t* A, int r, uint16_t* dX, int64_t T,
+                     int64_t N, int64_t K, const ProjArgs& g, uint64_t* words, hipStream_t stream) {
+    TileArgs a{};
+    a.w = w;
+    a.act = dY;
+    a.ld_act = N;
+    a.lt = nullptr;
+    a.la = A;
+    a.ld_la = K;
+    a.r_la = r;
+    a.rp = 64;
+    a.out = dX;
+    a.T = T;
+    a.N = N;
+    a.K = K;
+    // the projection workgroups: G = s dY B of one 16-token block each, the
+    // caller's layouts of it (G^T, U^T) and the raw sums as tagged words
+    a.proj = g;
+    a.proj.out_b = nullptr;
+    a.proj.uword = words;
+    a.proj.token = next_token();
+    a.proj.tag = static_cast<uint32_t>(a.proj.token % 0xFFFFFFFFull) + 1u;
+    a.r_u = r;
+    a.s_u = g.alpha_b;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return set_error(QL_ERR_HIP, "dequant GEMM: capture query");
+    if (cs != hipStreamCaptureStatusNone) {
+        a.epoch = words + static_cast<size_t>(T) * r;
+        launch_advance_epoch(words + static_cast<size_t>(T) * r, stream);
+    }
+    const char* e = std::getenv("QLORA_NF4_GEMM_SPIN");
+    a.spin = e ? std::atoi(e) : (1 << 14);
+    return launch_tiles<true>(a, nullptr, QL_KERNEL_GEMM_DX, "dequant GEMM dX", stream, static_cast<int>(ceil_div(T, 16)));
 }
 
 size_t gemm_fwd_u_words(int64_t T, int r) { return static_cast<size_t>(T) * r + 1; }  // + the epoch word

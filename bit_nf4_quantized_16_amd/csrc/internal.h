@@ -141,6 +141,15 @@ int launch_gemm_fwd(const NF4Dev& w, const uint16_t* X, const uint16_t* Us, cons
 // being captured into a graph take the separate projection.
 bool gemm_fwd_u_in_launch(int64_t N, int64_t K, int64_t T, int r);
 size_t gemm_fwd_u_words(int64_t T, int r);
+// The same for dX: G = s dY B computed by the dX GEMM launch's first
+// workgroups (rank 8 or 16, the dX plan's unsplit 256 tile, an unsplit
+// projection; QLORA_NF4_FWD_U=prepass turns it off); its workspace words are
+// gemm_fwd_u_words(T, r).
+bool gemm_dx_g_in_launch(int64_t N, int64_t K, int64_t T, int r);
+// dX = dY W' + G A with G from projection g (its G^T and U^T outputs as the
+// caller set them; out_b unused), one launch.
+int launch_gemm_dx_g(const NF4Dev& w, const uint16_t* dY, const uint16_t* A, int r, uint16_t* dX, int64_t T,
+                     int64_t N, int64_t K, const ProjArgs& g, uint64_t* words, hipStream_t stream);
 // Y = X W'^T + s (X A^T) B^T with U_out = X A^T (optional), one launch.
 int launch_gemm_fwd_u(const NF4Dev& w, const uint16_t* X, const uint16_t* A, const uint16_t* B, int r, float scale,
                       uint16_t* Y, float* U_out, int64_t T, int64_t N, int64_t K, uint64_t* words, hipStream_t stream);

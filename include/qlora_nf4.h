@@ -273,6 +273,17 @@ size_t qlora_linear_fwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t
  * rounding). No errors: invalid sizes give 0.
  */
 int qlora_linear_fwd_u_in_launch(int64_t rows, int64_t cols, int64_t T, int32_t r);
+/*
+ * qlora_linear_bwd_g_in_launch — 1 when qlora_linear_bwd with these sizes,
+ * asked for dX without dropout, computes G = s dY B inside the dX GEMM
+ * launch (its first workgroups, one per 16 tokens, also write G^T and U^T
+ * for the gradient kernel), 0 when a separate projection launch precedes
+ * the dX GEMM. The same conditions as qlora_linear_fwd_u_in_launch, for the
+ * dX GEMM's plan (output K, reduction N); QLORA_NF4_FWD_U=prepass turns it
+ * off. Either way dX, dA and dB are the same bits (unless a tile's bounded
+ * wait for the words runs out: then equal up to fp32 rounding). No errors.
+ */
+int qlora_linear_bwd_g_in_launch(int64_t rows, int64_t cols, int64_t T, int32_t r);
 int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint16_t* A,
                      const uint16_t* B, int32_t r, float scale, uint16_t* Y, float* U_out,
                      void* ws, size_t ws_bytes, void* stream);
@@ -361,8 +372,12 @@ int qlora_linear_fwd_dropout(const ql_nf4_weight* w, const uint16_t* X, int64_t 
  *               their current contents (gradient accumulation)
  *
  * Any of dX, dA, dB may be NULL to skip it. X is needed for dA and when
- * U_saved is NULL. K must be a multiple of 64 and N a multiple of 8. Outputs
- * must not alias inputs.
+ * U_saved is NULL. G runs in its own projection launch before the dX GEMM
+ * or, where qlora_linear_bwd_g_in_launch says so, inside the GEMM launch
+ * (also when the call is captured into a graph: the launch then records a
+ * one-thread kernel that advances an epoch word in the workspace, which the
+ * launch's tag mixes in). K must be a multiple of 64 and N a multiple of 8.
+ * Outputs must not alias inputs.
  * Errors: as qlora_linear_fwd.
  */
 size_t qlora_linear_bwd_workspace(int64_t rows, int64_t cols, int64_t T, int32_t r);

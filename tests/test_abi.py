@@ -182,6 +182,23 @@ def test_fwd_u_in_launch_query(lib, monkeypatch):
     assert words >= 1024 * 16 * 8 + 8 and prepass >= 1024 * 64 * 2 and words != prepass
 
 
+def test_bwd_g_in_launch_query(lib, monkeypatch):
+    """Where the backward computes G = s dY B inside its dX GEMM launch (host
+    logic, 256 CUs assumed): the 7B down shape at T = 1024 (172 unsplit dX
+    tiles over K = 11008), not gate/up (their dX reduction is split), other
+    ranks or invalid sizes; QLORA_NF4_FWD_U=prepass turns it off."""
+    assert lib.qlora_linear_bwd_g_in_launch(4096, 11008, 1024, 16) == 1
+    assert lib.qlora_linear_bwd_g_in_launch(4096, 11008, 1024, 8) == 1
+    assert lib.qlora_linear_bwd_g_in_launch(11008, 4096, 1024, 16) == 0
+    assert lib.qlora_linear_bwd_g_in_launch(4096, 11008, 1024, 32) == 0
+    for bad in ((0, 4096, 1024, 16), (4096, 0, 1024, 16), (4096, 11008, 0, 16), (4096, 11008, 1024, -1)):
+        assert lib.qlora_linear_bwd_g_in_launch(*bad) == 0
+    words = lib.qlora_linear_bwd_workspace(4096, 11008, 1024, 16)
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    assert lib.qlora_linear_bwd_g_in_launch(4096, 11008, 1024, 16) == 0
+    assert lib.qlora_linear_bwd_workspace(4096, 11008, 1024, 16) != words
+
+
 def test_linear_fwd_noalloc_rejects(lib):
     """The entry point without a workspace validates like qlora_linear_fwd and
     turns down, before touching the GPU, a call whose scratch need is larger

@@ -140,3 +140,116 @@ def test_in_launch_u_without_u_out(qn, monkeypatch):
     Y2, _ = qn.qlora_linear_fwd(w, X, A, B, case.scale, save_u=False)
     torch.cuda.synchronize()
     assert U1 is None and torch.equal(Y1, Y2)
+
+
+# (N, K, T, r) where the dX GEMM (output K, reduction N) runs unsplit 256
+# tiles with the tile forced: G = s dY B inside its launch
+BWD_SHAPES = [(512, 1024, 300, 16), (256, 520 // 8 * 64, 33, 8), (1024, 2048, 257, 16)]
+
+
+def _bwd(qn, w, case, U, **kw):
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    out = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, U=U, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("N,K,T,r", BWD_SHAPES)
+@pytest.mark.parametrize("with_u", [True, False])
+def test_in_launch_g_equals_prepass_and_oracle(qn, monkeypatch, N, K, T, r, with_u):
+    """dX, dA and dB with G computed by the dX GEMM's first workgroups (which
+    also write G^T and, from U_saved, U^T for the gradient kernel) equal
+    the separate projection's bit for bit, with U saved or recomputed, and
+    stay within the oracle's bar."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    W, case = _case(N, K, T, r, seed=7 * N + T)
+    assert qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) == 1
+    w = qn.quantize_weight(W.cuda())
+    _, U = _fwd(qn, w, case)
+    U = U if with_u else None
+    g1 = _bwd(qn, w, case, U)
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    assert qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) == 0
+    g2 = _bwd(qn, w, case, U)
+    for a, b, name in zip(g1, g2, ("dX", "dA", "dB")):
+        assert torch.equal(a, b), name
+    ref = oracle_weight(W.numpy())
+    dXo, dAo, dBo, _, _ = oracle.lora_backward(bf16_to_np(case.X), bf16_to_np(case.dY), ref["wd"],
+                                               bf16_to_np(case.A), bf16_to_np(case.B), case.scale)
+    assert normwise_rel_err(bf16_to_np(g1[0]), dXo) <= TOL
+    assert normwise_rel_err(f32_to_np(g1[1]), dAo) <= TOL
+    assert normwise_rel_err(f32_to_np(g1[2]), dBo) <= TOL
+
+
+def test_in_launch_g_dx_only_and_7b_down(qn, monkeypatch):
+    """The 7B down projection at T = 1024 (its dX GEMM has 172 tiles, the
+    default plan puts G inside): dX alone and all three gradients equal the
+    separate projection's bit for bit."""
+    N, K, T, r = 4096, 11008, 1024, 16
+    assert qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) == 1
+    W = workloads.normal_weight(N, K, 0.02, seed=15)
+    X = workloads.bf16_normal((T, K), 1.0, seed=16).cuda()
+    dY = workloads.bf16_normal((T, N), 1.0, seed=17).cuda()
+    A = workloads.bf16_normal((r, K), 1.0 / K, seed=18).cuda()
+    B = workloads.bf16_normal((N, r), 0.01, seed=19).cuda()
+    w = qn.quantize_weight(W.cuda())
+    _, U = qn.qlora_linear_fwd(w, X, A, B, 2.0)
+    a1 = qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U)
+    x1, _, _ = qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U, need_da=False, need_db=False)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    a2 = qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U)
+    torch.cuda.synchronize()
+    for a, b, name in zip(a1, a2, ("dX", "dA", "dB")):
+        assert torch.equal(a, b), name
+    assert torch.equal(x1, a2[0])
+
+
+def test_in_launch_g_local_fallback(qn, monkeypatch):
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    N, K, T, r = BWD_SHAPES[0]
+    W, case = _case(N, K, T, r, seed=99)
+    w = qn.quantize_weight(W.cuda())
+    _, U = _fwd(qn, w, case)
+    g2 = _bwd(qn, w, case, U)
+    monkeypatch.setenv("QLORA_NF4_GEMM_SPIN", "-1")
+    g1 = _bwd(qn, w, case, U)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])  # G^T and U^T come from the projection
+    assert normwise_rel_err(bf16_to_np(g1[0]), bf16_to_np(g2[0]).astype("float64")) <= 1e-2
+    ref = oracle_weight(W.numpy())
+    dXo, _, _, _, _ = oracle.lora_backward(bf16_to_np(case.X), bf16_to_np(case.dY), ref["wd"], bf16_to_np(case.A),
+                                           bf16_to_np(case.B), case.scale)
+    assert normwise_rel_err(bf16_to_np(g1[0]), dXo) <= TOL
+
+
+@pytest.mark.parametrize("spin", [None, "-1"])
+def test_captured_backward_replays_equal_eager_in_launch(qn, monkeypatch, spin):
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    if spin is not None:
+        monkeypatch.setenv("QLORA_NF4_GEMM_SPIN", spin)
+    N, K, T, r = BWD_SHAPES[0]
+    W, case = _case(N, K, T, r, seed=123)
+    w = qn.quantize_weight(W.cuda())
+    X, A, B = case.X.cuda(), case.A.cuda(), case.B.cuda()
+    _, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    dY = torch.empty(T, N, dtype=torch.bfloat16, device="cuda")
+    dys = [workloads.bf16_normal((T, N), 1.0, seed=130 + i).cuda() for i in range(4)]
+    dY.copy_(dys[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, U=U)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, U=U)
+    for rep in range(1, 7):
+        dY.copy_(dys[rep % 4])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = qn.qlora_linear_bwd(w, X, dys[rep % 4], A, B, case.scale, U=U)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), "replay %d differs from the eager call" % rep
