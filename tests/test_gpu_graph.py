@@ -60,9 +60,12 @@ def test_graph_replay_matches_eager(qn):
             assert torch.equal(a, b), "replay %d: output %d differs from the eager run" % (rep, i)
 
 
-def test_two_stream_graph_matches_serial(qn):
+@pytest.mark.parametrize("split_bwd", [False, True])
+def test_two_stream_graph_matches_serial(qn, split_bwd):
     # weights quantized on a second stream while the first runs the layer of
-    # the previous weight (event waits in between), captured and replayed
+    # the previous weight (event waits in between), captured and replayed;
+    # split_bwd: dX on the first stream, dA and dB by a second backward call
+    # on the other stream once the forward is done (the benchmark's step)
     Ws = [workloads.normal_weight(1024, 2048, 0.02, seed=40 + i).cuda() for i in range(3)]
     case = workloads.lora_case("streams", Ws[0].cpu(), 96, 16, 32.0, 1 / 2048, 0.05, seed=40)
     X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
@@ -92,7 +95,16 @@ def test_two_stream_graph_matches_serial(qn):
         for w, ev in zip(ws, evs):
             main.wait_event(ev)
             Y, U = qn.qlora_linear_fwd(w, X, A, B, s)
-            outs += [w.packed, Y, U, *qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U)]
+            if not split_bwd:
+                outs += [w.packed, Y, U, *qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U)]
+                continue
+            done = torch.cuda.Event()
+            done.record(main)
+            dX, _, _ = qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U, need_da=False, need_db=False)
+            side.wait_event(done)
+            with torch.cuda.stream(side):
+                _, dA, dB = qn.qlora_linear_bwd(w, X, dY, A, B, s, U=U, need_dx=False)
+            outs += [w.packed, Y, U, dX, dA, dB]
         main.wait_stream(side)
         return outs
 
