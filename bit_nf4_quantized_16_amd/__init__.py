@@ -141,12 +141,31 @@ def nf4_double_quant(absmax):
     return c8, scale, mean
 
 
+def nf4_quantize_dq(W):
+    """nf4_quantize and nf4_double_quant in one call (two launches where the
+    size allows). Returns (packed, absmax, c8, scale, mean)."""
+    assert W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    rows, cols = W.shape
+    dtype = {torch.float32: _lib.QL_F32, torch.bfloat16: _lib.QL_BF16}[W.dtype]
+    dev = W.device
+    n1 = lib.nf4_num_blocks(rows, cols, BLOCKSIZE)
+    packed = torch.empty(lib.nf4_packed_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    absmax = torch.empty(n1, dtype=torch.float32, device=dev)
+    c8 = torch.empty(n1, dtype=torch.uint8, device=dev)
+    scale = torch.empty(lib.nf4_dq_num_groups(n1, DQ_BLOCKSIZE), dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(lib.nf4_quantize_dq_workspace(rows, cols, dtype), dev)
+    _check(lib.nf4_quantize_dq(_ptr(W), dtype, rows, cols, BLOCKSIZE, _ptr(packed), _ptr(absmax), DQ_BLOCKSIZE,
+                               _ptr(c8), _ptr(scale), _ptr(mean), _ptr(ws), wsb, _stream()))
+    return packed, absmax, c8, scale, mean
+
+
 def quantize_weight(W, double_quant=True, keep_absmax=False):
-    """nf4_quantize (+ nf4_double_quant) into an NF4Weight."""
-    packed, absmax = nf4_quantize(W)
+    """nf4_quantize_dq (or nf4_quantize alone) into an NF4Weight."""
     if not double_quant:
+        packed, absmax = nf4_quantize(W)
         return NF4Weight(W.shape[0], W.shape[1], packed, absmax=absmax)
-    c8, scale, mean = nf4_double_quant(absmax)
+    packed, absmax, c8, scale, mean = nf4_quantize_dq(W)
     return NF4Weight(W.shape[0], W.shape[1], packed, absmax=absmax if keep_absmax else None, c8=c8, dq_scale=scale,
                      dq_mean=mean)
 

@@ -68,6 +68,8 @@ SIGNATURES = {
     "nf4_quantize": (_I, [_P, _I, _I64, _I64, _I32, _P, _P, _P]),
     "nf4_double_quant_workspace": (_SZ, [_I64]),
     "nf4_double_quant": (_I, [_P, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "nf4_quantize_dq_workspace": (_SZ, [_I64, _I64, _I]),
+    "nf4_quantize_dq": (_I, [_P, _I, _I64, _I64, _I32, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "nf4_dequantize": (_I, [_WP, _P, _I, _P]),
     "qlora_merge": (_I, [_WP, _P, _P, _I32, _F, _P, _P]),
     "q4_quant_error_workspace": (_SZ, [_I64, _I64, _I]),

@@ -275,6 +275,37 @@ int nf4_double_quant(const float* absmax, int64_t n1, int32_t dq_blocksize, uint
     return launch_double_quant(absmax, n1, c8, scale, mean, static_cast<double*>(ws), static_cast<hipStream_t>(stream));
 }
 
+size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols, int w_dtype) {
+    if (rows <= 0 || cols <= 0 || (w_dtype != QL_F32 && w_dtype != QL_BF16)) return 0;
+    return quantize_dq_workspace_bytes(w_dtype == QL_BF16, rows * cols);
+}
+
+int nf4_quantize_dq(const void* W, int w_dtype, int64_t rows, int64_t cols, int32_t blocksize, uint8_t* packed,
+                    float* absmax, int32_t dq_blocksize, uint8_t* c8, float* scale, float* mean, void* ws,
+                    size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (rows <= 0 || cols <= 0)
+        return set_error(QL_ERR_SHAPE, "shape %lld x %lld", (long long)rows, (long long)cols);
+    if (blocksize != QL_NF4_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "blocksize %d (only 64 is offered)", blocksize);
+    if (dq_blocksize != QL_DQ_BLOCKSIZE)
+        return set_error(QL_ERR_UNSUPPORTED, "dq_blocksize %d (only 256 is offered)", dq_blocksize);
+    if (w_dtype != QL_F32 && w_dtype != QL_BF16) return set_error(QL_ERR_UNSUPPORTED, "input dtype %d", w_dtype);
+    int s;
+    if ((s = check_ptr(W, "W")) != QL_OK) return s;
+    if ((s = check_ptr(packed, "packed")) != QL_OK) return s;
+    if ((s = check_ptr(absmax, "absmax")) != QL_OK) return s;
+    if ((s = check_ptr(c8, "c8")) != QL_OK) return s;
+    if ((s = check_ptr(scale, "scale")) != QL_OK) return s;
+    if ((s = check_ptr(mean, "mean")) != QL_OK) return s;
+    const size_t need = quantize_dq_workspace_bytes(w_dtype == QL_BF16, rows * cols);
+    if (ws == nullptr || ws_bytes < need)
+        return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    return launch_quantize_dq(W, w_dtype == QL_BF16, rows * cols, packed, absmax, c8, scale, mean, ws,
+                              static_cast<hipStream_t>(stream));
+}
+
 int nf4_dequantize(const ql_nf4_weight* w, void* out, int out_dtype, void* stream) {
     g_last_error[0] = '\0';
     int s;

@@ -21,6 +21,13 @@ struct NF4Dev {
 
 int launch_quantize(const void* W, bool bf16, int64_t n, uint8_t* packed, float* absmax, hipStream_t stream);
 size_t dq_workspace_bytes(int64_t n1);
+// Quantize and double quant in two launches: the quantize launch also forms
+// one node of the constants' mean tree per workgroup (whole 512- /
+// 256-element segments and at most 4096 nodes; otherwise the three-launch
+// path), the encoder adds them.
+size_t quantize_dq_workspace_bytes(bool bf16, int64_t n);
+int launch_quantize_dq(const void* W, bool bf16, int64_t n, uint8_t* packed, float* absmax, uint8_t* c8,
+                       float* scale, float* mean, void* ws, hipStream_t stream);
 int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* scale, float* mean, double* ws,
                         hipStream_t stream);
 int launch_dequantize(const ql_nf4_weight& w, void* out, bool bf16_out, hipStream_t stream);

@@ -52,10 +52,28 @@ constexpr int kQuantThreads = 256;
 constexpr int kSegsPerWave = 4;
 constexpr int kSegBytes = 1024;
 
-template <bool BF16>
+// The first level of the double quantization's mean, folded into the
+// quantize launch: each workgroup adds its aligned blocks' absmax values as
+// one node of the fp64 pairwise tree and stores it in part[workgroup]
+// (the last of its waves to finish, counted in LDS, adds the wave sums: no
+// barrier holds the other waves); the encoder launch adds the nodes.
+// Only up to 4096 nodes (16.8 M fp32 or 33.6 M bf16 weights): every encoder
+// workgroup reads all nodes, and 11008 of them took the encoder from 12 to
+// 24 us at 11008 x 4096; 16-wave workgroups (a quarter of the nodes) made
+// the quantize kernel 12 % slower, more than the launch saved. Counting
+// arrivals to let the last workgroup of a chunk add its nodes inside this
+// launch measured far slower too: up to 64 workgroups updating one
+// device-scope counter serialize on it.
+
+struct QFold {
+    double* part;
+};
+
+template <bool BF16, bool FOLD>
 __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t* __restrict__ W, int64_t nseg,
                                                                    uint8_t* __restrict__ packed,
-                                                                   float* __restrict__ absmax) {
+                                                                   float* __restrict__ absmax, QFold fold) {
+    constexpr int kThreads = kQuantThreads;
     constexpr int kPerLane = BF16 ? 8 : 4;           // elements per lane per segment
     constexpr int kLanesPerBlock = 64 / kPerLane;    // 8 or 16
     constexpr int kBlocksPerSeg = 64 / kLanesPerBlock;  // 8 or 4
@@ -63,14 +81,19 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t
     static_assert(kSegsPerWave == 4, "one quad of lanes per block row serves four segments");
 
     __shared__ LutEntry lut[kLutBuckets];
+    __shared__ int s_done;  // waves that have stored their sum (the fold)
     if (threadIdx.x < kLutBuckets) lut[threadIdx.x] = c_lut[threadIdx.x];
+    if (FOLD && threadIdx.x == 0) s_done = 0;
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6);
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
     const int64_t seg0 = wave * kSegsPerWave;
-    if (seg0 >= nseg) return;
-    const int nsegs = static_cast<int>(nseg - seg0 < kSegsPerWave ? nseg - seg0 : kSegsPerWave);  // wave-uniform
+    uint32_t mb[kSegsPerWave] = {0u, 0u, 0u, 0u};  // block absmax, as bits
+    int nsegs = 0;  // wave-uniform
+    // with the fold every wave reaches the workgroup's reduction below
+    if (seg0 < nseg) {
+    nsegs = static_cast<int>(nseg - seg0 < kSegsPerWave ? nseg - seg0 : kSegsPerWave);
 
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 v[kSegsPerWave];
@@ -86,7 +109,6 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t
     }
 
     float e[kSegsPerWave][kPerLane];
-    uint32_t mb[kSegsPerWave];  // block absmax, as bits
 #pragma unroll
     for (int s = 0; s < kSegsPerWave; ++s) {
         if (BF16) {
@@ -142,6 +164,44 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_main(const uint8_t
     const int row = lane / kLanesPerBlock;
     if ((lane % kLanesPerBlock) < 4 && sel < nsegs)
         absmax[seg0 * kBlocksPerSeg + sel * kBlocksPerSeg + row] = mf;
+    } else if (!FOLD) {
+        return;
+    }
+    if constexpr (FOLD) {
+        // The wave's blocks are [16 wave, 16 wave + 16) (fp32) or 32 (bf16),
+        // block s * kBlocksPerSeg + row of the wave in lane row `row` of
+        // segment s, every lane of a row holding it. Blocks past the end
+        // count as zero, as in the tree's zero padding. Rows pair up by xor
+        // butterflies (both partners form the same sum), then the segments
+        // as (0 + 1) + (2 + 3), then the waves the same way: a subtree of
+        // the contiguous pairwise tree.
+        double x[kSegsPerWave];
+#pragma unroll
+        for (int s = 0; s < kSegsPerWave; ++s) {
+            x[s] = s < nsegs ? static_cast<double>(__uint_as_float(mb[s])) : 0.0;
+#pragma unroll
+            for (int d = kLanesPerBlock; d < 64; d <<= 1) x[s] = x[s] + __shfl_xor(x[s], d, 64);
+        }
+        const double wsum = (x[0] + x[1]) + (x[2] + x[3]);
+        constexpr int kWaves = kThreads / 64;
+        __shared__ double s_wave[kWaves];
+        if (lane == 0) {
+            s_wave[threadIdx.x >> 6] = wsum;
+            // release orders the sum before the count, acquire the other
+            // waves' sums before the last wave's reads (LDS, workgroup scope)
+            const int arrived = __hip_atomic_fetch_add(&s_done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) + 1;
+            if (arrived == kWaves) {
+                double v[kWaves];
+#pragma unroll
+                for (int i = 0; i < kWaves; ++i) v[i] = s_wave[i];
+#pragma unroll
+                for (int w = kWaves / 2; w >= 1; w >>= 1)
+#pragma unroll
+                    for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+                fold.part[blockIdx.x] = v[0];
+            }
+        }
+    }
 }
 
 // Tail: the elements after the last whole segment (fewer than 512), one
@@ -181,11 +241,11 @@ int launch_quantize(const void* W, bool bf16, int64_t n, uint8_t* packed, float*
         const int64_t waves = ceil_div(nseg, kSegsPerWave);
         const int64_t grid = ceil_div(waves, kQuantThreads / 64);
         if (bf16)
-            hipLaunchKernelGGL(nf4_quantize_main<true>, dim3(static_cast<uint32_t>(grid)), dim3(kQuantThreads), 0,
-                               stream, wb, nseg, packed, absmax);
+            hipLaunchKernelGGL((nf4_quantize_main<true, false>), dim3(static_cast<uint32_t>(grid)),
+                               dim3(kQuantThreads), 0, stream, wb, nseg, packed, absmax, QFold{});
         else
-            hipLaunchKernelGGL(nf4_quantize_main<false>, dim3(static_cast<uint32_t>(grid)), dim3(kQuantThreads), 0,
-                               stream, wb, nseg, packed, absmax);
+            hipLaunchKernelGGL((nf4_quantize_main<false, false>), dim3(static_cast<uint32_t>(grid)),
+                               dim3(kQuantThreads), 0, stream, wb, nseg, packed, absmax, QFold{});
     }
     timer_end(QL_KERNEL_QUANTIZE, stream);
     const int64_t start = nseg * seg_elems;
@@ -251,9 +311,10 @@ __global__ __launch_bounds__(kTreeThreads) void dq_tree_level(const void* __rest
 }
 
 // Symmetric E4M3FN code of (a - mean) per group of 256 constants; one wave
-// per group, four groups per workgroup. With `partials` (at most 4096 chunk
-// sums of the tree), every workgroup first adds them up itself, in the tree's
-// order, instead of a separate launch doing it; workgroup 0 stores the mean.
+// per group, four waves per workgroup, groups strided over the grid. With
+// `partials` (at most 4096 sums of aligned subtrees of the tree), every
+// workgroup first adds them up itself, in the tree's order, instead of a
+// separate launch doing it; workgroup 0 stores the mean.
 __global__ __launch_bounds__(256) void dq_encode(const float* __restrict__ absmax, int64_t n1,
                                                  const float* __restrict__ mean_p, const double* __restrict__ partials,
                                                  int64_t npart, float* __restrict__ mean_out,
@@ -267,38 +328,40 @@ __global__ __launch_bounds__(256) void dq_encode(const float* __restrict__ absma
         mu = *mean_p;
     }
     const int lane = threadIdx.x & 63;
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (g * QL_DQ_BLOCKSIZE >= n1) return;
-    const int64_t i0 = g * QL_DQ_BLOCKSIZE + lane * 4;
-    float d[4];
-    bool valid[4];
-    if (i0 + 3 < n1) {
-        float4 a = *reinterpret_cast<const float4*>(absmax + i0);
-        d[0] = a.x - mu; d[1] = a.y - mu; d[2] = a.z - mu; d[3] = a.w - mu;
-        valid[0] = valid[1] = valid[2] = valid[3] = true;
-    } else {
+    const int64_t groups = ceil_div(n1, static_cast<int64_t>(QL_DQ_BLOCKSIZE));
+    for (int64_t g = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); g < groups;
+         g += static_cast<int64_t>(gridDim.x) * 4) {  // wave-uniform
+        const int64_t i0 = g * QL_DQ_BLOCKSIZE + lane * 4;
+        float d[4];
+        bool valid[4];
+        if (i0 + 3 < n1) {
+            float4 a = *reinterpret_cast<const float4*>(absmax + i0);
+            d[0] = a.x - mu; d[1] = a.y - mu; d[2] = a.z - mu; d[3] = a.w - mu;
+            valid[0] = valid[1] = valid[2] = valid[3] = true;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            valid[i] = (i0 + i) < n1;
-            d[i] = valid[i] ? absmax[i0 + i] - mu : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                valid[i] = (i0 + i) < n1;
+                d[i] = valid[i] ? absmax[i0 + i] - mu : 0.0f;
+            }
         }
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, valid[i] ? fabsf(d[i]) : 0.0f);
+        m = wave_max(m);
+        const float S = m / 448.0f;
+        uint32_t code[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) code[i] = (S > 0.0f) ? e4m3_encode_rne(d[i] / S) : 0u;
+        if (i0 + 3 < n1) {
+            *reinterpret_cast<uint32_t*>(c8 + i0) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (valid[i]) c8[i0 + i] = static_cast<uint8_t>(code[i]);
+        }
+        if (lane == 0) scale[g] = S;
     }
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, valid[i] ? fabsf(d[i]) : 0.0f);
-    m = wave_max(m);
-    const float S = m / 448.0f;
-    uint32_t code[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) code[i] = (S > 0.0f) ? e4m3_encode_rne(d[i] / S) : 0u;
-    if (i0 + 3 < n1) {
-        *reinterpret_cast<uint32_t*>(c8 + i0) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (valid[i]) c8[i0 + i] = static_cast<uint8_t>(code[i]);
-    }
-    if (lane == 0) scale[g] = S;
 }
 
 size_t dq_workspace_bytes(int64_t n1) {
@@ -320,6 +383,7 @@ int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* sca
     bool f32 = true;
     double* out = ws;
     const double* last = nullptr;  // partials the encoder reduces, or none (mean already stored)
+    timer_begin(QL_KERNEL_DQ_ENCODE, stream);  // the whole double quantization: tree levels and encoder
     while (true) {
         const int64_t grid = ceil_div(count, kTreeChunk);
         float* mean_out = (grid == 1) ? mean : nullptr;
@@ -341,11 +405,68 @@ int launch_double_quant(const float* absmax, int64_t n1, uint8_t* c8, float* sca
         out += grid;
     }
     const int64_t groups = ceil_div(n1, QL_DQ_BLOCKSIZE);
-    timer_begin(QL_KERNEL_DQ_ENCODE, stream);
     hipLaunchKernelGGL(dq_encode, dim3(static_cast<uint32_t>(ceil_div(groups, 4))), dim3(256), 0, stream, absmax, n1,
                        mean, last, last ? count : 0, mean, c8, scale);
     timer_end(QL_KERNEL_DQ_ENCODE, stream);
     return check_launch("nf4_double_quant");
+}
+
+namespace {
+
+// Whether quantize + double quant can fold the tree's first level into the
+// quantize launch: whole segments only (no tail launch) and at most 4096
+// workgroup nodes, which every encoder workgroup adds itself.
+struct FoldPlan {
+    bool ok;
+    int64_t nseg, nwg;
+};
+
+FoldPlan fold_plan(bool bf16, int64_t n) {
+    const int per_lane = bf16 ? 8 : 4;
+    const int64_t seg_elems = 64 * per_lane;
+    FoldPlan f{};
+    f.nseg = n / seg_elems;
+    f.nwg = ceil_div(ceil_div(f.nseg, kSegsPerWave), kQuantThreads / 64);
+    f.ok = f.nseg > 0 && n % seg_elems == 0 && f.nwg <= kTreeChunk;
+    return f;
+}
+
+}  // namespace
+
+size_t quantize_dq_workspace_bytes(bool bf16, int64_t n) {
+    const FoldPlan f = fold_plan(bf16, n);
+    if (!f.ok) return dq_workspace_bytes(ceil_div(n, 64));
+    return static_cast<size_t>(f.nwg) * sizeof(double);
+}
+
+int launch_quantize_dq(const void* W, bool bf16, int64_t n, uint8_t* packed, float* absmax, uint8_t* c8,
+                       float* scale, float* mean, void* ws, hipStream_t stream) {
+    const FoldPlan f = fold_plan(bf16, n);
+    const int64_t n1 = ceil_div(n, 64);
+    if (!f.ok) {
+        int s = launch_quantize(W, bf16, n, packed, absmax, stream);
+        if (s != QL_OK) return s;
+        return launch_double_quant(absmax, n1, c8, scale, mean, static_cast<double*>(ws), stream);
+    }
+    QFold q;
+    q.part = static_cast<double*>(ws);
+    const uint8_t* wb = static_cast<const uint8_t*>(W);
+    timer_begin(QL_KERNEL_QUANTIZE, stream);
+    const dim3 grid_q(static_cast<uint32_t>(f.nwg));
+    if (bf16)
+        hipLaunchKernelGGL((nf4_quantize_main<true, true>), grid_q, dim3(kQuantThreads), 0, stream, wb, f.nseg,
+                           packed, absmax, q);
+    else
+        hipLaunchKernelGGL((nf4_quantize_main<false, true>), grid_q, dim3(kQuantThreads), 0, stream, wb, f.nseg,
+                           packed, absmax, q);
+    timer_end(QL_KERNEL_QUANTIZE, stream);
+    const int64_t groups = ceil_div(n1, QL_DQ_BLOCKSIZE);
+    const int64_t grid = ceil_div(groups, 4);
+    timer_begin(QL_KERNEL_DQ_ENCODE, stream);
+    hipLaunchKernelGGL(dq_encode, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, absmax, n1, mean, q.part,
+                       f.nwg, mean, c8, scale);
+    timer_end(QL_KERNEL_DQ_ENCODE, stream);
+    return check_launch("nf4_quantize_dq");
 }
 
 }  // namespace qlnf4

@@ -174,6 +174,27 @@ int nf4_double_quant(const float* absmax, int64_t n1, int32_t dq_blocksize, uint
                      float* scale, float* mean, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nf4_quantize_dq — nf4_quantize followed by nf4_double_quant of its
+ * constants ([tqpw] NF4 and "Double Quantization"), in one call: the same
+ * packed, absmax, c8, scale and mean bit for bit, arguments as the two calls.
+ * When rows x cols is a multiple of 256 (fp32 input) or 512 (bf16) and at
+ * most 2^24 (fp32) or 2^25 (bf16), it takes two launches instead of three:
+ * the quantize launch also adds each workgroup's 64 (fp32) or 128 (bf16)
+ * constants as one node of the mean's pairwise tree, stored in the
+ * workspace, and the encoder adds the (at most 4096) nodes before it
+ * encodes; the separate tree-level launch is gone. Other sizes run the two
+ * calls' kernels.
+ *   ws   workspace of nf4_quantize_dq_workspace(rows, cols, w_dtype) bytes
+ *        (0 for invalid arguments); two calls that overlap in time must not
+ *        share one.
+ * Errors: those of the two calls.
+ */
+size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols, int w_dtype);
+int nf4_quantize_dq(const void* W, int w_dtype, int64_t rows, int64_t cols, int32_t blocksize,
+                    uint8_t* packed, float* absmax, int32_t dq_blocksize, uint8_t* c8, float* scale,
+                    float* mean, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * nf4_dequantize — expand the quantized weight to the compute dtype ([apxml]:
  * the 4-bit weight is temporarily dequantized to bfloat16 for the matmul).
  *

@@ -107,6 +107,38 @@ def _weight(L, rows=256, cols=256, dq=256, **over):
     return ctypes.byref(w)
 
 
+def test_quantize_dq_rejects_and_sizes(lib):
+    """nf4_quantize_dq validates like the two calls it replaces; its
+    workspace holds one fp64 tree node per quantize workgroup when the size
+    allows the fold, else the double quantization's tree levels."""
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    need = lib.nf4_quantize_dq_workspace(64, 4096, L.QL_F32)
+    # 262144 fp32 elements: 4096 constants, 64 workgroups of 64 constants
+    assert need == 64 * 8
+    assert lib.nf4_quantize_dq_workspace(64, 4096, L.QL_BF16) == 32 * 8
+    # more than 16384 nodes: the three-launch path
+    assert lib.nf4_quantize_dq_workspace(16384, 65536 + 256, L.QL_F32) == lib.nf4_double_quant_workspace(
+        16384 * (65536 + 256) // 64)
+    # a tail (n % 256 != 0) takes the three-launch path and its workspace
+    assert lib.nf4_quantize_dq_workspace(3, 100, L.QL_F32) == lib.nf4_double_quant_workspace(5)
+    assert lib.nf4_quantize_dq_workspace(0, 64, L.QL_F32) == 0
+    assert lib.nf4_quantize_dq_workspace(64, 64, 7) == 0
+
+    def call(W=P, dt=L.QL_F32, rows=64, cols=4096, bs=64, dqbs=256, c8=P2, ws=P3, wsb=need):
+        return lib.nf4_quantize_dq(W, dt, rows, cols, bs, P, P2, dqbs, c8, P3, P, ws, wsb, None)
+
+    assert call(W=None) == L.QL_ERR_NULL
+    assert call(rows=0) == L.QL_ERR_SHAPE
+    assert call(bs=128) == L.QL_ERR_UNSUPPORTED
+    assert call(dqbs=64) == L.QL_ERR_UNSUPPORTED
+    assert call(dt=9) == L.QL_ERR_UNSUPPORTED
+    assert call(c8=None) == L.QL_ERR_NULL
+    assert call(wsb=need - 1) == L.QL_ERR_WORKSPACE
+    assert call(ws=None) == L.QL_ERR_WORKSPACE
+    assert call(W=MIS) == L.QL_ERR_ALIGN
+
+
 def test_dequantize_rejects(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 

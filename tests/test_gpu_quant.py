@@ -223,3 +223,64 @@ def test_storage_path_attn_7b_full(qn):
     assert f32_to_np(w.dq_mean)[0].view(np.uint32) == np.float32(ref["mean"]).view(np.uint32)
     assert np.array_equal(bf16_bits_np(qn.nf4_dequantize(w)), ref["wd_bits"])
     assert np.all(ref["a_eff"] > 0)
+
+
+# (rows, cols): whole 256/512-element segments, one node (64 fp32 or 128
+# bf16 constants per quantize workgroup) to 4096 of them (4096 x 4096 fp32;
+# 8192 x 4096 bf16), partial last workgroups, sizes past the limit (the 7B
+# MLP shapes, 4112 x 4096 fp32) and with a tail (the three-launch path)
+QDQ_SHAPES = [(4, 64), (8, 64), (40, 192), (64, 4096), (65, 4096), (1000, 1024), (4096, 4096), (8192, 4096),
+              (4112, 4096), (11008, 4096), (4096, 11008), (3, 100), (513, 77)]
+
+
+@pytest.mark.parametrize("shape", QDQ_SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_dq_equals_the_two_calls(qn, shape, dtype):
+    """nf4_quantize_dq (the quantize launch also forming the nodes of the
+    constants' mean tree) gives the two separate calls' outputs bit for bit."""
+    W = workloads.normal_weight(*shape, 0.02, seed=shape[0] * 7 + shape[1]).to(dtype).contiguous().cuda()
+    p1, a1, c1, s1, m1 = qn.nf4_quantize_dq(W)
+    p2, a2 = qn.nf4_quantize(W)
+    c2, s2, m2 = qn.nf4_double_quant(a2)
+    torch.cuda.synchronize()
+    for x, y, name in zip((p1, a1, c1, s1, m1), (p2, a2, c2, s2, m2), ("packed", "absmax", "c8", "scale", "mean")):
+        assert torch.equal(x, y), name
+
+
+def test_quantize_dq_mean_matches_oracle(qn):
+    """The mean formed through the quantize launch's tree nodes equals the
+    oracle's pairwise tree mean (250 nodes, the last one partial)."""
+    W = workloads.normal_weight(1000, 1024, 0.02, seed=3)
+    _, a, _, _, m = qn.nf4_quantize_dq(W.cuda())
+    torch.cuda.synchronize()
+    an = f32_to_np(a)
+    m_ref = np.float32(oracle.pairwise_tree_sum(an) / np.float64(an.size))
+    assert f32_to_np(m)[0].view(np.uint32) == m_ref.view(np.uint32)
+    _, a_ref = oracle.quantize(W.numpy())
+    assert np.array_equal(an.view(np.uint32), a_ref.view(np.uint32))
+
+
+def test_quantize_dq_graph_replays_with_new_weights(qn):
+    """A captured quantize + double quant replayed with new weights in the
+    same buffer equals the eager call for those weights on every replay."""
+    Ws = [workloads.normal_weight(1000, 1024, 0.02 * (i + 1), seed=60 + i).cuda() for i in range(4)]
+    W = Ws[0].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qn.nf4_quantize_dq(W)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = qn.nf4_quantize_dq(W)
+    for rep in range(1, 7):
+        W.copy_(Ws[rep % 4])
+        qn.nf4_quantize_dq(Ws[(rep + 1) % 4])  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = qn.nf4_quantize_dq(Ws[rep % 4])
+        torch.cuda.synchronize()
+        for x, y in zip(out, ref):
+            assert torch.equal(x, y), "replay %d" % rep
