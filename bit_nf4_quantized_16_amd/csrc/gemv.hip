@@ -55,7 +55,7 @@ namespace qlnf4 {
 //
 // One launch can serve up to kGemvGroup layers that read the same x (q/k/v,
 // gate/up): the argument holds a descriptor per layer (weight, adapters,
-// outputs, its own workspace slice of words and counters), the grid puts all
+// outputs, its own workspace slice of tagged words and its epoch word), the grid puts all
 // layers' U workgroups first and then all their row workgroups, and each
 // workgroup finds its layer from its index. Per layer the arithmetic and its
 // order are those of a launch for that layer alone.

@@ -56,7 +56,7 @@ def test_size_helpers(lib):
     assert lib.nf4_dq_num_groups(257, 256) == 2
     assert lib.nf4_double_quant_workspace(1024) >= 8
     assert lib.qlora_linear_fwd_workspace(4096, 4096, 1024, 16) > 0
-    # decode (T <= 16): U's tagged partials and the done counters when r > 0
+    # decode (T <= 16): U's tagged words and the epoch word when r > 0
     assert lib.qlora_linear_fwd_workspace(4096, 4096, 1, 0) == 0
     assert lib.qlora_linear_fwd_workspace(4096, 4096, 16, 16) >= 16 * 16 * 8 * 4
     assert lib.qlora_linear_bwd_workspace(4096, 4096, 1024, 16) > 0

@@ -30,7 +30,7 @@ def _case(qn, N, K, T, r, seed):
 
 # (first call, second smaller call): N, K, T, r
 PAIRS = [
-    # decode GEMV: U's tagged words and the done counters live in the scratch
+    # decode GEMV: U's tagged words and the epoch word live in the scratch
     ((4096, 4096, 16, 16), (1024, 4096, 1, 8)),
     ((11008, 4096, 5, 64), (264, 1088, 3, 5)),
     # GEMM: bf16 s U staging, the projection's split partials and, for the
