@@ -1022,7 +1022,7 @@ def compare_fwd_u(torch, qn):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (--gpus 1); no multi-GPU path is built.", file=sys.stderr)
+        print("bench.py: the library runs on one GPU (--gpus 1); it has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.cpu_suite:
         print(json.dumps({"cpu_suite": cpu_suite()}), flush=True)
