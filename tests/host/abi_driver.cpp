@@ -69,6 +69,11 @@ int main() {
     EXPECT(qlora_linear_fwd_group_workspace(rows3, 3, 4096, 1, 16) > 0);
     EXPECT(qlora_linear_fwd_group_workspace(rows3, 5, 4096, 1, 16) == 0);
     EXPECT(qlora_linear_fwd_group_workspace(nullptr, 3, 4096, 1, 16) == 0);
+    // where the forward's U and the backward's G run inside the GEMM launch
+    EXPECT(qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 16) == 1 &&
+           qlora_linear_fwd_u_in_launch(-1, 4096, 1024, 16) == 0);
+    EXPECT(qlora_linear_bwd_g_in_launch(4096, 11008, 1024, 16) == 1 &&
+           qlora_linear_bwd_g_in_launch(4096, 11008, 1024, 200) == 0);
 
     // quantize / double quant / dequantize
     EXPECT(nf4_quantize(nullptr, QL_F32, 4, 64, 64, B8, F, nullptr) == QL_ERR_NULL);
@@ -82,6 +87,23 @@ int main() {
     EXPECT(nf4_double_quant(F, -2, 256, B8, F, F, WS, 1 << 20, nullptr) == QL_ERR_SHAPE);
     EXPECT(launch_stop(nf4_double_quant(F, (int64_t)4096 * 4096 + 4097, 256, B8, F, F, WS,
                                         nf4_double_quant_workspace((int64_t)4096 * 4096 + 4097), nullptr)));
+    // quantize + double quant in one call: both launch plans (the folded
+    // tree level up to 4096 quantize workgroups, the three launches past it
+    // or with a tail), rejected arguments
+    const int64_t qshapes[][2] = {{4096, 4096}, {11008, 4096}, {4, 64}, {3, 100}, {16448, 4096}};
+    for (int dt : {QL_F32, QL_BF16})
+        for (const auto& rc : qshapes) {
+            const size_t qw = nf4_quantize_dq_workspace(rc[0], rc[1], dt);
+            EXPECT(qw > 0);
+            EXPECT(launch_stop(nf4_quantize_dq(P, dt, rc[0], rc[1], 64, B8, F, 256, B8, F, F, WS, qw, nullptr)));
+            EXPECT(nf4_quantize_dq(P, dt, rc[0], rc[1], 64, B8, F, 256, B8, F, F, WS, qw - 1, nullptr) ==
+                   QL_ERR_WORKSPACE);
+        }
+    EXPECT(nf4_quantize_dq_workspace(0, 64, QL_F32) == 0 && nf4_quantize_dq_workspace(4, 64, 7) == 0);
+    EXPECT(nf4_quantize_dq(P, QL_F32, 4, 64, 64, B8, F, 128, B8, F, F, WS, 1 << 20, nullptr) == QL_ERR_UNSUPPORTED);
+    EXPECT(nf4_quantize_dq(P, QL_F32, 4, 64, 64, B8, F, 256, nullptr, F, F, WS, 1 << 20, nullptr) == QL_ERR_NULL);
+    EXPECT(nf4_quantize_dq(MIS, QL_F32, 4, 64, 64, B8, F, 256, B8, F, F, WS, 1 << 20, nullptr) == QL_ERR_ALIGN);
+
     ql_nf4_weight w = weight(4096, 4096, 1);
     EXPECT(launch_stop(nf4_dequantize(&w, P, QL_BF16, nullptr)));
     EXPECT(nf4_dequantize(&w, P, 9, nullptr) == QL_ERR_UNSUPPORTED);
