@@ -5,7 +5,9 @@ for bit, the oracle within the usual bar, ragged token counts, and the
 tile's local fallback (forced from the host, so every kernel still ends
 normally). A captured forward (its tag mixes in an epoch word that a kernel
 recorded before it advances at every replay) replayed with new inputs
-equals the eager calls bit for bit, also when the tiles form U themselves."""
+equals the eager calls bit for bit, also when the tiles form U themselves.
+The same for the backward with G = s dY B inside the dX launch (dX, dA, dB,
+subsets of them, accumulation, the autograd wrapper)."""
 
 import pytest
 import torch
@@ -253,3 +255,68 @@ def test_captured_backward_replays_equal_eager_in_launch(qn, monkeypatch, spin):
         torch.cuda.synchronize()
         for a, b in zip(outs, eager):
             assert torch.equal(a, b), "replay %d differs from the eager call" % rep
+
+
+@pytest.mark.parametrize("need", [(True, True, False), (True, False, True), (False, True, False), (False, False, True)])
+def test_in_launch_g_partial_outputs_and_accumulation(qn, monkeypatch, need):
+    """Subsets of (dX, dA, dB), and dA, dB added to existing gradients, with
+    G inside the dX launch where dX is asked for: bitwise the separate
+    projection's results."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    N, K, T, r = BWD_SHAPES[2]
+    need_dx, need_da, need_db = need
+    W, case = _case(N, K, T, r, seed=31 + sum(need))
+    w = qn.quantize_weight(W.cuda())
+    X, dY, A, B = (t.cuda() for t in (case.X, case.dY, case.A, case.B))
+    _, U = qn.qlora_linear_fwd(w, X, A, B, case.scale)
+    dA0 = workloads.bf16_normal((r, K), 0.1, seed=40).float().cuda()
+    dB0 = workloads.bf16_normal((N, r), 0.1, seed=41).float().cuda()
+
+    def run():
+        dA, dB = dA0.clone(), dB0.clone()
+        out = qn.qlora_linear_bwd(w, X, dY, A, B, case.scale, U=U, need_dx=need_dx, need_da=need_da, need_db=need_db,
+                                  dA=dA if need_da else None, dB=dB if need_db else None, accumulate=True)
+        torch.cuda.synchronize()
+        return out
+
+    assert qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) == 1
+    g1 = run()
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    g2 = run()
+    for a, b, want, name in zip(g1, g2, need, ("dX", "dA", "dB")):
+        assert (a is None) == (not want) and (b is None) == (not want), name
+        if want:
+            assert torch.equal(a, b), name
+
+
+def test_autograd_with_u_and_g_inside_the_launches(qn, monkeypatch):
+    """The autograd wrapper at a shape where both the forward's U and the
+    backward's G run inside their GEMM launches: gradients bitwise those of
+    the separate projections, and within the oracle's bar."""
+    monkeypatch.setenv("QLORA_NF4_GEMM_TILE", "256")
+    N, K, T, r = 512, 1024, 300, 16
+    assert qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r) == 1
+    assert qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) == 1
+    W, case = _case(N, K, T, r, seed=77)
+    w = qn.quantize_weight(W.cuda())
+
+    def run():
+        X = case.X.cuda().requires_grad_(True)
+        A = case.A.cuda().requires_grad_(True)
+        B = case.B.cuda().requires_grad_(True)
+        Y = qn.QLoRALinearFunction.apply(X, A, B, w, case.scale)
+        Y.backward(case.dY.cuda())
+        torch.cuda.synchronize()
+        return Y.detach(), X.grad, A.grad, B.grad
+
+    r1 = run()
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    r2 = run()
+    for a, b, name in zip(r1, r2, ("Y", "dX", "dA", "dB")):
+        assert torch.equal(a, b), name
+    ref = oracle_weight(W.numpy())
+    dXo, dAo, dBo, _, _ = oracle.lora_backward(bf16_to_np(case.X), bf16_to_np(case.dY), ref["wd"],
+                                               bf16_to_np(case.A), bf16_to_np(case.B), case.scale)
+    assert normwise_rel_err(bf16_to_np(r1[1]), dXo) <= TOL
+    assert normwise_rel_err(f32_to_np(r1[2].float()), dAo) <= TOL
+    assert normwise_rel_err(f32_to_np(r1[3].float()), dBo) <= TOL
