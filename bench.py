@@ -78,6 +78,12 @@ def parse():
                     help="instead of the step: the 7B gate forward at T = 1024, r = 16 with U inside the GEMM "
                          "launch and with a separate projection launch first (eager calls and graph replays), "
                          "one JSON line")
+    ap.add_argument("--bwd-g", action="store_true",
+                    help="instead of the step: the 7B down backward at T = 1024, r = 16 with G inside the dX GEMM "
+                         "launch and with a separate projection launch first, one JSON line")
+    ap.add_argument("--quantize-dq", action="store_true",
+                    help="instead of the step: nf4_quantize_dq against nf4_quantize + nf4_double_quant at the 7B "
+                         "weight shapes, fp32 and bf16 input, one JSON line")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step: the wider measurement set (32-layer 7B stack, 65B linears, "
                          "a GEMV pass over the stack, residency, torch.matmul context), one JSON line")
@@ -980,8 +986,7 @@ def compare_fwd_u(torch, qn):
     issued both ways, in alternating rounds: U = X A^T computed by the
     GEMM's first workgroups (one launch) and by a separate projection launch
     before the GEMM (QLORA_NF4_FWD_U=prepass). HIP events around 20
-    back-to-back eager calls; captured launches always take the separate
-    projection, so graph replays of each mode time the same kernels."""
+    back-to-back eager calls."""
     N, K, T, r = 11008, 4096, 1024, 16
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
@@ -1019,6 +1024,106 @@ def compare_fwd_u(torch, qn):
     return res
 
 
+def compare_bwd_g(torch, qn):
+    """The backward of the 7B down projection (4096 x 11008, T = 1024,
+    r = 16; its dX GEMM runs 172 unsplit tiles) issued both ways, in
+    alternating rounds: G = s dY B computed by the dX GEMM's first
+    workgroups (one launch) and by a separate projection launch before it
+    (QLORA_NF4_FWD_U=prepass); dX alone and dX with dA and dB. HIP events
+    around 20 back-to-back eager calls."""
+    N, K, T, r = 4096, 11008, 1024, 16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    W = torch.randn(N, K, device="cuda", generator=g) * 0.02
+    X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+    dY = torch.randn(T, N, device="cuda", generator=g).to(torch.bfloat16)
+    A = (torch.randn(r, K, device="cuda", generator=g) / K).to(torch.bfloat16)
+    B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    w = qn.quantize_weight(W)
+    _, U = qn.qlora_linear_fwd(w, X, A, B, 2.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"shape": [N, K], "T": T, "r": r, "in_launch_applies": qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r)}
+    for kind, kw in (("dx", dict(need_da=False, need_db=False)), ("dx_da_db", {})):
+        times = {"in_launch": [], "separate_projection": []}
+        outs = {}
+        for rnd in range(3):
+            for mode in ("in_launch", "separate_projection"):
+                if mode == "separate_projection":
+                    os.environ["QLORA_NF4_FWD_U"] = "prepass"
+                else:
+                    os.environ.pop("QLORA_NF4_FWD_U", None)
+                for _ in range(3):
+                    qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U, **kw)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(20):
+                    o = qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U, **kw)
+                e1.record()
+                torch.cuda.synchronize()
+                times[mode].append(e0.elapsed_time(e1) / 20 * 1e3)
+                outs[mode] = [t.clone() for t in o if t is not None]
+        os.environ.pop("QLORA_NF4_FWD_U", None)
+        sub = {}
+        for mode, v in times.items():
+            sub[mode + "_us"] = round(sorted(v)[1], 1)
+            sub[mode + "_rounds_us"] = [round(x, 1) for x in v]
+        sub["same_bits"] = all(torch.equal(a, b) for a, b in zip(outs["in_launch"], outs["separate_projection"]))
+        res[kind] = sub
+    return res
+
+
+def compare_quantize_dq(torch, qn):
+    """Quantize + double quantization of the 7B weight shapes, fp32 and bf16
+    input, both ways in alternating rounds: nf4_quantize_dq (one call; two
+    launches where the quantize launch folds in the mean tree's first level)
+    and nf4_quantize followed by nf4_double_quant (three launches). HIP
+    events around 20 back-to-back eager calls; bitwise equality of the five
+    outputs."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2)
+    res = {}
+    for rows, cols in ((4096, 4096), (11008, 4096)):
+        Wf = torch.randn(rows, cols, device="cuda", generator=g) * 0.02
+        for name, W in (("f32", Wf), ("bf16", Wf.to(torch.bfloat16))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            times = {"one_call": [], "two_calls": []}
+            outs = {}
+            for rnd in range(3):
+                for mode in ("one_call", "two_calls"):
+                    def run():
+                        if mode == "one_call":
+                            return qn.nf4_quantize_dq(W)
+                        packed, absmax = qn.nf4_quantize(W)
+                        return (packed, absmax) + qn.nf4_double_quant(absmax)
+
+                    for _ in range(3):
+                        run()
+                    torch.cuda.synchronize()
+                    e0.record()
+                    for _ in range(20):
+                        o = run()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times[mode].append(e0.elapsed_time(e1) / 20 * 1e3)
+                    outs[mode] = o
+            sub = {"fold": lib_fold_applies(qn, rows, cols, name)}
+            for mode, v in times.items():
+                sub[mode + "_us"] = round(sorted(v)[1], 1)
+                sub[mode + "_rounds_us"] = [round(x, 1) for x in v]
+            sub["same_bits"] = all(torch.equal(a, b) for a, b in zip(outs["one_call"], outs["two_calls"]))
+            res["%dx%d_%s" % (rows, cols, name)] = sub
+    return res
+
+
+def lib_fold_applies(qn, rows, cols, dtype):
+    """Whether nf4_quantize_dq folds the tree level into its quantize launch
+    at this size (its workspace is then one fp64 node per quantize
+    workgroup, smaller than the tree levels' own)."""
+    dt = {"f32": qn._lib.QL_F32, "bf16": qn._lib.QL_BF16}[dtype]
+    n1 = -(-rows * cols // 64)
+    return qn.lib.nf4_quantize_dq_workspace(rows, cols, dt) != qn.lib.nf4_double_quant_workspace(n1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1039,6 +1144,12 @@ def main():
         return
     if args.fwd_u:
         print(json.dumps({"fwd_u": compare_fwd_u(torch, qn)}), flush=True)
+        return
+    if args.bwd_g:
+        print(json.dumps({"bwd_g": compare_bwd_g(torch, qn)}), flush=True)
+        return
+    if args.quantize_dq:
+        print(json.dumps({"quantize_dq": compare_quantize_dq(torch, qn)}), flush=True)
         return
     print("bench: generating inputs", file=sys.stderr, flush=True)
     inp = Inputs(torch, workloads)
