@@ -981,12 +981,39 @@ def run_suite(torch, qn):
                                       reps=11) * 1e6, 1)}
     return res
 
+def replay_us_per_call(torch, fn, calls=10, replays=5):
+    """fn() captured `calls` times into one HIP graph (after a warm-up call on
+    a side stream), replayed 3 times untimed, then `replays` times between
+    HIP events: microseconds per captured call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (calls * replays) * 1e3
+
+
 def compare_fwd_u(torch, qn):
     """The forward of the 7B gate projection (11008 x 4096, T = 1024, r = 16)
     issued both ways, in alternating rounds: U = X A^T computed by the
     GEMM's first workgroups (one launch) and by a separate projection launch
     before the GEMM (QLORA_NF4_FWD_U=prepass). HIP events around 20
-    back-to-back eager calls."""
+    back-to-back eager calls, then around replays of 10 calls captured in a
+    HIP graph (a captured in-launch call also records its epoch kernel)."""
     N, K, T, r = 11008, 4096, 1024, 16
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
@@ -1016,10 +1043,19 @@ def compare_fwd_u(torch, qn):
             torch.cuda.synchronize()
             times[mode].append(e0.elapsed_time(e1) / 20 * 1e3)
             outs[mode] = Y.clone()
+    graph = {"in_launch": [], "separate_projection": []}
+    for rnd in range(3):
+        for mode in graph:
+            if mode == "separate_projection":
+                os.environ["QLORA_NF4_FWD_U"] = "prepass"
+            else:
+                os.environ.pop("QLORA_NF4_FWD_U", None)
+            graph[mode].append(replay_us_per_call(torch, lambda: qn.qlora_linear_fwd(w, X, A, B, 2.0, out=Y)))
     os.environ.pop("QLORA_NF4_FWD_U", None)
     for mode, v in times.items():
         res[mode + "_us"] = round(sorted(v)[1], 1)
         res[mode + "_rounds_us"] = [round(x, 1) for x in v]
+        res[mode + "_graph_rounds_us"] = [round(x, 1) for x in graph[mode]]
     res["same_bits"] = bool(torch.equal(outs["in_launch"], outs["separate_projection"]))
     return res
 
@@ -1030,7 +1066,8 @@ def compare_bwd_g(torch, qn):
     alternating rounds: G = s dY B computed by the dX GEMM's first
     workgroups (one launch) and by a separate projection launch before it
     (QLORA_NF4_FWD_U=prepass); dX alone and dX with dA and dB. HIP events
-    around 20 back-to-back eager calls."""
+    around 20 back-to-back eager calls, then around replays of 10 calls
+    captured in a HIP graph."""
     N, K, T, r = 4096, 11008, 1024, 16
     g = torch.Generator(device="cuda")
     g.manual_seed(1)
@@ -1062,11 +1099,20 @@ def compare_bwd_g(torch, qn):
                 torch.cuda.synchronize()
                 times[mode].append(e0.elapsed_time(e1) / 20 * 1e3)
                 outs[mode] = [t.clone() for t in o if t is not None]
+        graph = {"in_launch": [], "separate_projection": []}
+        for rnd in range(3):
+            for mode in graph:
+                if mode == "separate_projection":
+                    os.environ["QLORA_NF4_FWD_U"] = "prepass"
+                else:
+                    os.environ.pop("QLORA_NF4_FWD_U", None)
+                graph[mode].append(replay_us_per_call(torch, lambda: qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U, **kw)))
         os.environ.pop("QLORA_NF4_FWD_U", None)
         sub = {}
         for mode, v in times.items():
             sub[mode + "_us"] = round(sorted(v)[1], 1)
             sub[mode + "_rounds_us"] = [round(x, 1) for x in v]
+            sub[mode + "_graph_rounds_us"] = [round(x, 1) for x in graph[mode]]
         sub["same_bits"] = all(torch.equal(a, b) for a, b in zip(outs["in_launch"], outs["separate_projection"]))
         res[kind] = sub
     return res
