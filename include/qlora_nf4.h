@@ -59,9 +59,10 @@
  *     the T > 16 GEMMs, QLORA_NF4_PROJ_SPLITS for the rank-r projections, and
  *     QLORA_NF4_GEMV_SPIN (loads of the shared U before a decode workgroup
  *     computes U itself; 0 forces that path), QLORA_NF4_GEMM_SPIN (the same
- *     for a GEMM forward tile; -1 forces it) and QLORA_NF4_FWD_U=prepass (U
- *     in a separate launch before the GEMM). Results stay within the stated
- *     tolerances under any of them.
+ *     for a GEMM tile waiting on U or G; -1 forces it), QLORA_NF4_FWD_U=prepass
+ *     (U, and the backward's G, in a separate launch before the GEMM) and
+ *     QLORA_NF4_ADAMW_PAGING=staged (qlora_paged_adamw). Results stay within
+ *     the stated tolerances under any of them.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
