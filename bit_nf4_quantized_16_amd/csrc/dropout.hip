@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void keep_apply_kernel(const uint16_t* __restr
 // dX[t][k] += fl32(c * sum_j G[t][j] A[j][k]) for kept (t, k), rounded to
 // bf16 (fp32 products and sums). A workgroup owns 32 tokens x 128 columns:
 // the rank-r slices of G (as fp32) and A are staged in LDS; thread (tt, kc)
-// computes tokens tt and tt + 16 at columns 8 kc .. 8 kc + 7.
+// computes tokens tt and tt + 16 at columns 8 kc .. 8 kc + 7, whose dX values
+// and keep bits it loads first, so that their latency overlaps the staging.
 constexpr int kKeepTT = 32, kKeepCols = 128;
 constexpr int kKeepGLd = QL_MAX_RANK + 1;  // fp32 row stride of the staged G (odd: rows in different banks)
 
@@ -59,6 +60,17 @@ __global__ __launch_bounds__(256) void lora_dx_keep_kernel(const uint16_t* __res
     const int tid = threadIdx.x;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kKeepTT;  // x: tokens (any T), y: column tiles
     const int64_t k0 = static_cast<int64_t>(blockIdx.y) * kKeepCols;
+    const int tt = tid >> 4, kc = tid & 15;
+    const int64_t k = k0 + 8 * kc;
+    uint4 xin[2];
+    uint32_t kbits[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t t = t0 + tt + 16 * h;
+        const bool in = t < T && k < K;
+        xin[h] = in ? *reinterpret_cast<const uint4*>(dX + t * K + k) : make_uint4(0, 0, 0, 0);
+        kbits[h] = in ? keep[t * (K / 8) + k / 8] : 0u;
+    }
     for (int q = tid; q < r * (kKeepCols / 8); q += 256) {
         const int j = q / (kKeepCols / 8), col = 8 * (q % (kKeepCols / 8));
         const int64_t k = k0 + col;
@@ -72,7 +84,6 @@ __global__ __launch_bounds__(256) void lora_dx_keep_kernel(const uint16_t* __res
     }
     __syncthreads();
 
-    const int tt = tid >> 4, kc = tid & 15;
     float acc0[8], acc1[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.0f;
@@ -89,16 +100,15 @@ __global__ __launch_bounds__(256) void lora_dx_keep_kernel(const uint16_t* __res
             acc1[2 * q + 1] = __builtin_fmaf(g1, hi, acc1[2 * q + 1]);
         }
     }
-    const int64_t k = k0 + 8 * kc;
     if (k >= K) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int64_t t = t0 + tt + 16 * h;
         if (t >= T) continue;
         const float* acc = h == 0 ? acc0 : acc1;
-        const uint32_t bits = keep[t * (K / 8) + k / 8];
+        const uint32_t bits = kbits[h];
         uint16_t* px = dX + t * K + k;
-        const uint4 xv = *reinterpret_cast<const uint4*>(px);
+        const uint4 xv = xin[h];
         const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
         uint32_t o[4];
 #pragma unroll
