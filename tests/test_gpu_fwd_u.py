@@ -320,3 +320,32 @@ def test_autograd_with_u_and_g_inside_the_launches(qn, monkeypatch):
     assert normwise_rel_err(bf16_to_np(r1[1]), dXo) <= TOL
     assert normwise_rel_err(f32_to_np(r1[2].float()), dAo) <= TOL
     assert normwise_rel_err(f32_to_np(r1[3].float()), dBo) <= TOL
+
+
+@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008)])
+def test_in_launch_u_and_g_at_t4096(qn, monkeypatch, N, K):
+    """T = 4096, r = 16 at the 7B MLP shapes: 256 projection workgroups and
+    688 tiles, so the tiles run in several rounds after the projection
+    workgroups. Forward (U inside) and backward (G inside) bitwise the
+    separate projections'."""
+    T, r = 4096, 16
+    assert qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r) == 1
+    assert qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) == 1
+    W = workloads.normal_weight(N, K, 0.02, seed=N // 64 + 1)
+    X = workloads.bf16_normal((T, K), 1.0, seed=50).cuda()
+    dY = workloads.bf16_normal((T, N), 1.0, seed=51).cuda()
+    A = workloads.bf16_normal((r, K), 1.0 / K, seed=52).cuda()
+    B = workloads.bf16_normal((N, r), 0.01, seed=53).cuda()
+    w = qn.quantize_weight(W.cuda())
+
+    def run():
+        Y, U = qn.qlora_linear_fwd(w, X, A, B, 2.0)
+        g = qn.qlora_linear_bwd(w, X, dY, A, B, 2.0, U=U)
+        torch.cuda.synchronize()
+        return (Y, U) + tuple(g)
+
+    r1 = run()
+    monkeypatch.setenv("QLORA_NF4_FWD_U", "prepass")
+    r2 = run()
+    for a, b, name in zip(r1, r2, ("Y", "U", "dX", "dA", "dB")):
+        assert torch.equal(a, b), name
