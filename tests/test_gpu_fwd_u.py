@@ -349,3 +349,46 @@ def test_in_launch_u_and_g_at_t4096(qn, monkeypatch, N, K):
     r2 = run()
     for a, b, name in zip(r1, r2, ("Y", "U", "dX", "dA", "dB")):
         assert torch.equal(a, b), name
+
+
+def test_in_launch_calls_on_two_streams_at_once(qn):
+    """Two forwards with U inside (7B gate and up shapes) and two backwards
+    with G inside (down shape) issued on two streams at the same time, so
+    their projection workgroups and tiles share the chip: every output
+    equals the same call made alone."""
+    T, r = 1024, 16
+    shapes = [(11008, 4096), (11008, 4096), (4096, 11008), (4096, 11008)]
+    cases = []
+    for i, (N, K) in enumerate(shapes):
+        W = workloads.normal_weight(N, K, 0.02, seed=60 + i)
+        X = workloads.bf16_normal((T, K), 1.0, seed=70 + i).cuda()
+        dY = workloads.bf16_normal((T, N), 1.0, seed=80 + i).cuda()
+        A = workloads.bf16_normal((r, K), 1.0 / K, seed=90 + i).cuda()
+        B = workloads.bf16_normal((N, r), 0.01, seed=100 + i).cuda()
+        cases.append((qn.quantize_weight(W.cuda()), X, dY, A, B))
+
+    def call(i):
+        w, X, dY, A, B = cases[i]
+        if i < 2:
+            return qn.qlora_linear_fwd(w, X, A, B, 2.0)
+        return qn.qlora_linear_bwd(w, X, dY, A, B, 2.0)
+
+    alone = []
+    for i in range(4):
+        alone.append([t.clone() for t in call(i) if t is not None])
+        torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    together = [None] * 4
+    for rep in range(3):
+        for pair in ((0, 1), (2, 3)):
+            with torch.cuda.stream(s1):
+                together[pair[0]] = call(pair[0])
+            with torch.cuda.stream(s2):
+                together[pair[1]] = call(pair[1])
+        torch.cuda.synchronize()
+        for i in range(4):
+            got = [t for t in together[i] if t is not None]
+            for a, b in zip(got, alone[i]):
+                assert torch.equal(a, b), "call %d, repetition %d" % (i, rep)
