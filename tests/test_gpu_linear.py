@@ -328,3 +328,33 @@ def test_long_batch_backward_with_gradients_skipped(qn, need_da, need_db):
         assert normwise_rel_err(f32_to_np(dA), dAo) <= TOL
     if need_db:
         assert normwise_rel_err(f32_to_np(dB), dBo) <= TOL
+
+
+def test_decode_calls_on_two_streams_at_once(qn):
+    """Decode GEMVs (U handed over in tagged words inside each launch) issued
+    on two streams at the same time, several rounds: every Y and U equals
+    the same call made alone."""
+    cases = []
+    for i, (N, K, T, r) in enumerate([(4096, 4096, 1, 16), (11008, 4096, 16, 16), (1024, 4096, 5, 8),
+                                      (4096, 11008, 1, 64)]):
+        W = workloads.normal_weight(N, K, 0.02, seed=110 + i)
+        X = workloads.bf16_normal((T, K), 1.0, seed=120 + i).cuda()
+        A = workloads.bf16_normal((r, K), 1.0 / K, seed=130 + i).cuda()
+        B = workloads.bf16_normal((N, r), 0.01, seed=140 + i).cuda()
+        cases.append((qn.quantize_weight(W.cuda()), X, A, B))
+    alone = []
+    for w, X, A, B in cases:
+        alone.append([t.clone() for t in qn.qlora_linear_fwd(w, X, A, B, 2.0)])
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        outs = []
+        for i, (w, X, A, B) in enumerate(cases):
+            with torch.cuda.stream(streams[i % 2]):
+                outs.append(qn.qlora_linear_fwd(w, X, A, B, 2.0))
+        torch.cuda.synchronize()
+        for i, (o, a) in enumerate(zip(outs, alone)):
+            for x, y in zip(o, a):
+                assert torch.equal(x, y), "call %d, repetition %d" % (i, rep)
