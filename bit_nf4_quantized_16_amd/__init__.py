@@ -321,8 +321,11 @@ def paged_adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr=2e-4, betas=(0.9
     """One AdamW step (fp32 state) of a flat fp32 parameter tensor in place.
     ``exp_avg`` / ``exp_avg_sq``: fp32 tensors of the same size, both on the
     GPU or both in pinned host memory (``pin_memory=True``): paged-out state
-    streams through a device staging buffer, its copies on ``copy_stream``
-    (a torch.cuda.Stream; None runs them on the current stream).
+    is read and written in place over the host link (pinned memory is mapped
+    into the device's address space); with QLORA_NF4_ADAMW_PAGING=staged it
+    streams through a device staging buffer instead, its copies on
+    ``copy_stream`` (a torch.cuda.Stream; None runs them on the current
+    stream).
     ``param_bf16``: optional bf16 tensor that receives the updated values."""
     n = param.numel()
     for t in (param, grad, exp_avg, exp_avg_sq):
