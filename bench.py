@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step: the wider measurement set (32-layer 7B stack, 65B linears, "
                          "a GEMV pass over the stack, residency, torch.matmul context), one JSON line")
+    ap.add_argument("--suite-stack", action="store_true",
+                    help="instead of the step: only the 7B stack passes of --suite (quantize, dequantize, decode "
+                         "GEMV), e.g. under a kernel trace for the kernels' own durations, one JSON line")
     return ap.parse_args()
 
 
@@ -654,7 +657,7 @@ def clock_info():
     return out
 
 
-def run_suite(torch, qn):
+def run_suite(torch, qn, stack_only=False):
     res = {}
     prop = torch.cuda.get_device_properties(0)
     res["device"] = {"name": prop.name, "compute_units": prop.multi_processor_count,
@@ -748,9 +751,30 @@ def run_suite(torch, qn):
     ndq, msdq = tdq.read()
     tdq.disarm()
     dq_bytes = BPW_DEQUANT * nweights
+
+    # the same 224 launches captured once into a HIP graph and replayed: the
+    # pass's wall time without host-side gaps or per-launch timer events
+    def dequant_pass():
+        for _, n, k, w in stack:
+            qn.nf4_dequantize(w, out=outs_dq[(n, k)])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dequant_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dequant_pass()
+    dq_graph_s = timed(graph.replay, reps=5)
+    del graph
     res["c4_stack_dequantize_bf16"] = {"launches": ndq, "kernel_ms": round(msdq, 3), "GB": round(dq_bytes / 1e9, 2),
                                        "GB/s": round(dq_bytes / (msdq / 1e3) / 1e9, 1),
-                                       "frac": round(dq_bytes / (msdq / 1e3) / PEAK_HBM, 4)}
+                                       "frac": round(dq_bytes / (msdq / 1e3) / PEAK_HBM, 4),
+                                       "graph_ms": round(dq_graph_s * 1e3, 3),
+                                       "graph_GB/s": round(dq_bytes / dq_graph_s / 1e9, 1),
+                                       "graph_frac": round(dq_bytes / dq_graph_s / PEAK_HBM, 4)}
     del outs_dq
 
     # (2) one decode GEMV pass over all 224 linears, r = 16, T in {1, 16}:
@@ -833,6 +857,8 @@ def run_suite(torch, qn):
                                             "grouped_graph_GB/s": round(nbytes / ggraph_s / 1e9, 1),
                                             "grouped_graph_frac": round(nbytes / ggraph_s / PEAK_HBM, 4)})
         del outs
+    if stack_only:
+        return res
 
     def gemm_rows(shapes, T, r, alpha, std, seed0, weights=None):
         rows, tf_f, tf_b, t_f, t_b = {}, 0.0, 0.0, 0.0, 0.0
@@ -1185,8 +1211,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     torch.cuda.set_device(0)
-    if args.suite:
-        print(json.dumps({"suite": run_suite(torch, qn)}), flush=True)
+    if args.suite or args.suite_stack:
+        print(json.dumps({"suite": run_suite(torch, qn, stack_only=args.suite_stack)}), flush=True)
         return
     if args.fwd_u:
         print(json.dumps({"fwd_u": compare_fwd_u(torch, qn)}), flush=True)
