@@ -27,6 +27,7 @@ __all__ = [
     "qlora_linear_fwd",
     "qlora_linear_fwd_group",
     "qlora_linear_bwd",
+    "qlora_linear_bwd_group",
     "quantize_weight",
     "QLoRALinearFunction",
     "KernelTimer",
@@ -314,6 +315,42 @@ def qlora_linear_bwd(w, X, dY, A=None, B=None, scale=1.0, U=None, need_dx=True, 
                                          _stream())
         )
     return dX, dA, dB
+
+
+def qlora_linear_bwd_group(ws, X, dYs, As=None, Bs=None, scale=1.0, Us=None, need_dx=True, need_da=True,
+                           need_db=True, dAs=None, dBs=None, accumulate=False):
+    """qlora_linear_bwd for up to four layers that read the same X (q/k/v,
+    gate/up). Returns (dX bf16 [T, K] = the sum of the layers' input
+    gradients, or None; list of dA or None; list of dB or None). ``ws``
+    NF4Weights sharing ``cols``; ``dYs`` their upstream gradients; ``As``,
+    ``Bs``, ``Us`` lists per layer (None for r = 0 / no saved U)."""
+    nw = len(ws)
+    T = dYs[0].shape[0]
+    r = 0 if As is None else As[0].shape[0]
+    dev = dYs[0].device
+    cols = ws[0].cols if nw else 0
+    dX = torch.empty(T, cols, dtype=torch.bfloat16, device=dev) if need_dx else None
+    new = torch.zeros if accumulate else torch.empty
+    if r > 0 and need_da and dAs is None:
+        dAs = [new(r, cols, dtype=torch.float32, device=dev) for _ in ws]
+    if r > 0 and need_db and dBs is None:
+        dBs = [new(w.rows, r, dtype=torch.float32, device=dev) for w in ws]
+    if not need_da:
+        dAs = None
+    if not need_db:
+        dBs = None
+    descs = [w.descriptor() for w in ws]
+    arr = lambda ts: (ctypes.c_void_p * max(nw, 1))(*[_ptr(t) for t in ts]) if ts is not None else None
+    wp = (ctypes.c_void_p * max(nw, 1))(*[ctypes.addressof(d) for d in descs])
+    rows = (ctypes.c_int64 * max(nw, 1))(*[w.rows for w in ws])
+    ws_, wsb = _workspace(lib.qlora_linear_bwd_group_workspace(rows, nw, cols, max(T, 1), r), dev)
+    _check(
+        lib.qlora_linear_bwd_group(wp, nw, _ptr(_bits(X)), arr([_bits(d) for d in dYs]), T,
+                                   arr([_bits(a) for a in As]) if As is not None else None,
+                                   arr([_bits(b) for b in Bs]) if Bs is not None else None, r, float(scale), arr(Us),
+                                   _ptr(dX), arr(dAs), arr(dBs), 1 if accumulate else 0, _ptr(ws_), wsb, _stream())
+    )
+    return dX, dAs, dBs
 
 
 def paged_adamw_step(param, grad, exp_avg, exp_avg_sq, step, lr=2e-4, betas=(0.9, 0.999), eps=1e-8,

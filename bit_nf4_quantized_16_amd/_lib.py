@@ -85,6 +85,8 @@ SIGNATURES = {
     "qlora_linear_fwd_dropout": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_bwd": (_I, [_WP, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
+    "qlora_linear_bwd_group_workspace": (_SZ, [_P, _I32, _I64, _I64, _I32]),
+    "qlora_linear_bwd_group": (_I, [_P, _I32, _P, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
     "qlora_linear_bwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_bwd_dropout": (_I, [_WP, _P, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _P, _I, _P, _SZ, _P]),
     "qlora_paged_adamw_workspace": (_SZ, [_I64]),

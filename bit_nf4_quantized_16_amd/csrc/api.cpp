@@ -215,6 +215,47 @@ BwdWs carve_bwd(void* ws, int64_t N, int64_t K, int64_t T, int32_t r, bool want_
     return b;
 }
 
+// ---- grouped backward workspace -----------------------------------------
+// Layers that read the same X: G of every layer (the grouped dX GEMM reads
+// them all), one set of gradient operands and partials reused layer by layer
+// (stream order), and the dX GEMM's split partials.
+struct GroupBwdWs {
+    uint16_t* Gp[kGemmMaxGroup] = {};  // bf16 [T, rp64] per layer
+    uint16_t* Gt = nullptr;            // bf16 [rp16, T], the layer being processed
+    uint16_t* Ut = nullptr;
+    float* gpart = nullptr;
+    void* proj = nullptr;
+    float* split = nullptr;
+    size_t bytes = 0;
+};
+
+GroupBwdWs carve_bwd_group(void* ws, const int64_t* N, int nw, int64_t K, int64_t T, int32_t r, bool want_dx,
+                           bool want_da, bool want_db) {
+    Carver c(ws);
+    GroupBwdWs b;
+    if (r > 0) {
+        const int rp = rank_pad64(r);
+        const int rp16 = lora_grad_rp(r);
+        if (want_dx)
+            for (int i = 0; i < nw; ++i) b.Gp[i] = c.take<uint16_t>(static_cast<size_t>(T) * rp);
+        if (want_da) b.Gt = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
+        if (want_db) b.Ut = c.take<uint16_t>(static_cast<size_t>(rp16) * lora_vt_ld(T));
+        size_t gb = 0, pb = lora_proj_ws_bytes(T, r, K, false);
+        for (int i = 0; i < nw; ++i) {
+            gb = std::max(gb, lora_grads_part_bytes(T, want_da ? K : 0, want_db ? N[i] : 0, r));
+            pb = std::max(pb, lora_proj_ws_bytes(T, r, N[i], true));
+        }
+        if (gb && (want_da || want_db)) b.gpart = c.take<float>(gb / sizeof(float));
+        if (pb) b.proj = c.take<char>(pb);
+    }
+    if (want_dx) {
+        const size_t sb = gemm_split_bytes(K, T, int64_t{64} * gemm_group_steps(N, nw));
+        if (sb) b.split = c.take<float>(sb / sizeof(float));
+    }
+    b.bytes = align_up(c.off, 256);
+    return b;
+}
+
 }  // namespace
 }  // namespace qlnf4
 
@@ -626,6 +667,136 @@ int linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, in
     return QL_OK;
 }
 
+size_t group_bwd_ws(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
+    if (rows == nullptr || nw < 1 || nw > kGemmMaxGroup || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    for (int i = 0; i < nw; ++i)
+        if (rows[i] <= 0) return 0;
+    return carve_bwd_group(nullptr, rows, nw, cols, T, r, true, true, true).bytes;
+}
+
+int linear_bwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, const uint16_t* const* dY,
+                     int64_t T, const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                     const float* const* U_saved, uint16_t* dX, float* const* dA, float* const* dB, int accumulate,
+                     void* ws, size_t ws_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    int s;
+    if (nw < 1 || nw > kGemmMaxGroup)
+        return set_error(QL_ERR_SHAPE, "%d weights in a group (1 to %d)", nw, kGemmMaxGroup);
+    // w, dY, A, B, U_saved, dA and dB are host arrays of pointers
+    if (w == nullptr || dY == nullptr) return set_error(QL_ERR_NULL, "%s array is NULL", w == nullptr ? "w" : "dY");
+    if (r > 0 && (A == nullptr || B == nullptr))
+        return set_error(QL_ERR_NULL, "%s array is NULL", A == nullptr ? "A" : "B");
+    if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_UNSUPPORTED, "accumulate = %d", accumulate);
+    int64_t rows[kGemmMaxGroup];
+    bool want_da = false, want_db = false, need_x = false;
+    for (int i = 0; i < nw; ++i) {
+        if ((s = check_weight(w[i])) != QL_OK) return s;
+        if ((s = check_linear_shape(w[i], T, r)) != QL_OK) return s;
+        if (w[i]->cols != w[0]->cols)
+            return set_error(QL_ERR_SHAPE, "weight %d has %lld columns, weight 0 %lld", i, (long long)w[i]->cols,
+                             (long long)w[0]->cols);
+        if ((w[i]->dq_blocksize != 0) != (w[0]->dq_blocksize != 0))
+            return set_error(QL_ERR_UNSUPPORTED, "weight %d and weight 0 differ in double quantization", i);
+        rows[i] = w[i]->rows;
+        const bool da = dA != nullptr && dA[i] != nullptr, db = dB != nullptr && dB[i] != nullptr;
+        const bool hu = U_saved != nullptr && U_saved[i] != nullptr;
+        if (r == 0 && (da || db)) return set_error(QL_ERR_SHAPE, "dA / dB requested with rank 0");
+        if (da && (s = check_ptr(dA[i], "dA[i]")) != QL_OK) return s;
+        if (db && (s = check_ptr(dB[i], "dB[i]")) != QL_OK) return s;
+        if (hu && (s = check_ptr(U_saved[i], "U_saved[i]")) != QL_OK) return s;
+        if (r > 0) {
+            if ((s = check_ptr(A[i], "A[i]")) != QL_OK) return s;
+            if ((s = check_ptr(B[i], "B[i]")) != QL_OK) return s;
+        }
+        want_da = want_da || da;
+        want_db = want_db || db;
+        need_x = need_x || da || (db && !hu);
+    }
+    const bool want_dx = dX != nullptr;
+    if (T == 0 || (!want_dx && !want_da && !want_db)) return QL_OK;
+    for (int i = 0; i < nw; ++i)
+        if ((s = check_ptr(dY[i], "dY[i]")) != QL_OK) return s;
+    if (want_dx && (s = check_ptr(dX, "dX")) != QL_OK) return s;
+    if (need_x && (s = check_ptr(X, "X")) != QL_OK) return s;
+    const int64_t K = w[0]->cols;
+    const GroupBwdWs need = carve_bwd_group(nullptr, rows, nw, K, T, r, want_dx, want_da, want_db);
+    if (need.bytes > 0) {
+        if (ws == nullptr || ws_bytes < need.bytes)
+            return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
+                             need.bytes);
+        if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const GroupBwdWs b = carve_bwd_group(ws, rows, nw, K, T, r, want_dx, want_da, want_db);
+    const int rp = rank_pad64(r);
+    const int rp16 = lora_grad_rp(r);
+    const int64_t ldv = lora_vt_ld(T);
+    // layer by layer: G (for dX, kept per layer; G^T for dA), U^T for dB, then
+    // that layer's dA and dB (the operands are reused by the next layer)
+    for (int i = 0; i < nw && r > 0; ++i) {
+        const int64_t N = rows[i];
+        const bool da = dA != nullptr && dA[i] != nullptr, db = dB != nullptr && dB[i] != nullptr;
+        const bool hu = U_saved != nullptr && U_saved[i] != nullptr;
+        if (want_dx || da || (db && hu)) {
+            ProjArgs a{};
+            a.proj = (want_dx || da) ? 1 : 0;
+            a.P = dY[i];
+            a.ldp = N;
+            a.Q = B[i];
+            a.ldq = r;
+            a.rq = r;
+            a.T = T;
+            a.kred = N;
+            a.alpha_b = scale;
+            a.out_b = want_dx ? b.Gp[i] : nullptr;
+            a.ld_b = rp;
+            a.out_bt = da ? b.Gt : nullptr;
+            a.rows_bt = rp16;
+            a.ld_bt = ldv;
+            if (db && hu) {
+                a.Usrc = U_saved[i];
+                a.ru = r;
+                a.Ut = b.Ut;
+                a.rows_ut = rp16;
+                a.ld_ut = ldv;
+            }
+            if ((s = launch_lora_proj(a, true, b.proj, st)) != QL_OK) return s;
+        }
+        if (db && !hu) {  // U^T = (X A^T)^T recomputed
+            ProjArgs a{};
+            a.proj = 1;
+            a.P = X;
+            a.ldp = K;
+            a.Q = A[i];
+            a.ldq = K;
+            a.rq = r;
+            a.T = T;
+            a.kred = K;
+            a.alpha_b = 1.0f;
+            a.out_bt = b.Ut;
+            a.rows_bt = rp16;
+            a.ld_bt = ldv;
+            if ((s = launch_lora_proj(a, false, b.proj, st)) != QL_OK) return s;
+        }
+        if (da || db) {
+            GradArgs g{};
+            g.r = r;
+            g.T = T;
+            g.accumulate = accumulate;
+            if (da) g.pb[0] = GradProblem{X, K, K, b.Gt, ldv, dA[i], 1, 1.0f, nullptr};
+            if (db) g.pb[1] = GradProblem{dY[i], N, N, b.Ut, ldv, dB[i], 0, scale, nullptr};
+            if ((s = launch_lora_grads(g, b.gpart, st)) != QL_OK) return s;
+        }
+    }
+    if (want_dx) {
+        GemmLayer layers[kGemmMaxGroup];
+        for (int i = 0; i < nw; ++i)
+            layers[i] = GemmLayer{to_dev(w[i]), dY[i], rows[i], r > 0 ? b.Gp[i] : nullptr, r > 0 ? A[i] : nullptr};
+        if ((s = launch_gemm_dx_group(layers, nw, r, rp, dX, T, K, b.split, st)) != QL_OK) return s;
+    }
+    return QL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -670,6 +841,17 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
                      float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
     return linear_bwd(w, X, dY, T, A, B, r, scale, nullptr, 0.0f, U_saved, dX, dA, dB, accumulate, ws, ws_bytes,
                       stream);
+}
+
+size_t qlora_linear_bwd_group_workspace(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
+    return group_bwd_ws(rows, nw, cols, T, r);
+}
+
+int qlora_linear_bwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, const uint16_t* const* dY,
+                           int64_t T, const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
+                           const float* const* U_saved, uint16_t* dX, float* const* dA, float* const* dB,
+                           int accumulate, void* ws, size_t ws_bytes, void* stream) {
+    return linear_bwd_group(w, nw, X, dY, T, A, B, r, scale, U_saved, dX, dA, dB, accumulate, ws, ws_bytes, stream);
 }
 
 int qlora_linear_bwd_dropout(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* dY, int64_t T,

@@ -68,6 +68,15 @@ struct TileArgs {
     float s_u;
     int spin;  // word loads before the tile forms its tokens' U itself
     const uint64_t* epoch;  // captured launch: the epoch word its tag mixes in (launch_tag), else null
+    // Grouped dX (the GRP kernels): dX = sum over ng layers that read the same
+    // X of dY_L W_L' + G_L A_L. The layers' rows form one reduction of
+    // gstep[ng] steps, layer L owning steps [gstep[L], gstep[L + 1]); the
+    // split plan cuts that reduction as it cuts one layer's (a workgroup's
+    // steps may span layers), and the rank step of layer L runs on split
+    // L % splits.
+    int ng;
+    int gstep[kGemmMaxGroup + 1];
+    GemmLayer gl[kGemmMaxGroup];
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -138,8 +147,9 @@ struct Codes {
     BlockConst bc;
 };
 
-template <int TA, int TT, int WA, int WT, bool DX, bool DQ>
+template <int TA, int TT, int WA, int WT, bool DX, bool DQ, bool GRP>
 __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_kernel(TileArgs p) {
+    static_assert(!GRP || DX, "grouped launches run dX");
     using S = TileShape<TA, TT, WA, WT, DX>;
     constexpr int SA = S::SA, ST = S::ST, CPT = S::CPT, CC = S::CC, LDA = S::LDA, TPR = S::TPR;
     constexpr int MW = S::MW, TW = S::TW, NW = S::NW, NTHR = S::NTHR;
@@ -195,27 +205,64 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     const int64_t t0 = static_cast<int64_t>(logical / p.tiles_a) * TT;
     const int64_t MA = DX ? p.K : p.N;
     const int64_t RED = DX ? p.N : p.K;
-    const int nsteps_all = static_cast<int>(ceil_div(RED, kStep));
+    const int nsteps_all = GRP ? p.gstep[p.ng] : static_cast<int>(ceil_div(RED, kStep));
     // split-K: this workgroup covers reduction steps [sb, se)
     const int split = blockIdx.y;
     const int spp = (nsteps_all + p.splits - 1) / p.splits;
     const int sb = split * spp;
     const int se = min(nsteps_all, sb + spp);
     const int msteps = se;
-    const float mu = DQ ? *p.w.mean : 0.0f;
+    const float mu = (DQ && !GRP) ? *p.w.mean : 0.0f;
+    // The operands of reduction step `step`: the arguments' own, or in a
+    // grouped dX those of the layer bound below for the part of [sb, se) that
+    // layer owns (its weight, dY with row stride N, N, double-quantization
+    // mean, first step).
+    NF4Dev gw{};
+    const uint16_t* gact = nullptr;
+    int64_t gN = 0;
+    float gmu = 0.0f;
+    int gbase = 0;
+    auto lstep = [&](int step) -> int {
+        if constexpr (GRP) return step - gbase;
+        else return step;
+    };
+    auto lw = [&](int) -> const NF4Dev& {
+        if constexpr (GRP) return gw;
+        else return p.w;
+    };
+    auto lact = [&](int) {
+        if constexpr (GRP) return gact;
+        else return p.act;
+    };
+    auto lred = [&](int) -> int64_t {
+        if constexpr (GRP) return gN;
+        else return RED;
+    };
+    auto lld = [&](int) -> int64_t {
+        if constexpr (GRP) return gN;
+        else return p.ld_act;
+    };
+    auto lmu = [&](int) -> float {
+        if constexpr (GRP) return gmu;
+        else return mu;
+    };
 
     // ---- token tile: direct loads into LDS --------------------------------
     // Wave w issues loads q = NW i + w (i < DMA); load q fills rows 8q..8q+7.
     auto dma = [&](int step, uint16_t* sX) {
-        const int64_t r0 = static_cast<int64_t>(step) * kStep;
+        const int64_t r0 = static_cast<int64_t>(lstep(step)) * kStep;
 #pragma unroll
         for (int i = 0; i < S::DMA; ++i) {
             const int q = NW * i + wave;
             const int row = 8 * q + (lane >> 3);
             const int lc = (lane & 7) ^ swz(row);
             const int64_t t = min(t0 + row, p.T - 1);
-            const int64_t col = min(r0 + 8 * lc, RED - 8);
-            __builtin_amdgcn_global_load_lds(p.act + t * p.ld_act + col, (QL_LDS void*)(sX + q * 512), 16, 0, 0);
+            const int64_t col = min(r0 + 8 * lc, lred(step) - 8);
+            // the address is formed before the builtin's argument list: with
+            // the accessor calls inside it, the host pass of hipcc emitted no
+            // launch stubs for this kernel template
+            const uint16_t* const src = lact(step) + t * lld(step) + col;
+            __builtin_amdgcn_global_load_lds(src, (QL_LDS void*)(sX + q * 512), 16, 0, 0);
         }
     };
 
@@ -231,10 +278,10 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     const int wrow = (DX && TPR == 8) ? (tid >> 6) * 8 + (((tid >> 5) & 1) << 2) + ((tid >> 2) & 3) : tid / TPR;
     const int wcol = ((DX && TPR == 8) ? (((tid >> 4) & 1) << 2) + (tid & 3) : tid % TPR) * CPT;
     auto gcodes = [&](int step, Codes<CC>& cs) {
-        const int64_t r0 = static_cast<int64_t>(step) * kStep;
+        const int64_t r0 = static_cast<int64_t>(lstep(step)) * kStep;
         int64_t e;
         if constexpr (DX) {
-            const int64_t n = min(r0 + wrow, p.N - 1);
+            const int64_t n = min(r0 + wrow, lred(step) - 1);
             e = n * p.K + min(m0 + wcol, p.K - CPT);
         } else {
             const int64_t n = min(m0 + wrow, p.N - 1);
@@ -243,21 +290,22 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         // block constant first, the CC code chunks last (the stage barrier
         // lets the last CC loads of a stage stay in flight)
         const int64_t b = e / 64;
+        const NF4Dev& w = lw(step);
         if constexpr (DQ) {
-            cs.bc.c8 = p.w.c8[b];
-            cs.bc.s = p.w.scale[b / QL_DQ_BLOCKSIZE];
+            cs.bc.c8 = w.c8[b];
+            cs.bc.s = w.scale[b / QL_DQ_BLOCKSIZE];
         } else {
             cs.bc.c8 = 0;
-            cs.bc.s = p.w.absmax[b];
+            cs.bc.s = w.absmax[b];
         }
 #pragma unroll
-        for (int cc = 0; cc < CC; ++cc) cs.c[cc] = ld16(p.w.packed + e / 2 + 16 * cc);
+        for (int cc = 0; cc < CC; ++cc) cs.c[cc] = ld16(w.packed + e / 2 + 16 * cc);
     };
 
     // ---- expand one step's codes into a weight stage -----------------------
     auto expand = [&](int step, const Codes<CC>& cs, uint16_t* sA) {
-        float a = block_value(cs.bc, DQ ? 1 : 0, mu);
-        if constexpr (DX) a = (static_cast<int64_t>(step) * kStep + wrow < p.N) ? a : 0.0f;
+        float a = block_value(cs.bc, DQ ? 1 : 0, lmu(step));
+        if constexpr (DX) a = (static_cast<int64_t>(lstep(step)) * kStep + wrow < lred(step)) ? a : 0.0f;
         const Lut16 L = make_lut(a);
         uint16_t* dst = sA + wrow * LDA;
 #pragma unroll
@@ -367,7 +415,52 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     //   step s:   token loads for s+1 -> the other stage; codes for s+2 -> the
     //             free register set; MFMAs on stage s; expand step s+1.
     Codes<CC> cs0, cs1;
-    if (sb < se) {
+    if constexpr (GRP) {
+        // A grouped dX: the same pipeline (dX form) over the part of [sb, se)
+        // each layer owns, layer by layer into the same accumulators; each
+        // part ends with every wave past a barrier after its last MFMA, so
+        // the stages are free for the next. (Kept apart from the one-layer
+        // text below, whose code it would otherwise change.)
+        for (int L = 0; L < p.ng; ++L) {
+            const int b = max(sb, p.gstep[L]), e = min(se, p.gstep[L + 1]);
+            if (b >= e) continue;
+            gw = p.gl[L].w;
+            gact = p.gl[L].act;
+            gN = p.gl[L].N;
+            gmu = DQ ? *p.gl[L].w.mean : 0.0f;
+            gbase = p.gstep[L];
+            dma(b, sX0);
+            gcodes(b, cs0);
+            gcodes(min(b + 1, e - 1), cs1);
+            expand(b, cs0, sA0);
+            __syncthreads();
+            for (int s = b; s < e; s += 2) {
+                dma(min(s + 1, e - 1), sX1);
+                __builtin_amdgcn_sched_barrier(0);
+                gcodes(min(s + 2, e - 1), cs0);
+                if (expand_first) {
+                    expand(s + 1, cs1, sA1);
+                    compute(sA0, sX0);
+                } else {
+                    compute(sA0, sX0);
+                    expand(s + 1, cs1, sA1);
+                }
+                stage_barrier<CC>();
+                if (s + 1 >= e) break;
+                dma(min(s + 2, e - 1), sX0);
+                __builtin_amdgcn_sched_barrier(0);
+                gcodes(min(s + 3, e - 1), cs1);
+                if (expand_first) {
+                    expand(s + 2, cs0, sA0);
+                    compute(sA1, sX1);
+                } else {
+                    compute(sA1, sX1);
+                    expand(s + 2, cs0, sA0);
+                }
+                stage_barrier<CC>();
+            }
+        }
+    } else if (sb < se) {
     dma(sb, sX0);
     gcodes(sb, cs0);
     gcodes(min(sb + 1, msteps - 1), cs1);
@@ -506,9 +599,16 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     };
 
     // LoRA term: rp/64 more reduction steps over the rank, staged directly
-    // (by the first split only).
-    for (int ls = 0; ls < (split == 0 ? p.rp / kStep : 0); ++ls) {
-        const int64_t j0 = static_cast<int64_t>(ls) * kStep;
+    // (by the first split only; in a grouped dX, each layer's by split
+    // L % splits: rank step ls of this split is step ls % nr of layer
+    // split + (ls / nr) splits).
+    const int nr = p.rp / kStep;
+    const int nls = GRP ? (split < p.ng ? nr * ((p.ng - 1 - split) / p.splits + 1) : 0) : (split == 0 ? nr : 0);
+    for (int ls = 0; ls < nls; ++ls) {
+        const int rl = GRP ? split + (ls / nr) * p.splits : 0;  // the rank step's layer
+        const uint16_t* const lt = GRP ? p.gl[rl].lt : p.lt;
+        const uint16_t* const la = GRP ? p.gl[rl].la : p.la;
+        const int64_t j0 = static_cast<int64_t>(GRP ? ls % nr : ls) * kStep;
         if (kUin && p.nu > 0) {
             stage_u_words();  // rp == 64: the one rank step
         } else {
@@ -517,7 +617,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                 const int c = tid + NTHR * i;
                 const int row = c >> 3, lc = c & 7;
                 const int64_t t = t0 + row;
-                const uint4 v = (t < p.T) ? ld16(p.lt + t * p.rp + j0 + 8 * lc) : make_uint4(0, 0, 0, 0);
+                const uint4 v = (t < p.T) ? ld16(lt + t * p.rp + j0 + 8 * lc) : make_uint4(0, 0, 0, 0);
                 st16(sX0 + row * kStep + 8 * (lc ^ swz(row)), v);
             }
         }
@@ -528,7 +628,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                 const int c = tid + NTHR * i;
                 const int64_t n = m0 + (c >> 3);
                 const int64_t j = j0 + 8 * (c & 7);
-                const uint4 v = (n < p.N && j < p.r_la) ? ld16(p.la + n * p.ld_la + j) : make_uint4(0, 0, 0, 0);
+                const uint4 v = (n < p.N && j < p.r_la) ? ld16(la + n * p.ld_la + j) : make_uint4(0, 0, 0, 0);
                 st16(sA0 + (c >> 3) * LDA + 8 * (c & 7), v);
             }
         } else {
@@ -539,7 +639,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                 const int row = c / (TA / 8), col = 8 * (c % (TA / 8));
                 const int64_t j = j0 + row;
                 const int64_t k = m0 + col;
-                const uint4 v = (j < p.r_la && k < p.K) ? ld16(p.la + j * p.ld_la + k) : make_uint4(0, 0, 0, 0);
+                const uint4 v = (j < p.r_la && k < p.K) ? ld16(la + j * p.ld_la + k) : make_uint4(0, 0, 0, 0);
                 st16(sA0 + row * LDA + dx_col(row, col), v);
             }
         }
@@ -640,10 +740,11 @@ __global__ void split_reduce_kernel(const float* __restrict__ part, int splits, 
     reinterpret_cast<uint2*>(out)[i] = o;
 }
 
-template <bool DX>
+// GRP: a grouped dX (a.ng layers, a.gstep set; a.w only gives the format).
+template <bool DX, bool GRP = false>
 int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStream_t stream, int nu = 0) {
     const int64_t MA = DX ? a.K : a.N;
-    const GemmPlan pl = plan_gemm(MA, a.T, DX ? a.N : a.K);
+    const GemmPlan pl = plan_gemm(MA, a.T, GRP ? int64_t{kStep} * a.gstep[a.ng] : (DX ? a.N : a.K));
     const int tile = pl.tile;
     a.tiles_a = static_cast<int>(ceil_div(MA, tile));
     a.tiles_t = static_cast<int>(ceil_div(a.T, tile));
@@ -658,14 +759,14 @@ int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStr
     timer_begin(kid, stream);
     if (tile == 256) {
         if (a.w.dq)
-            hipLaunchKernelGGL((tile_gemm_kernel<256, 256, 4, 2, DX, true>), grid, dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((tile_gemm_kernel<256, 256, 4, 2, DX, true, GRP>), grid, dim3(512), 0, stream, a);
         else
-            hipLaunchKernelGGL((tile_gemm_kernel<256, 256, 4, 2, DX, false>), grid, dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((tile_gemm_kernel<256, 256, 4, 2, DX, false, GRP>), grid, dim3(512), 0, stream, a);
     } else {
         if (a.w.dq)
-            hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, true, GRP>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, false>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, false, GRP>), grid, dim3(256), 0, stream, a);
     }
     if (a.splits > 1) {
         const int64_t n4 = a.T * MA / 4;
@@ -853,6 +954,32 @@ int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, cons
     a.N = N;
     a.K = K;
     return launch_tiles<true>(a, split_ws, QL_KERNEL_GEMM_DX, "dequant GEMM dX", stream);
+}
+
+int64_t gemm_group_steps(const int64_t* N, int ng) {
+    int64_t st = 0;
+    for (int i = 0; i < ng; ++i) st += ceil_div(N[i], kStep);
+    return st;
+}
+
+int launch_gemm_dx_group(const GemmLayer* layers, int ng, int r, int rp, uint16_t* dX, int64_t T, int64_t K,
+                         float* split_ws, hipStream_t stream) {
+    if (ng < 1 || ng > kGemmMaxGroup) return set_error(QL_ERR_SHAPE, "grouped dX: %d layers", ng);
+    TileArgs a{};
+    a.w = layers[0].w;  // the format; every layer has the same
+    a.ng = ng;
+    a.gstep[0] = 0;
+    for (int i = 0; i < ng; ++i) {
+        a.gl[i] = layers[i];
+        a.gstep[i + 1] = a.gstep[i] + static_cast<int>(ceil_div(layers[i].N, kStep));
+    }
+    a.ld_la = K;
+    a.r_la = r;
+    a.rp = rp;
+    a.out = dX;
+    a.T = T;
+    a.K = K;
+    return launch_tiles<true, true>(a, split_ws, QL_KERNEL_GEMM_DX, "grouped dequant GEMM dX", stream);
 }
 
 }  // namespace qlnf4

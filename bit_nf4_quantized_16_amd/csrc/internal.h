@@ -162,6 +162,24 @@ int launch_gemm_fwd_u(const NF4Dev& w, const uint16_t* X, const uint16_t* A, con
                       uint16_t* Y, float* U_out, int64_t T, int64_t N, int64_t K, uint64_t* words, hipStream_t stream);
 int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, const uint16_t* A, int r, int rp,
                    uint16_t* dX, int64_t T, int64_t N, int64_t K, float* split_ws, hipStream_t stream);
+// dX = sum over ng layers that read the same X of dY_L W_L' + G_L A_L, one
+// GEMM launch (+ the split reduce): the layers' rows are one reduction of
+// gemm_group_steps(N, ng) 64-row steps, planned as plan_gemm(K, T, 64 x
+// steps) plans one layer's. Every layer has the same format (double
+// quantization or not), rank r and padded rank rp.
+constexpr int kGemmMaxGroup = 4;
+// One layer of a grouped dX launch: its weight, dY [T, N] (row stride N),
+// G [T, rp] bf16 (lt) and A [r, K] (la, row stride K).
+struct GemmLayer {
+    NF4Dev w;
+    const uint16_t* act;
+    int64_t N;
+    const uint16_t* lt;
+    const uint16_t* la;
+};
+int64_t gemm_group_steps(const int64_t* N, int ng);
+int launch_gemm_dx_group(const GemmLayer* layers, int ng, int r, int rp, uint16_t* dX, int64_t T, int64_t K,
+                         float* split_ws, hipStream_t stream);
 
 int lora_grad_rp(int r);         // rank rounded up to 16
 int64_t lora_vt_ld(int64_t T);  // row stride of the transposed [rp16, T] operands

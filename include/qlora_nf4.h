@@ -409,6 +409,44 @@ int qlora_linear_bwd(const ql_nf4_weight* w, const uint16_t* X, const uint16_t* 
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qlora_linear_bwd_group — qlora_linear_bwd for up to four layers that read
+ * the same input X (q/k/v, or gate/up: [aivaro] §10 puts adapters on these
+ * projections), whose input gradients add up ([aivaro] §7: the gradient
+ * flows through each dequantized weight to X):
+ *
+ *   dX     optional out [T, K] bf16 = sum over layers i of dY_i W_i' + G_i A_i,
+ *          G_i = s dY_i B_i, summed in fp32 and rounded to bf16 once
+ *   dA[i]  optional out [r, K] fp32 = G_i^T X      (as qlora_linear_bwd)
+ *   dB[i]  optional out [N_i, r] fp32 = s dY_i^T U_i
+ *
+ *   w, dY, A, B, U_saved, dA, dB  host arrays of nw pointers, per layer as in
+ *          qlora_linear_bwd (A and B may be NULL when r == 0; U_saved, dA and
+ *          dB may be NULL, or hold NULL entries, to skip them)
+ *   nw     1..4 layers; all share K = w[i]->cols, r, scale and the format
+ *          (all with double quantization or all without)
+ *   ws     workspace of qlora_linear_bwd_group_workspace(rows, nw, K, T, r)
+ *          bytes, rows = the nw values w[i]->rows
+ *
+ * dX runs as one dequant GEMM launch whose reduction walks the layers' rows
+ * one after another (plus, when the plan splits that reduction, one pass
+ * adding the fp32 partials): one launch and one rounding instead of nw, and
+ * at T = 1024 the split reductions of gate and up share one partial set.
+ * With nw == 1 dX is bitwise qlora_linear_bwd's. Each layer's G runs in a
+ * projection launch before it; dA[i] and dB[i] are bitwise those of
+ * qlora_linear_bwd for layer i. K must be a multiple of 64 and each N_i a
+ * multiple of 8. Outputs must not alias inputs or one another.
+ * Errors: as qlora_linear_bwd, plus QL_ERR_SHAPE for nw outside 1..4 or
+ * layers of different K, QL_ERR_UNSUPPORTED for a group mixing formats; the
+ * workspace query returns 0 for invalid sizes.
+ */
+size_t qlora_linear_bwd_group_workspace(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r);
+int qlora_linear_bwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X,
+                           const uint16_t* const* dY, int64_t T, const uint16_t* const* A,
+                           const uint16_t* const* B, int32_t r, float scale, const float* const* U_saved,
+                           uint16_t* dX, float* const* dA, float* const* dB, int accumulate, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * qlora_linear_bwd_dropout — the backward of qlora_linear_fwd_dropout with
  * the same keep mask and p ([codex] §3.4):
  *

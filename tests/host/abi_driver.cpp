@@ -173,6 +173,26 @@ int main() {
     EXPECT(qlora_linear_fwd_group(gwp, 0, P, 1, As, Bs, 16, 2.0f, Ys, Us, WS, 1 << 20, nullptr) == QL_ERR_SHAPE);
     EXPECT(qlora_linear_fwd_group(nullptr, 3, P, 1, As, Bs, 16, 2.0f, Ys, Us, WS, 1 << 20, nullptr) == QL_ERR_NULL);
 
+    // grouped backward: the summed dX of layers that share X, dA and dB per layer
+    const int64_t rows2[2] = {11008, 11008};
+    ql_nf4_weight bw[2] = {weight(11008, 4096, 1), weight(11008, 4096, 1)};
+    const ql_nf4_weight* bwp[2] = {&bw[0], &bw[1]};
+    const uint16_t* dYs[2] = {P, P};
+    const float* Usv[2] = {F, nullptr};
+    float* dAs[2] = {F, F};
+    float* dBs[2] = {F, nullptr};
+    for (int64_t T : {64, 1024, 4096}) {
+        const size_t bws = qlora_linear_bwd_group_workspace(rows2, 2, 4096, T, 16);
+        EXPECT(bws > 0);
+        EXPECT(launch_stop(
+            qlora_linear_bwd_group(bwp, 2, P, dYs, T, As, Bs, 16, 2.0f, Usv, P, dAs, dBs, 0, WS, bws, nullptr)));
+    }
+    EXPECT(qlora_linear_bwd_group_workspace(rows2, 5, 4096, 64, 16) == 0);
+    EXPECT(qlora_linear_bwd_group(bwp, 5, P, dYs, 64, As, Bs, 16, 2.0f, Usv, P, dAs, dBs, 0, WS, 1 << 30, nullptr) ==
+           QL_ERR_SHAPE);
+    EXPECT(qlora_linear_bwd_group(bwp, 2, P, nullptr, 64, As, Bs, 16, 2.0f, Usv, P, dAs, dBs, 0, WS, 1 << 30,
+                                  nullptr) == QL_ERR_NULL);
+
     // optimizer: rejected arguments (the state's memory type is asked of the
     // runtime only after these)
     EXPECT(qlora_paged_adamw(F, nullptr, F, F, F, 0, 1, 2e-4f, 0.9f, 0.999f, 1e-8f, 0.0f, nullptr, 0, nullptr,

@@ -356,6 +356,67 @@ def test_linear_bwd_rejects(lib):
     assert call(dX=None, dA=None, dB=None) == L.QL_OK  # nothing requested
 
 
+def test_linear_bwd_group_rejects(lib):
+    from bit_nf4_quantized_16_amd import _lib as L
+
+    def descs(shapes, dq=256):
+        ws = []
+        for rows, cols in shapes:
+            w = L.QlNf4Weight()
+            w.rows, w.cols, w.blocksize, w.dq_blocksize = rows, cols, 64, dq
+            w.packed, w.absmax, w.c8, w.dq_scale, w.dq_mean = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+            ws.append(w)
+        return ws
+
+    def ptrs(vals, n):
+        return (ctypes.c_void_p * max(n, 1))(*vals)
+
+    def rows(*r):
+        return (ctypes.c_int64 * len(r))(*r)
+
+    # G of every layer, one set of gradient operands, the summed dX's split
+    # partials: more than the largest single-layer workspace, less than the sum
+    one = [lib.qlora_linear_bwd_workspace(n, 4096, 1024, 16) for n in (11008, 11008)]
+    grp = lib.qlora_linear_bwd_group_workspace(rows(11008, 11008), 2, 4096, 1024, 16)
+    assert max(one) < grp < sum(one) + 2 * 1024 * 64 * 2
+    assert lib.qlora_linear_bwd_group_workspace(rows(256), 0, 256, 16, 8) == 0
+    assert lib.qlora_linear_bwd_group_workspace(rows(*[256] * 5), 5, 256, 16, 8) == 0
+    assert lib.qlora_linear_bwd_group_workspace(rows(256, 0), 2, 256, 16, 8) == 0
+    assert lib.qlora_linear_bwd_group_workspace(None, 1, 256, 16, 8) == 0
+    assert lib.qlora_linear_bwd_group_workspace(rows(256), 1, 256, 16, 129) == 0
+
+    def call(shapes=((256, 256), (512, 256)), nw=None, T=64, r=8, X=P, dY=P2, A=True, B=True, U=False, dX=P,
+             dA=True, dB=True, acc=0, wsb=None, ws=P, dq=(256, 256)):
+        ds = []
+        for sh, q in zip(shapes, dq + (256,) * len(shapes)):
+            ds += descs((sh,), q)
+        n = len(ds) if nw is None else nw
+        wp = ptrs([ctypes.addressof(d) for d in ds], len(ds))
+        need = lib.qlora_linear_bwd_group_workspace(rows(*[d.rows for d in ds]), len(ds), ds[0].cols, T, r)
+        arr = lambda v: ptrs([v] * len(ds), len(ds))
+        return lib.qlora_linear_bwd_group(wp, n, X, arr(dY), T, arr(P3) if A else None, arr(P) if B else None, r,
+                                          2.0, arr(P2) if U else None, dX, arr(P2) if dA else None,
+                                          arr(P3) if dB else None, acc, ws, need if wsb is None else wsb, None)
+
+    assert call(nw=0) == L.QL_ERR_SHAPE
+    assert call(shapes=((256, 256),) * 5) == L.QL_ERR_SHAPE
+    assert call(shapes=((256, 256), (256, 320))) == L.QL_ERR_SHAPE  # layers of different K
+    assert call(shapes=((256, 256), (100, 256))) == L.QL_ERR_SHAPE  # N % 8
+    assert call(dq=(256, 0)) == L.QL_ERR_UNSUPPORTED  # formats mixed
+    assert call(r=129) == L.QL_ERR_SHAPE
+    assert call(r=0, A=False, B=False) == L.QL_ERR_SHAPE  # dA/dB requested without adapters
+    assert call(acc=2) == L.QL_ERR_UNSUPPORTED
+    assert call(A=False) == L.QL_ERR_NULL
+    assert call(dY=None) == L.QL_ERR_NULL
+    assert call(X=None) == L.QL_ERR_NULL  # dA needs X
+    assert call(dX=MIS) == L.QL_ERR_ALIGN
+    assert call(wsb=0) == L.QL_ERR_WORKSPACE
+    assert call(T=0) == L.QL_OK
+    assert call(dX=None, dA=False, dB=False) == L.QL_OK  # nothing requested
+    assert lib.qlora_linear_bwd_group(None, 1, P, None, 4, None, None, 0, 1.0, None, P, None, None, 0, None, 0,
+                                      None) == L.QL_ERR_NULL
+
+
 def test_merge_rejects(lib):
     from bit_nf4_quantized_16_amd import _lib as L
 
