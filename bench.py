@@ -105,6 +105,9 @@ class Inputs:
         self.A_attn, self.B_attn = attn.A.cuda(), attn.B.cuda()
         self.s_attn = attn.scale
         self.mlp = [workloads.mlp_7b(w, T=1024, seed=2) for w in ("gate", "up", "down")]
+        # gate and up read the same activations, the MLP's input, as in the
+        # model: their input gradients add up, in one grouped backward
+        self.mlp[1].X = self.mlp[0].X
         self.mlp_dev = []
         for c in self.mlp:
             self.mlp_dev.append(dict(W=c.W.cuda(), X=c.X.cuda(), dY=c.dY.cuda(), A=c.A.cuda(), B=c.B.cuda(),
@@ -112,7 +115,10 @@ class Inputs:
 
 
 def run_step(qn, inp):
-    """One pass of the whole path. Returns nothing; results stay on device."""
+    """One pass of the whole path. Returns nothing; results stay on device.
+    The MLP: forward of gate, up and down; backward of down, then of gate
+    and up together (they read the same X: one grouped call gives their
+    summed dX and each one's dA, dB)."""
     wa = qn.quantize_weight(inp.W_attn)
     qn.nf4_dequantize(wa)
     wm = [qn.quantize_weight(m["W"]) for m in inp.mlp_dev]
@@ -120,9 +126,11 @@ def run_step(qn, inp):
     # through the caches, so the attention weight is read from HBM
     qn.qlora_linear_fwd(wa, inp.X1, inp.A_attn, inp.B_attn, inp.s_attn)
     qn.qlora_linear_fwd(wa, inp.X16, inp.A_attn, inp.B_attn, inp.s_attn)
-    for w, m in zip(wm, inp.mlp_dev):
-        _, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
-        qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U)
+    Us = [qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])[1] for w, m in zip(wm, inp.mlp_dev)]
+    gate, up, down = inp.mlp_dev
+    qn.qlora_linear_bwd(wm[2], down["X"], down["dY"], down["A"], down["B"], down["s"], U=Us[2])
+    qn.qlora_linear_bwd_group(wm[:2], gate["X"], [gate["dY"], up["dY"]], [gate["A"], up["A"]], [gate["B"], up["B"]],
+                              gate["s"], Us=Us[:2])
 
 
 def run_step_streams(torch, qn, inp, side):
@@ -138,13 +146,15 @@ def run_step_streams(torch, qn, inp, side):
     MB of a 256 MB last-level cache); moving them behind the MLP weights'
     quantization, as in run_step, made the replayed step 8 % slower (the
     GEMVs then wait for CUs behind the split-K GEMMs).
-    Each backward is two calls of the library: dX on the current stream
-    right after the forward, and dA, dB (the adapter gradients need G^T, X,
-    dY and the forward's U, not dX) on the side stream once the forward is
-    done, so the gradient kernel overlaps the next GEMM instead of following
-    the dX GEMM. The side call forms G again with its own projection (the
-    ideal step counts it once); the outputs are those of run_step, bit for
-    bit (measured 3-4 % faster per replayed step than one backward call)."""
+    Each backward is two calls of the library: dX on the current stream, and
+    dA, dB (the adapter gradients need G^T, X, dY and the forward's U, not
+    dX) on the side stream once the forward is done, so the gradient kernel
+    overlaps the next GEMM instead of following the dX GEMM. The side call
+    forms G again with its own projection (the ideal step counts it once);
+    the outputs are those of run_step, bit for bit (measured 3-4 % faster
+    per replayed step than one backward call). Gate and up take their
+    backward together (one grouped dX call, their dA and dB in one grouped
+    side call), after down's, as in run_step."""
     main = torch.cuda.current_stream()
     side.wait_stream(main)
     ready = []
@@ -159,17 +169,27 @@ def run_step_streams(torch, qn, inp, side):
         qn.nf4_dequantize(wa)
         qn.qlora_linear_fwd(wa, inp.X1, inp.A_attn, inp.B_attn, inp.s_attn)
         qn.qlora_linear_fwd(wa, inp.X16, inp.A_attn, inp.B_attn, inp.s_attn)
-    outs = []
+    outs, fw = [], []
     for w, m, ev in zip(wm, inp.mlp_dev, ready):
         main.wait_event(ev)
         Y, U = qn.qlora_linear_fwd(w, m["X"], m["A"], m["B"], m["s"])
         done = torch.cuda.Event()
         done.record(main)
-        dX, _, _ = qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_da=False, need_db=False)
-        side.wait_event(done)
-        with torch.cuda.stream(side):
-            _, dA, dB = qn.qlora_linear_bwd(w, m["X"], m["dY"], m["A"], m["B"], m["s"], U=U, need_dx=False)
-        outs.append((Y, U, dX, dA, dB))
+        fw.append((Y, U, done))
+    gate, up, down = inp.mlp_dev
+    (Yg, Ug, _), (Yu, Uu, done_gu), (Yd, Ud, done_d) = fw
+    dX, _, _ = qn.qlora_linear_bwd(wm[2], down["X"], down["dY"], down["A"], down["B"], down["s"], U=Ud, need_da=False,
+                                   need_db=False)
+    side.wait_event(done_d)
+    with torch.cuda.stream(side):
+        _, dA, dB = qn.qlora_linear_bwd(wm[2], down["X"], down["dY"], down["A"], down["B"], down["s"], U=Ud,
+                                        need_dx=False)
+    grp = (wm[:2], gate["X"], [gate["dY"], up["dY"]], [gate["A"], up["A"]], [gate["B"], up["B"]], gate["s"])
+    dXgu, _, _ = qn.qlora_linear_bwd_group(*grp, Us=[Ug, Uu], need_da=False, need_db=False)
+    side.wait_event(done_gu)
+    with torch.cuda.stream(side):
+        _, dAs, dBs = qn.qlora_linear_bwd_group(*grp, Us=[Ug, Uu], need_dx=False)
+    outs = [(Yg, Ug, Yu, Uu, dXgu, dAs[0], dBs[0], dAs[1], dBs[1]), (Yd, Ud, dX, dA, dB)]
     main.wait_stream(side)
     return outs
 
@@ -229,14 +249,17 @@ def per_launch_work(qn, inp):
     over the step's launches of it (the per-kernel timers come from eager
     steps: there U = X A^T runs inside the forward GEMM launch, and
     G = s dY B inside the dX GEMM launch, where the library says so, else in
-    a separate projection launch)."""
+    a separate projection launch). The dX of gate and up is one grouped
+    launch (its G projections run apart)."""
     fwd, dx = [], []
     for m in inp.mlp_dev:
         N, K, T, r = m["N"], m["K"], m["T"], m["r"]
         u_in = qn.lib.qlora_linear_fwd_u_in_launch(N, K, T, r)
-        g_in = qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r)
         fwd.append(fwd_flops(N, K, T, r) - (0 if u_in else 2 * T * K * r))
-        dx.append(dx_flops(N, K, T, r) - (0 if g_in else 2 * T * N * r))
+    gate, up, down = inp.mlp_dev
+    dx.append(sum(dx_flops(m["N"], m["K"], m["T"], m["r"]) - 2 * m["T"] * m["N"] * m["r"] for m in (gate, up)))
+    N, K, T, r = down["N"], down["K"], down["T"], down["r"]
+    dx.append(dx_flops(N, K, T, r) - (0 if qn.lib.qlora_linear_bwd_g_in_launch(N, K, T, r) else 2 * T * N * r))
     return {
         "gemm_fwd": ("mfma", sum(fwd) / len(fwd), "TFLOP/s"),
         "gemm_dx": ("mfma", sum(dx) / len(dx), "TFLOP/s"),
