@@ -127,6 +127,80 @@ def test_two_stream_graph_matches_serial(qn, split_bwd):
             assert torch.equal(a, b), "replay %d: output %d differs from the serial run" % (rep, i)
 
 
+def test_two_stream_graph_with_grouped_backward(qn):
+    # the benchmark's step shape: three layers, the first two reading the same
+    # X; weights quantized on the second stream, forwards on the first, then
+    # the third layer's backward and the first two's grouped backward (dX on
+    # the first stream, dA and dB by a second call on the other), captured
+    # and replayed against the same calls made serially on one stream
+    Ws = [workloads.normal_weight(n, 2048, 0.02, seed=50 + i).cuda() for i, n in enumerate((1024, 1024, 512))]
+    cases = [workloads.lora_case("g%d" % i, W.cpu(), 96, 16, 32.0, 1 / 2048, 0.05, seed=50 + i)
+             for i, W in enumerate(Ws)]
+    X = cases[0].X.cuda()
+    dYs = [c.dY.cuda() for c in cases]
+    As = [c.A.cuda() for c in cases]
+    Bs = [c.B.cuda() for c in cases]
+    s = cases[0].scale
+
+    def serial():
+        ws = [qn.quantize_weight(W) for W in Ws]
+        fw = [qn.qlora_linear_fwd(w, X, As[i], Bs[i], s) for i, w in enumerate(ws)]
+        outs = [t for Y, U in fw for t in (Y, U)]
+        outs += list(qn.qlora_linear_bwd(ws[2], X, dYs[2], As[2], Bs[2], s, U=fw[2][1]))
+        dX, dA, dB = qn.qlora_linear_bwd_group(ws[:2], X, dYs[:2], As[:2], Bs[:2], s, Us=[fw[0][1], fw[1][1]])
+        return outs + [dX, *dA, *dB]
+
+    side = torch.cuda.Stream()
+
+    def two_streams():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        ws, evs = [], []
+        with torch.cuda.stream(side):
+            for W in Ws:
+                ws.append(qn.quantize_weight(W))
+                ev = torch.cuda.Event()
+                ev.record(side)
+                evs.append(ev)
+        fw = []
+        for i, (w, ev) in enumerate(zip(ws, evs)):
+            main.wait_event(ev)
+            Y, U = qn.qlora_linear_fwd(w, X, As[i], Bs[i], s)
+            done = torch.cuda.Event()
+            done.record(main)
+            fw.append((Y, U, done))
+        dX2, _, _ = qn.qlora_linear_bwd(ws[2], X, dYs[2], As[2], Bs[2], s, U=fw[2][1], need_da=False, need_db=False)
+        side.wait_event(fw[2][2])
+        with torch.cuda.stream(side):
+            _, dA2, dB2 = qn.qlora_linear_bwd(ws[2], X, dYs[2], As[2], Bs[2], s, U=fw[2][1], need_dx=False)
+        grp = (ws[:2], X, dYs[:2], As[:2], Bs[:2], s)
+        Us = [fw[0][1], fw[1][1]]
+        dX, _, _ = qn.qlora_linear_bwd_group(*grp, Us=Us, need_da=False, need_db=False)
+        side.wait_event(fw[1][2])
+        with torch.cuda.stream(side):
+            _, dA, dB = qn.qlora_linear_bwd_group(*grp, Us=Us, need_dx=False)
+        main.wait_stream(side)
+        return [t for Y, U, _ in fw for t in (Y, U)] + [dX2, dA2, dB2, dX, *dA, *dB]
+
+    ref = [t.clone() for t in serial()]
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
+        two_streams()
+    torch.cuda.current_stream().wait_stream(warm)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = two_streams()
+    for rep in range(3):
+        qn.quantize_weight(Ws[1])  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), "replay %d: output %d differs from the serial run" % (rep, i)
+
+
 @pytest.mark.parametrize("spin", [None, "1"])
 @pytest.mark.parametrize("T", [1, 16])
 def test_decode_graph_replays_with_new_inputs(qn, monkeypatch, T, spin):
