@@ -80,6 +80,7 @@ SIGNATURES = {
     "qlora_linear_fwd": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_noalloc": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _P, _P]),
     "qlora_linear_fwd_group_workspace": (_SZ, [_P, _I32, _I64, _I64, _I32]),
+    "qlora_linear_fwd_group_one_launch": (_I32, [_P, _I32, _I64, _I64, _I32]),
     "qlora_linear_fwd_group": (_I, [_P, _I32, _P, _I64, _P, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "qlora_linear_fwd_dropout_workspace": (_SZ, [_I64, _I64, _I64, _I32]),
     "qlora_linear_fwd_dropout": (_I, [_WP, _P, _I64, _P, _P, _I32, _F, _P, _F, _P, _P, _P, _SZ, _P]),

@@ -492,6 +492,37 @@ int linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const uint1
     return launch_gemm_fwd(wd, X, f.Us, Bsrc, ld_b, r_b, rp, Y, T, N, K, f.split, st);
 }
 
+// A grouped forward at T > 16 takes one GEMM launch over all layers' row
+// tiles when r is a multiple of 8 (B's rows 16-byte aligned) and the plan
+// says it beats the layers' own launches; otherwise the layers run one
+// after another.
+bool fwd_group_one_launch(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
+    return T > kGemvMaxT && r % 8 == 0 && gemm_fwd_group_pays(rows, nw, T, cols);
+}
+
+// Its workspace: bf16(s U_i) per layer, the U projection's partials, the
+// GEMM's split partials.
+struct FwdGroupWs {
+    uint16_t* Us[kGemmMaxGroup] = {};
+    void* proj = nullptr;
+    float* split = nullptr;
+    size_t bytes = 0;
+};
+
+FwdGroupWs carve_fwd_group(void* ws, const int64_t* rows, int32_t nw, int64_t K, int64_t T, int32_t r) {
+    Carver c(ws);
+    FwdGroupWs f;
+    if (r > 0) {
+        for (int i = 0; i < nw; ++i) f.Us[i] = c.take<uint16_t>(static_cast<size_t>(T) * rank_pad64(r));
+        const size_t pb = lora_proj_ws_bytes(T, r, K, false);
+        if (pb) f.proj = c.take<char>(pb);
+    }
+    const size_t sb = gemm_fwd_group_split_bytes(rows, nw, T, K);
+    if (sb) f.split = c.take<float>(sb / sizeof(float));
+    f.bytes = align_up(c.off, 256);
+    return f;
+}
+
 size_t group_fwd_ws(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
     if (rows == nullptr || nw < 1 || nw > kGemvMaxGroup || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
     size_t m = 0;
@@ -499,9 +530,11 @@ size_t group_fwd_ws(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, in
         if (rows[i] <= 0) return 0;
         m = std::max(m, carve_fwd(nullptr, rows[i], cols, T, r).bytes);
     }
-    // decode: one launch, a workspace slice per weight; larger T: the weights
-    // one after another, sharing one workspace
-    return T <= kGemvMaxT ? static_cast<size_t>(nw) * gemv_ws_bytes(T, cols, r) : m;
+    // decode: one launch, a workspace slice per weight; larger T: one GEMM
+    // launch over all weights, or the weights one after another sharing one
+    // workspace
+    if (T <= kGemvMaxT) return static_cast<size_t>(nw) * gemv_ws_bytes(T, cols, r);
+    return fwd_group_one_launch(rows, nw, cols, T, r) ? carve_fwd_group(nullptr, rows, nw, cols, T, r).bytes : m;
 }
 
 int linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,
@@ -532,12 +565,50 @@ int linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* 
     if (T == 0) return QL_OK;
     if ((s = check_ptr(X, "X")) != QL_OK) return s;
     const int64_t K = w[0]->cols;
-    if (T > kGemvMaxT) {
+    bool same_format = true;
+    for (int i = 1; i < nw; ++i) same_format = same_format && (w[i]->dq_blocksize != 0) == (w[0]->dq_blocksize != 0);
+    if (T > kGemvMaxT && !(same_format && fwd_group_one_launch(rows, nw, K, T, r))) {
         for (int i = 0; i < nw; ++i)
             if ((s = linear_fwd(w[i], X, T, r > 0 ? A[i] : nullptr, r > 0 ? B[i] : nullptr, r, scale, nullptr, 0.0f,
                                 Y[i], (r > 0 && U_out != nullptr) ? U_out[i] : nullptr, ws, ws_bytes, stream)) != QL_OK)
                 return s;
         return QL_OK;
+    }
+    if (T > kGemvMaxT) {
+        // one GEMM launch over all layers' row tiles, after each layer's U
+        // projection (fp32 U for the caller, bf16(s U) for the rank step)
+        const FwdGroupWs f = carve_fwd_group(ws, rows, nw, K, T, r);
+        if (f.bytes > 0) {
+            if (ws == nullptr || ws_bytes < f.bytes)
+                return set_error(QL_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws == nullptr ? 0 : ws_bytes,
+                                 f.bytes);
+            if (!aligned16(ws)) return set_error(QL_ERR_ALIGN, "workspace is not 16-byte aligned");
+        }
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        const int rp = rank_pad64(r);
+        GemmLayer layers[kGemmMaxGroup];
+        for (int i = 0; i < nw; ++i) {
+            if (r > 0) {
+                ProjArgs a{};
+                a.proj = 1;
+                a.P = X;
+                a.ldp = K;
+                a.Q = A[i];
+                a.ldq = K;
+                a.rq = r;
+                a.T = T;
+                a.kred = K;
+                a.alpha_f = 1.0f;
+                a.out_f = U_out != nullptr ? U_out[i] : nullptr;
+                a.ld_f = r;
+                a.alpha_b = scale;
+                a.out_b = f.Us[i];
+                a.ld_b = rp;
+                if ((s = launch_lora_proj(a, false, f.proj, st)) != QL_OK) return s;
+            }
+            layers[i] = GemmLayer{to_dev(w[i]), nullptr, rows[i], r > 0 ? f.Us[i] : nullptr, r > 0 ? B[i] : nullptr, Y[i]};
+        }
+        return launch_gemm_fwd_group(layers, nw, X, r, rp, T, K, f.split, st);
     }
     const size_t need = group_fwd_ws(rows, nw, K, T, r);
     if (need > 0) {
@@ -791,7 +862,8 @@ int linear_bwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* 
     if (want_dx) {
         GemmLayer layers[kGemmMaxGroup];
         for (int i = 0; i < nw; ++i)
-            layers[i] = GemmLayer{to_dev(w[i]), dY[i], rows[i], r > 0 ? b.Gp[i] : nullptr, r > 0 ? A[i] : nullptr};
+            layers[i] = GemmLayer{to_dev(w[i]), dY[i], rows[i], r > 0 ? b.Gp[i] : nullptr, r > 0 ? A[i] : nullptr,
+                                  nullptr};
         if ((s = launch_gemm_dx_group(layers, nw, r, rp, dX, T, K, b.split, st)) != QL_OK) return s;
     }
     return QL_OK;
@@ -808,6 +880,13 @@ int qlora_linear_fwd(const ql_nf4_weight* w, const uint16_t* X, int64_t T, const
 
 size_t qlora_linear_fwd_group_workspace(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
     return group_fwd_ws(rows, nw, cols, T, r);
+}
+
+int qlora_linear_fwd_group_one_launch(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r) {
+    if (rows == nullptr || nw < 1 || nw > kGemvMaxGroup || cols <= 0 || T <= 0 || r < 0 || r > QL_MAX_RANK) return 0;
+    for (int i = 0; i < nw; ++i)
+        if (rows[i] <= 0) return 0;
+    return fwd_group_one_launch(rows, nw, cols, T, r) ? 1 : 0;
 }
 
 int qlora_linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,

@@ -77,6 +77,12 @@ struct TileArgs {
     int ng;
     int gstep[kGemmMaxGroup + 1];
     GemmLayer gl[kGemmMaxGroup];
+    // Grouped forward (the GRP kernels with DX false): Y_L = X W_L'^T +
+    // Us_L B_L^T for ng layers that read the same X. Layer L owns row tiles
+    // [gtile[L], gtile[L + 1]) of the tiles_a; its split partials sit at
+    // columns gcol[L] .. of a [splits, T, gcol[ng]] buffer.
+    int gtile[kGemmMaxGroup + 1];
+    int64_t gcol[kGemmMaxGroup + 1];
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -149,7 +155,6 @@ struct Codes {
 
 template <int TA, int TT, int WA, int WT, bool DX, bool DQ, bool GRP>
 __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_kernel(TileArgs p) {
-    static_assert(!GRP || DX, "grouped launches run dX");
     using S = TileShape<TA, TT, WA, WT, DX>;
     constexpr int SA = S::SA, ST = S::ST, CPT = S::CPT, CC = S::CC, LDA = S::LDA, TPR = S::TPR;
     constexpr int MW = S::MW, TW = S::TW, NW = S::NW, NTHR = S::NTHR;
@@ -201,11 +206,18 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     // activation rows to all its workgroups.
     const int g = static_cast<int>(blockIdx.x) - p.nu, qx = ntiles / 8, rem = ntiles % 8, x = g % 8;
     const int logical = x * qx + (x < rem ? x : rem) + g / 8;
-    const int64_t m0 = static_cast<int64_t>(logical % p.tiles_a) * TA;
+    // a grouped forward: the layer owning this row tile, and the tile's
+    // rows within it
+    int fl = 0;
+    if constexpr (GRP && !DX) {
+#pragma unroll
+        for (int i = 1; i < kGemmMaxGroup; ++i) fl += (i < p.ng && logical % p.tiles_a >= p.gtile[i]) ? 1 : 0;
+    }
+    const int64_t m0 = static_cast<int64_t>(logical % p.tiles_a - ((GRP && !DX) ? p.gtile[fl] : 0)) * TA;
     const int64_t t0 = static_cast<int64_t>(logical / p.tiles_a) * TT;
-    const int64_t MA = DX ? p.K : p.N;
+    const int64_t MA = DX ? p.K : ((GRP && !DX) ? p.gl[fl].N : p.N);
     const int64_t RED = DX ? p.N : p.K;
-    const int nsteps_all = GRP ? p.gstep[p.ng] : static_cast<int>(ceil_div(RED, kStep));
+    const int nsteps_all = (GRP && DX) ? p.gstep[p.ng] : static_cast<int>(ceil_div(RED, kStep));
     // split-K: this workgroup covers reduction steps [sb, se)
     const int split = blockIdx.y;
     const int spp = (nsteps_all + p.splits - 1) / p.splits;
@@ -246,6 +258,12 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         if constexpr (GRP) return gmu;
         else return mu;
     };
+    if constexpr (GRP && !DX) {  // a grouped forward binds its tile's layer once (X, K are shared)
+        gw = p.gl[fl].w;
+        gact = p.act;
+        gN = p.K;
+        gmu = DQ ? *p.gl[fl].w.mean : 0.0f;
+    }
 
     // ---- token tile: direct loads into LDS --------------------------------
     // Wave w issues loads q = NW i + w (i < DMA); load q fills rows 8q..8q+7.
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
             const int64_t n = min(r0 + wrow, lred(step) - 1);
             e = n * p.K + min(m0 + wcol, p.K - CPT);
         } else {
-            const int64_t n = min(m0 + wrow, p.N - 1);
+            const int64_t n = min(m0 + wrow, MA - 1);
             e = n * p.K + r0 + wcol;
         }
         // block constant first, the CC code chunks last (the stage barrier
@@ -372,7 +390,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     // keeps (its A operands take two transposing reads each, and the fused
     // form measured slower there).
     auto compute_expand = [&](const uint16_t* sA, const uint16_t* sX, const Codes<CC>& cs, uint16_t* sAo) {
-        const Lut16 L = make_lut(block_value(cs.bc, DQ ? 1 : 0, mu));
+        const Lut16 L = make_lut(block_value(cs.bc, DQ ? 1 : 0, lmu(0)));
         uint16_t* dst = sAo + wrow * LDA + wcol;
         constexpr int NQ = CC * 4, PER = NQ / (kStep / 16);  // 8-code words per slice
         static_assert(NQ % (kStep / 16) == 0, "expansion split over the slices");
@@ -415,7 +433,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     //   step s:   token loads for s+1 -> the other stage; codes for s+2 -> the
     //             free register set; MFMAs on stage s; expand step s+1.
     Codes<CC> cs0, cs1;
-    if constexpr (GRP) {
+    if constexpr (GRP && DX) {
         // A grouped dX: the same pipeline (dX form) over the part of [sb, se)
         // each layer owns, layer by layer into the same accumulators; each
         // part ends with every wave past a barrier after its last MFMA, so
@@ -603,12 +621,13 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     // L % splits: rank step ls of this split is step ls % nr of layer
     // split + (ls / nr) splits).
     const int nr = p.rp / kStep;
-    const int nls = GRP ? (split < p.ng ? nr * ((p.ng - 1 - split) / p.splits + 1) : 0) : (split == 0 ? nr : 0);
+    constexpr bool kGdx = GRP && DX, kGfwd = GRP && !DX;
+    const int nls = kGdx ? (split < p.ng ? nr * ((p.ng - 1 - split) / p.splits + 1) : 0) : (split == 0 ? nr : 0);
     for (int ls = 0; ls < nls; ++ls) {
-        const int rl = GRP ? split + (ls / nr) * p.splits : 0;  // the rank step's layer
+        const int rl = kGdx ? split + (ls / nr) * p.splits : fl;  // the rank step's layer
         const uint16_t* const lt = GRP ? p.gl[rl].lt : p.lt;
         const uint16_t* const la = GRP ? p.gl[rl].la : p.la;
-        const int64_t j0 = static_cast<int64_t>(GRP ? ls % nr : ls) * kStep;
+        const int64_t j0 = static_cast<int64_t>(kGdx ? ls % nr : ls) * kStep;
         if (kUin && p.nu > 0) {
             stage_u_words();  // rp == 64: the one rank step
         } else {
@@ -628,7 +647,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                 const int c = tid + NTHR * i;
                 const int64_t n = m0 + (c >> 3);
                 const int64_t j = j0 + 8 * (c & 7);
-                const uint4 v = (n < p.N && j < p.r_la) ? ld16(la + n * p.ld_la + j) : make_uint4(0, 0, 0, 0);
+                const uint4 v = (n < MA && j < p.r_la) ? ld16(la + n * p.ld_la + j) : make_uint4(0, 0, 0, 0);
                 st16(sA0 + (c >> 3) * LDA + 8 * (c & 7), v);
             }
         } else {
@@ -652,7 +671,10 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
     // m = 32a + 8(r/4) + 4(lane/32) + r%4, t = 32b + lane%32 of the wave tile.
     if (p.splits > 1) {
         // fp32 partial tile of this split (staging these through LDS like the
-        // bf16 tile below measured no faster)
+        // bf16 tile below measured no faster); a grouped forward's layer
+        // writes its columns of the shared partial rows
+        const int64_t pld = kGfwd ? p.gcol[p.ng] : MA;
+        const int64_t pcol = kGfwd ? p.gcol[fl] : 0;
 #pragma unroll
         for (int a = 0; a < SA; ++a)
 #pragma unroll
@@ -664,7 +686,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
                     if (t < p.T && m < MA) {
                         const float4 v = make_float4(acc[a][b][4 * qq], acc[a][b][4 * qq + 1], acc[a][b][4 * qq + 2],
                                                      acc[a][b][4 * qq + 3]);
-                        *reinterpret_cast<float4*>(p.part + (static_cast<int64_t>(split) * p.T + t) * MA + m) = v;
+                        *reinterpret_cast<float4*>(p.part + (static_cast<int64_t>(split) * p.T + t) * pld + pcol + m) = v;
                     }
                 }
         return;
@@ -704,7 +726,7 @@ __global__ __launch_bounds__(64 * WA * WT, 512 / (64 * WA * WT)) void tile_gemm_
         const int64_t gt = t0 + t, gm = m0 + 8 * c;
         if (gt >= p.T || gm >= MA) continue;  // MA is a multiple of 8: a chunk is whole or outside
         const uint4 v = *reinterpret_cast<const uint4*>(out_row(t) + (c ^ (t % RPA % CPR)) * 16);
-        *reinterpret_cast<uint4*>(p.out + gt * MA + gm) = v;
+        *reinterpret_cast<uint4*>((kGfwd ? p.gl[fl].out : p.out) + gt * MA + gm) = v;
     }
 }
 
@@ -740,12 +762,46 @@ __global__ void split_reduce_kernel(const float* __restrict__ part, int splits, 
     reinterpret_cast<uint2*>(out)[i] = o;
 }
 
-// GRP: a grouped dX (a.ng layers, a.gstep set; a.w only gives the format).
+// A grouped forward's reduce pass: the summed partials of column chunk m of
+// the layers' concatenated columns go to the layer owning m (every layer's
+// column count is a multiple of 8, so a 4-column chunk has one owner).
+struct GroupOut {
+    uint16_t* out[kGemmMaxGroup];
+    int64_t col[kGemmMaxGroup + 1];
+    int ng;
+};
+
+__global__ void split_reduce_group_kernel(const float* __restrict__ part, int splits, int64_t T, GroupOut g) {
+    const int64_t ncat = g.col[g.ng], n4 = T * ncat / 4;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    float4 s = reinterpret_cast<const float4*>(part)[i];
+    for (int k = 1; k < splits; ++k) {
+        const float4 v = reinterpret_cast<const float4*>(part)[k * n4 + i];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    const int64_t t = 4 * i / ncat, m = 4 * i - t * ncat;
+    int L = 0;
+    for (int j = 1; j < g.ng; ++j) L += m >= g.col[j] ? 1 : 0;
+    const int64_t n = g.col[L + 1] - g.col[L];
+    uint2 o;
+    o.x = pack_bf16x2(s.x, s.y);
+    o.y = pack_bf16x2(s.z, s.w);
+    *reinterpret_cast<uint2*>(g.out[L] + t * n + (m - g.col[L])) = o;
+}
+
+// GRP: a grouped dX (a.ng layers, a.gstep set) or forward (a.gtile, a.gcol
+// set, a.N the row tiles' total rows, the 256 tile only); a.w only gives
+// the format.
 template <bool DX, bool GRP = false>
 int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStream_t stream, int nu = 0) {
     const int64_t MA = DX ? a.K : a.N;
-    const GemmPlan pl = plan_gemm(MA, a.T, GRP ? int64_t{kStep} * a.gstep[a.ng] : (DX ? a.N : a.K));
+    const GemmPlan pl = plan_gemm(MA, a.T, (GRP && DX) ? int64_t{kStep} * a.gstep[a.ng] : (DX ? a.N : a.K));
     const int tile = pl.tile;
+    if (GRP && !DX && tile != 256) return set_error(QL_ERR_UNSUPPORTED, "%s: needs the 256 tile", what);
     a.tiles_a = static_cast<int>(ceil_div(MA, tile));
     a.tiles_t = static_cast<int>(ceil_div(a.T, tile));
     a.splits = pl.splits;
@@ -768,7 +824,15 @@ int launch_tiles(TileArgs& a, float* split_ws, int kid, const char* what, hipStr
         else
             hipLaunchKernelGGL((tile_gemm_kernel<128, 128, 2, 2, DX, false, GRP>), grid, dim3(256), 0, stream, a);
     }
-    if (a.splits > 1) {
+    if (a.splits > 1 && GRP && !DX) {
+        GroupOut g{};
+        g.ng = a.ng;
+        for (int i = 0; i < a.ng; ++i) g.out[i] = a.gl[i].out;
+        for (int i = 0; i <= a.ng; ++i) g.col[i] = a.gcol[i];
+        const int64_t n4 = a.T * a.gcol[a.ng] / 4;
+        hipLaunchKernelGGL(split_reduce_group_kernel, dim3(static_cast<uint32_t>(ceil_div(n4, 256))), dim3(256), 0,
+                           stream, split_ws, a.splits, a.T, g);
+    } else if (a.splits > 1) {
         const int64_t n4 = a.T * MA / 4;
         hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<uint32_t>(ceil_div(n4, 256))), dim3(256), 0, stream,
                            split_ws, a.splits, n4, a.out);
@@ -806,6 +870,7 @@ GemmPlan plan_gemm(int64_t MA, int64_t T, int64_t RED) {
     if (e && std::strcmp(e, "128") == 0) pl.tile = 128;
     if (e && std::strcmp(e, "256") == 0) pl.tile = 256;
     pl.splits = (pl.tile == 256) ? static_cast<int>(splits) : 1;
+    pl.cost = pl.tile == 256 ? c256 : c128;
     return pl;
 }
 
@@ -954,6 +1019,68 @@ int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, cons
     a.N = N;
     a.K = K;
     return launch_tiles<true>(a, split_ws, QL_KERNEL_GEMM_DX, "dequant GEMM dX", stream);
+}
+
+namespace {
+
+// Rows of a grouped forward's row tiles (256 rows a tile, per layer).
+int64_t fwd_group_rows(const int64_t* N, int ng) {
+    int64_t rows = 0;
+    for (int i = 0; i < ng; ++i) rows += ceil_div(N[i], 256) * 256;
+    return rows;
+}
+
+}  // namespace
+
+// One launch when its plan costs less than the layers' own, or up to 5 %
+// more when it needs no reduction split and some layer's own plan does:
+// the partials' round trip weighs more than the plan's split penalty says
+// (q/k/v at T = 2048: 128 against 125 units, measured 17 % faster).
+bool gemm_fwd_group_pays(const int64_t* N, int ng, int64_t T, int64_t K) {
+    if (ng < 2 || ng > kGemmMaxGroup) return false;
+    const GemmPlan g = plan_gemm(fwd_group_rows(N, ng), T, K);
+    if (g.tile != 256) return false;
+    double sep = 0.0;
+    bool split = false;
+    for (int i = 0; i < ng; ++i) {
+        const GemmPlan pl = plan_gemm(N[i], T, K);
+        sep += pl.cost;
+        split = split || pl.splits > 1;
+    }
+    return g.cost < sep || (g.splits == 1 && split && g.cost <= 1.05 * sep);
+}
+
+size_t gemm_fwd_group_split_bytes(const int64_t* N, int ng, int64_t T, int64_t K) {
+    const GemmPlan g = plan_gemm(fwd_group_rows(N, ng), T, K);
+    int64_t ncat = 0;
+    for (int i = 0; i < ng; ++i) ncat += N[i];
+    return g.splits > 1 ? static_cast<size_t>(g.splits) * T * ncat * sizeof(float) : 0;
+}
+
+int launch_gemm_fwd_group(const GemmLayer* layers, int ng, const uint16_t* X, int r, int rp, int64_t T, int64_t K,
+                          float* split_ws, hipStream_t stream) {
+    if (ng < 1 || ng > kGemmMaxGroup) return set_error(QL_ERR_SHAPE, "grouped forward: %d layers", ng);
+    TileArgs a{};
+    a.w = layers[0].w;  // the format; every layer has the same
+    a.act = X;
+    a.ld_act = K;
+    a.ng = ng;
+    a.gtile[0] = 0;
+    a.gcol[0] = 0;
+    int64_t N[kGemmMaxGroup];
+    for (int i = 0; i < ng; ++i) {
+        a.gl[i] = layers[i];
+        N[i] = layers[i].N;
+        a.gtile[i + 1] = a.gtile[i] + static_cast<int>(ceil_div(layers[i].N, 256));
+        a.gcol[i + 1] = a.gcol[i] + layers[i].N;
+    }
+    a.ld_la = r;
+    a.r_la = r;
+    a.rp = rp;
+    a.T = T;
+    a.N = fwd_group_rows(N, ng);
+    a.K = K;
+    return launch_tiles<false, true>(a, split_ws, QL_KERNEL_GEMM_FWD, "grouped dequant GEMM forward", stream);
 }
 
 int64_t gemm_group_steps(const int64_t* N, int ng) {

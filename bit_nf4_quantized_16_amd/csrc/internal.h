@@ -130,6 +130,7 @@ int launch_gemv_group(const GemvCall* calls, int nw, const uint16_t* X, int64_t 
 struct GemmPlan {
     int tile;
     int splits;
+    double cost;  // rounds of the chip x steps per round (+ the split penalty), in 256-tile step units
 };
 GemmPlan plan_gemm(int64_t MA, int64_t T, int64_t RED);
 size_t gemm_split_bytes(int64_t MA, int64_t T, int64_t RED);
@@ -168,18 +169,30 @@ int launch_gemm_dx(const NF4Dev& w, const uint16_t* dY, const uint16_t* Gp, cons
 // steps) plans one layer's. Every layer has the same format (double
 // quantization or not), rank r and padded rank rp.
 constexpr int kGemmMaxGroup = 4;
-// One layer of a grouped dX launch: its weight, dY [T, N] (row stride N),
-// G [T, rp] bf16 (lt) and A [r, K] (la, row stride K).
+// One layer of a grouped launch. dX: its weight, dY [T, N] (act, row stride
+// N), G [T, rp] bf16 (lt) and A [r, K] (la, row stride K). Forward: its
+// weight, bf16(s U) [T, rp] (lt), B [N, r] (la, row stride r; r % 8 == 0)
+// and Y [T, N] (out).
 struct GemmLayer {
     NF4Dev w;
     const uint16_t* act;
     int64_t N;
     const uint16_t* lt;
     const uint16_t* la;
+    uint16_t* out;
 };
 int64_t gemm_group_steps(const int64_t* N, int ng);
 int launch_gemm_dx_group(const GemmLayer* layers, int ng, int r, int rp, uint16_t* dX, int64_t T, int64_t K,
                          float* split_ws, hipStream_t stream);
+// Y_i = X W_i'^T + Us_i B_i^T for ng layers that read the same X, one GEMM
+// launch over all layers' row tiles (+ one reduce pass when the plan splits
+// the reduction): whether that is planned to beat the layers' own launches
+// (the 256 tile, by plan_gemm's cost of rounds x steps), and the fp32 split
+// workspace it needs.
+bool gemm_fwd_group_pays(const int64_t* N, int ng, int64_t T, int64_t K);
+size_t gemm_fwd_group_split_bytes(const int64_t* N, int ng, int64_t T, int64_t K);
+int launch_gemm_fwd_group(const GemmLayer* layers, int ng, const uint16_t* X, int r, int rp, int64_t T, int64_t K,
+                          float* split_ws, hipStream_t stream);
 
 int lora_grad_rp(int r);         // rank rounded up to 16
 int64_t lora_vt_ld(int64_t T);  // row stride of the transposed [rp16, T] operands

@@ -347,13 +347,25 @@ int qlora_linear_fwd_noalloc(const ql_nf4_weight* w, const uint16_t* X, int64_t 
  *          bytes, rows = the nw values w[i]->rows
  *
  * T <= 16 runs all layers in one dequant-GEMV launch (each layer's U and
- * outputs bitwise equal to qlora_linear_fwd's); larger T runs the layers one
- * after another through qlora_linear_fwd on the one workspace. Each Y[i] and
- * U_out[i] must not alias an input or another output.
+ * outputs bitwise equal to qlora_linear_fwd's). Larger T runs one dequant
+ * GEMM launch over all layers' 256-row tiles, after each layer's U
+ * projection, when r is a multiple of 8, the layers share the format and
+ * the tile plan favours it (e.g. q/k/v at T = 1024, whose single GEMMs
+ * would split their reduction): U bitwise qlora_linear_fwd's, Y the same up
+ * to fp32 summation order; otherwise the layers run one after another
+ * through qlora_linear_fwd on the one workspace. Each Y[i] and U_out[i]
+ * must not alias an input or another output.
  * Errors: as qlora_linear_fwd, plus QL_ERR_SHAPE for nw outside 1..4 or
  * layers of different K; the workspace query returns 0 for invalid sizes.
  */
 size_t qlora_linear_fwd_group_workspace(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r);
+/*
+ * qlora_linear_fwd_group_one_launch — 1 when qlora_linear_fwd_group with
+ * these sizes (T > 16) runs one GEMM launch over all layers' row tiles
+ * (given layers of one format), 0 when it runs them one after another or
+ * T <= 16 (the one GEMV launch). No errors: invalid sizes give 0.
+ */
+int qlora_linear_fwd_group_one_launch(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, int32_t r);
 int qlora_linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,
                            const uint16_t* const* A, const uint16_t* const* B, int32_t r, float scale,
                            uint16_t* const* Y, float* const* U_out, void* ws, size_t ws_bytes,

@@ -69,6 +69,13 @@ int main() {
     EXPECT(qlora_linear_fwd_group_workspace(rows3, 3, 4096, 1, 16) > 0);
     EXPECT(qlora_linear_fwd_group_workspace(rows3, 5, 4096, 1, 16) == 0);
     EXPECT(qlora_linear_fwd_group_workspace(nullptr, 3, 4096, 1, 16) == 0);
+    // a grouped forward above decode sizes: one GEMM launch where the plan favours it
+    const int64_t qkv[3] = {4096, 4096, 4096}, gu[2] = {11008, 11008};
+    EXPECT(qlora_linear_fwd_group_one_launch(qkv, 3, 4096, 1024, 16) == 1);
+    EXPECT(qlora_linear_fwd_group_one_launch(qkv, 3, 4096, 16, 16) == 0);
+    EXPECT(qlora_linear_fwd_group_one_launch(qkv, 3, 4096, 1024, 12) == 0);
+    EXPECT(qlora_linear_fwd_group_one_launch(gu, 2, 4096, 1024, 16) == 0);
+    EXPECT(qlora_linear_fwd_group_one_launch(nullptr, 3, 4096, 1024, 16) == 0);
     // where the forward's U and the backward's G run inside the GEMM launch
     EXPECT(qlora_linear_fwd_u_in_launch(11008, 4096, 1024, 16) == 1 &&
            qlora_linear_fwd_u_in_launch(-1, 4096, 1024, 16) == 0);

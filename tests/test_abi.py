@@ -311,6 +311,16 @@ def test_linear_fwd_group_rejects(lib):
     assert lib.qlora_linear_fwd_group_workspace(rows(256, 256, 256, 256, 256), 5, 256, 16, 8) == 0
     assert lib.qlora_linear_fwd_group_workspace(rows(256, 0), 2, 256, 16, 8) == 0
     assert lib.qlora_linear_fwd_group_workspace(None, 1, 256, 16, 8) == 0
+    # above decode sizes one GEMM launch over all layers where the tile plan
+    # favours it (q/k/v at T = 1024, whose single GEMMs split the reduction);
+    # its workspace then holds every layer's bf16(s U)
+    assert lib.qlora_linear_fwd_group_one_launch(rows(4096, 4096, 4096), 3, 4096, 1024, 16) == 1
+    assert lib.qlora_linear_fwd_group_workspace(rows(4096, 4096, 4096), 3, 4096, 1024, 16) >= 3 * 1024 * 64 * 2
+    assert lib.qlora_linear_fwd_group_one_launch(rows(11008, 11008), 2, 4096, 1024, 16) == 0  # 344 tiles: no
+    assert lib.qlora_linear_fwd_group_one_launch(rows(11008, 11008), 2, 4096, 2048, 16) == 1
+    assert lib.qlora_linear_fwd_group_one_launch(rows(4096, 4096, 4096), 3, 4096, 1024, 12) == 0  # r % 8
+    assert lib.qlora_linear_fwd_group_one_launch(rows(4096, 4096, 4096), 3, 4096, 16, 16) == 0  # the GEMV
+    assert lib.qlora_linear_fwd_group_one_launch(None, 3, 4096, 1024, 16) == 0
 
     def call(shapes=((256, 256), (512, 256)), nw=None, T=4, r=8, X=P, A=True, B=True, Y=P, wsb=None, ws=P):
         ds = descs(shapes)
