@@ -84,6 +84,10 @@ def parse():
     ap.add_argument("--quantize-dq", action="store_true",
                     help="instead of the step: nf4_quantize_dq against nf4_quantize + nf4_double_quant at the 7B "
                          "weight shapes, fp32 and bf16 input, one JSON line")
+    ap.add_argument("--grouped", action="store_true",
+                    help="instead of the step: layers that read the same X (7B q/k/v, gate/up; r = 16) through "
+                         "qlora_linear_fwd_group / qlora_linear_bwd_group against one call per layer, forward "
+                         "and dX, T = 256 .. 4096, one JSON line")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step: the wider measurement set (32-layer 7B stack, 65B linears, "
                          "a GEMV pass over the stack, residency, torch.matmul context), one JSON line")
@@ -1167,6 +1171,62 @@ def compare_bwd_g(torch, qn):
     return res
 
 
+def compare_grouped(torch, qn):
+    """--grouped: the 7B layers that read the same X (q/k/v 3 x 4096x4096,
+    gate/up 2 x 11008x4096), r = 16, alpha = 32, at T in {256, 512, 1024,
+    2048, 4096}: the forward as one qlora_linear_fwd_group call against one
+    qlora_linear_fwd per layer, and dX alone as one qlora_linear_bwd_group
+    call against one qlora_linear_bwd per layer. HIP events around 20
+    back-to-back calls after 3 untimed ones, three alternating rounds (us
+    per call); `fwd_one_launch` is what qlora_linear_fwd_group_one_launch
+    says (0: the grouped forward runs one call per layer itself)."""
+    import ctypes
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / 20 * 1e3, 1)
+
+    res = {}
+    r = 16
+    for name, N, K, m in (("qkv", 4096, 4096, 3), ("gate_up", 11008, 4096, 2)):
+        ws = [qn.quantize_weight(torch.randn(N, K, device="cuda", generator=g) * 0.02) for _ in range(m)]
+        As = [(torch.randn(r, K, device="cuda", generator=g) / K).to(torch.bfloat16) for _ in range(m)]
+        Bs = [(torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16) for _ in range(m)]
+        for T in (256, 512, 1024, 2048, 4096):
+            print("grouped: %s T=%d" % (name, T), file=sys.stderr, flush=True)
+            X = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+            dYs = [torch.randn(T, N, device="cuda", generator=g).to(torch.bfloat16) for _ in range(m)]
+            ways = {
+                "fwd_separate": lambda: [qn.qlora_linear_fwd(ws[i], X, As[i], Bs[i], 2.0) for i in range(m)],
+                "fwd_grouped": lambda: qn.qlora_linear_fwd_group(ws, X, As, Bs, 2.0),
+                "dx_separate": lambda: [qn.qlora_linear_bwd(ws[i], X, dYs[i], As[i], Bs[i], 2.0, need_da=False,
+                                                            need_db=False) for i in range(m)],
+                "dx_grouped": lambda: qn.qlora_linear_bwd_group(ws, X, dYs, As, Bs, 2.0, need_da=False,
+                                                                need_db=False),
+            }
+            row = {"fwd_one_launch": qn.lib.qlora_linear_fwd_group_one_launch((ctypes.c_int64 * m)(*[N] * m), m, K,
+                                                                              T, r)}
+            for _ in range(3):
+                for k, fn in ways.items():
+                    row.setdefault(k + "_us", []).append(timed(fn))
+            res["%s_T%d" % (name, T)] = row
+            del X, dYs
+        del ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def compare_quantize_dq(torch, qn):
     """Quantize + double quantization of the 7B weight shapes, fp32 and bf16
     input, both ways in alternating rounds: nf4_quantize_dq (one call; two
@@ -1245,6 +1305,9 @@ def main():
         return
     if args.quantize_dq:
         print(json.dumps({"quantize_dq": compare_quantize_dq(torch, qn)}), flush=True)
+        return
+    if args.grouped:
+        print(json.dumps({"grouped": compare_grouped(torch, qn)}), flush=True)
         return
     print("bench: generating inputs", file=sys.stderr, flush=True)
     inp = Inputs(torch, workloads)
