@@ -533,8 +533,10 @@ size_t group_fwd_ws(const int64_t* rows, int32_t nw, int64_t cols, int64_t T, in
     // decode: one launch, a workspace slice per weight; larger T: one GEMM
     // launch over all weights, or the weights one after another sharing one
     // workspace
+    // (layers of mixed formats take the one-after-another path: enough for both)
     if (T <= kGemvMaxT) return static_cast<size_t>(nw) * gemv_ws_bytes(T, cols, r);
-    return fwd_group_one_launch(rows, nw, cols, T, r) ? carve_fwd_group(nullptr, rows, nw, cols, T, r).bytes : m;
+    return fwd_group_one_launch(rows, nw, cols, T, r) ? std::max(m, carve_fwd_group(nullptr, rows, nw, cols, T, r).bytes)
+                                                      : m;
 }
 
 int linear_fwd_group(const ql_nf4_weight* const* w, int32_t nw, const uint16_t* X, int64_t T,

@@ -344,7 +344,8 @@ int qlora_linear_fwd_noalloc(const ql_nf4_weight* w, const uint16_t* X, int64_t 
  *          be NULL when r == 0, U_out NULL or U_out[i] NULL to skip U)
  *   nw     1..4 layers; all share K = w[i]->cols, r and scale
  *   ws     workspace of qlora_linear_fwd_group_workspace(rows, nw, K, T, r)
- *          bytes, rows = the nw values w[i]->rows
+ *          bytes, rows = the nw values w[i]->rows (enough for either path
+ *          below, whatever the layers' formats)
  *
  * T <= 16 runs all layers in one dequant-GEMV launch (each layer's U and
  * outputs bitwise equal to qlora_linear_fwd's). Larger T runs one dequant

@@ -139,3 +139,22 @@ def test_fwd_group_gemm_graph_replays(qn):
         torch.cuda.synchronize()
         for i, ((Y, U), (Yw, Uw)) in enumerate(zip(outs, want)):
             assert torch.equal(Y, Yw) and torch.equal(U, Uw), "replay %d, layer %d" % (rep, i)
+
+
+def test_fwd_group_mixed_formats_run_one_call_per_layer(qn):
+    """A group whose layers differ in double quantization takes the
+    one-after-another path (the workspace query covers it): Y and U bitwise
+    one qlora_linear_fwd per layer."""
+    shapes, K, T, r = (1024, 1024, 1024), 2048, 512, 16
+    assert _one_launch(qn, shapes, K, T, r)
+    cases = _layers(shapes, K, T, r, seed=21)
+    s = cases[0].scale
+    ws = [qn.quantize_weight(c.W.cuda(), double_quant=(i != 1)) for i, c in enumerate(cases)]
+    X = cases[0].X.cuda()
+    As = [c.A.cuda() for c in cases]
+    Bs = [c.B.cuda() for c in cases]
+    outs = qn.qlora_linear_fwd_group(ws, X, As, Bs, s)
+    for i, w in enumerate(ws):
+        Y1, U1 = qn.qlora_linear_fwd(w, X, As[i], Bs[i], s)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[i][0], Y1) and torch.equal(outs[i][1], U1), "layer %d" % i
