@@ -3,7 +3,6 @@ at T > 16 where it runs one GEMM launch over all layers' row tiles): Y and U
 of every layer against the fp64 CPU oracle, U bitwise the single calls', and
 Y bitwise one call on the stacked weight where the two plans coincide."""
 
-import numpy as np
 import pytest
 import torch
 
