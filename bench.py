@@ -1409,7 +1409,8 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the 7B workloads)",
         "config": {
             "workload": "llama7b_qlora_step: attn 4096x4096 quantize+DQ+dequant+GEMV T=1,16 (r=16); "
-                        "MLP 11008x4096 x2 + 4096x11008 quantize+DQ+fwd+bwd at T=1024 (r=16)",
+                        "MLP 11008x4096 x2 + 4096x11008 quantize+DQ+fwd+bwd at T=1024 (r=16; gate and up read "
+                        "the same X, their backward one grouped call)",
             "ideal_step_ms": round(ideal * 1e3, 4),
             "blocksize": 64,
             "dq_blocksize": 256,
