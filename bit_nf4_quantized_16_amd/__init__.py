@@ -30,6 +30,7 @@ __all__ = [
     "qlora_linear_bwd_group",
     "quantize_weight",
     "QLoRALinearFunction",
+    "QLoRAGroupFunction",
     "KernelTimer",
     "lib",
 ]
@@ -399,6 +400,37 @@ class QLoRALinearFunction(torch.autograd.Function):
         dX, dA, dB = qlora_linear_bwd(ctx.w, X, dY.contiguous().to(torch.bfloat16), A, B, ctx.scale, U=U,
                                       need_dx=ctx.needs_input_grad[0], keep=ctx.keep, p=ctx.p)
         return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None, None
+
+
+class QLoRAGroupFunction(torch.autograd.Function):
+    """autograd wrapper for up to four layers that read the same X (q/k/v,
+    gate/up): apply(X, scale, ws, A_0, B_0, A_1, B_1, ...) returns the
+    layers' Y; the forward is one qlora_linear_fwd_group call, the backward
+    one qlora_linear_bwd_group call (X receives the summed input gradient;
+    the weights in ``ws`` are frozen)."""
+
+    @staticmethod
+    def forward(ctx, X, scale, ws, *adapters):
+        As, Bs = [a.contiguous() for a in adapters[0::2]], [b.contiguous() for b in adapters[1::2]]
+        outs = qlora_linear_fwd_group(ws, X.contiguous(), As, Bs, scale)
+        ctx.save_for_backward(X, *As, *Bs, *[U for _, U in outs])
+        ctx.ws = ws
+        ctx.scale = scale
+        return tuple(Y for Y, _ in outs)
+
+    @staticmethod
+    def backward(ctx, *dYs):
+        n = len(ctx.ws)
+        saved = ctx.saved_tensors
+        X, As, Bs, Us = saved[0], list(saved[1:1 + n]), list(saved[1 + n:1 + 2 * n]), list(saved[1 + 2 * n:])
+        dYs = [(d if d is not None else torch.zeros(X.shape[0], w.rows, device=X.device)).contiguous()
+               .to(torch.bfloat16) for d, w in zip(dYs, ctx.ws)]
+        dX, dAs, dBs = qlora_linear_bwd_group(ctx.ws, X, dYs, As, Bs, ctx.scale, Us=Us,
+                                              need_dx=ctx.needs_input_grad[0])
+        grads = []
+        for i in range(n):
+            grads += [dAs[i].to(As[i].dtype), dBs[i].to(Bs[i].dtype)]
+        return (dX, None, None, *grads)
 
 
 class KernelTimer:

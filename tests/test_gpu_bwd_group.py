@@ -202,3 +202,31 @@ def test_bwd_group_full_size_gate_up(qn):
         assert normwise_rel_err(f32_to_np(dAs[i])[:, cols], dAi) <= TOL, "layer %d: dA" % i
     err = normwise_rel_err(bf16_to_np(dX)[:, cols], dXo)
     assert err <= TOL, "dX error %.3e" % err
+
+
+@pytest.mark.parametrize("shapes,K,T,r", [((264, 512, 128), 320, 48, 8), ((1024, 1024, 1024), 2048, 512, 16)])
+def test_group_autograd_function(qn, shapes, K, T, r):
+    """QLoRAGroupFunction: the grouped forward and backward through autograd;
+    X receives the summed input gradient of the layers, each adapter its own
+    (against the oracle)."""
+    cases = _layers(shapes, K, T, r, seed=31)
+    s = cases[0].scale
+    ws = [qn.quantize_weight(c.W.cuda()) for c in cases]
+    X = cases[0].X.cuda().requires_grad_(True)
+    ad = []
+    for c in cases:
+        ad += [c.A.cuda().requires_grad_(True), c.B.cuda().requires_grad_(True)]
+    Ys = qn.QLoRAGroupFunction.apply(X, s, ws, *ad)
+    torch.autograd.backward(Ys, [c.dY.cuda() for c in cases])
+    Xn = bf16_to_np(cases[0].X)
+    dXo = 0.0
+    for i, c in enumerate(cases):
+        An, Bn = bf16_to_np(c.A), bf16_to_np(c.B)
+        wd = oracle_weight(c.W.numpy())["wd"]
+        H, _ = oracle.lora_forward(Xn, wd, An, Bn, s)
+        assert normwise_rel_err(bf16_to_np(Ys[i]), H) <= TOL, "layer %d: Y" % i
+        dXi, dAo, dBo, _, _ = oracle.lora_backward(Xn, bf16_to_np(c.dY), wd, An, Bn, s)
+        dXo = dXo + dXi
+        assert normwise_rel_err(bf16_to_np(ad[2 * i].grad), dAo) <= TOL, "layer %d: dA" % i
+        assert normwise_rel_err(bf16_to_np(ad[2 * i + 1].grad), dBo) <= TOL, "layer %d: dB" % i
+    assert normwise_rel_err(bf16_to_np(X.grad), dXo) <= TOL
